@@ -1,0 +1,202 @@
+/*
+ * moe.h -- C ABI of libmoe: the routed, block-quantized Mixture-of-Experts
+ * layer (top-k routed experts plus one shared expert, 2-3-bit weights), on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Where the operations come from (the pages this library follows):
+ *   [forum] discuss.pytorch.kr, "Strata: 12GB 그래픽카드 PC에서 125B 모델
+ *           Qwen3.8-Flash-Next만을 위해 만든 추론 엔진":
+ *           section "Strata 소개" -- each layer selects 10 of 512 experts;
+ *           section "Strata의 동작 원리 / 그래픽카드, RAM, SSD에 나눠 담은 전문가"
+ *           -- per layer the router picks the expert ids, the ids are split
+ *           among the places that compute them, and the GPU merges the results
+ *           before the next layer; the router and the shared expert always sit
+ *           on the GPU;
+ *           section "추측 후 검증: MTP 층을 이용한 투기적 디코딩" -- the verify pass
+ *           runs 1 + 3 tokens through the layers at once;
+ *           section "긴 프롬프트와 긴 컨텍스트 처리" -- prompts are read in chunks
+ *           of up to 8,192 tokens.
+ *   [guide] tech.okbari.net, "Strata와 Qwen3.8-Flash-Next: RTX 4090 Windows 실행
+ *           가이드", section "Strata, Qwen, GSQ-RCO는 서로 다른 구성 요소다" --
+ *           48 layers; per MoE layer 10 of 512 routed experts plus 1 shared
+ *           expert are active.
+ *   [video] kangdaejong.com, "2026-10-09 strata-qwen-flash-next-soulseeker"
+ *           summary, section "픽업" -- the selected experts' compressed weights
+ *           are decompressed and computed on the GPU.
+ * The pages give no formulas, tensor shapes or bit layouts.  The readings this
+ * library takes: softmax over the E logits, top-k, renormalised over the k;
+ * SwiGLU experts h = silu(x Wg^T) * (x Wu^T), y = h Wd^T; the shared expert is
+ * added with weight 1; weights are stored in the block-32 formats below.
+ *
+ * Conventions for every call
+ *   - Array pointers are DEVICE pointers owned by the caller (e.g. allocated
+ *     through PyTorch).  `moe_layer` is a host struct holding device pointers;
+ *     it is read during the call and not kept.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on `stream` and returns; the library never allocates,
+ *     frees or synchronises.  Results are ready when the stream reaches them.
+ *   - Arguments are validated on the host before anything is enqueued.  On any
+ *     error nothing is enqueued and no output is written.
+ *   - T == 0 is valid: MOE_OK, nothing enqueued.
+ *   - Errors: MOE_ERR_INVALID_ARGUMENT (null pointer where one is required,
+ *     bad size, misaligned pointer), MOE_ERR_UNSUPPORTED (unknown format or a
+ *     shape outside the supported set), MOE_ERR_WORKSPACE (workspace too small
+ *     or misaligned), MOE_ERR_HIP (a kernel launch failed; the HIP error is
+ *     cleared).  Faults inside kernels surface at the caller's next
+ *     synchronisation, as HIP reports them.
+ *   - Supported shapes: 1 <= k <= E <= 1024; d_model and d_ff multiples of 128
+ *     and at most 16384; T * k < 2^31.  Every pointer is 16-byte aligned.
+ *   - Integer results (ids, offsets, permutation) are bit-exact and identical
+ *     run to run; float results are deterministic on a given device.
+ *   - Calls on different streams are independent only if they use different
+ *     workspaces.
+ *
+ * Block-32 weight formats (rows x K matrix, K the reduction axis, blocks of 32
+ * consecutive K elements share one scale):
+ *   MOE_FMT_Q2_B32  2-bit codes q in 0..3, fp16 scale d, fp16 min m:
+ *                   w = d*q + m                     (0.375 bytes per weight)
+ *   MOE_FMT_Q3_B32  3-bit codes q in 0..7, fp16 scale d:
+ *                   w = d*(q - 4)                   (0.4375 bytes per weight)
+ * Storage order (rows % 16 == 0, K % 128 == 0).  The matrix is cut into units
+ * of 16 rows x 128 columns, unit u = (r/16)*(K/128) + k/128.  Inside a unit:
+ * rr = r%16, block j = (k%128)/32, eighth g = (k%32)/8, s = k%8, c = s%4.
+ *   lo    512 bytes per unit.  Byte ((g*16 + rr)*4 + j)*2 + s/4 holds the low
+ *         two code bits of four columns; column c of the four is at bit
+ *         4*(c&1) + 2*(c>>1) (so bits 1:0 = c0, 3:2 = c2, 5:4 = c1, 7:6 = c3).
+ *   hi    (Q3 only) 256 bytes per unit: little-endian 32-bit word g*16 + rr,
+ *         bit 4*s + j holds code bit 2.
+ *   scale 64 fp16 per unit, element rr*4 + j.
+ *   min   (Q2 only) 64 fp16 per unit, element rr*4 + j.
+ * n matrices of one kind are stacked expert-major (expert e starts at unit
+ * e*(rows/16)*(K/128)).  Each plane is a separate array.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1,
+    MOE_ERR_UNSUPPORTED = 2,
+    MOE_ERR_WORKSPACE = 3,
+    MOE_ERR_HIP = 4
+} moe_status;
+
+typedef enum { MOE_FMT_Q2_B32 = 1, MOE_FMT_Q3_B32 = 2 } moe_format;
+
+/* n stacked rows x K matrices in the storage order above. */
+typedef struct {
+    const uint8_t *lo;     /* required                                  */
+    const uint8_t *hi;     /* Q3: required; Q2: must be NULL            */
+    const uint16_t *scale; /* fp16 bits, required                       */
+    const uint16_t *min;   /* Q2: required (fp16 bits); Q3: must be NULL */
+} moe_qmat;
+
+/* One MoE layer.  Routed: n = n_experts matrices each; shared: n = 1.
+ * gate, up: rows = d_ff, K = d_model.   down: rows = d_model, K = d_ff. */
+typedef struct {
+    int32_t format; /* moe_format */
+    int32_t d_model;
+    int32_t d_ff;
+    int32_t n_experts;
+    moe_qmat gate, up, down;
+    moe_qmat sh_gate, sh_up, sh_down;
+} moe_layer;
+
+/*
+ * moe_route -- router scores, top-k selection and routing weights.
+ * [forum] "Strata의 동작 원리": the router runs on the GPU for every token of
+ * every layer and names the k experts the token uses ("Strata 소개": 10 of 512).
+ *
+ *   logits[t][e] = sum_c x[t][c] * Wr[c][e]  (+ bias[e])      fp32
+ *   ids[t][0..k) = the k largest logits[t][.], in descending order; equal
+ *                  values (also -0.0 vs +0.0) rank the lower expert first
+ *   w[t][j]      = exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0), l_j = logit of ids[t][j]
+ *                  (= softmax over all E, restricted to the top k, renormalised)
+ *
+ * x_bf16   [T][d_model] bfloat16 bits, row-major.
+ * w_router [d_model][E] fp32, E contiguous.  If NULL, `logits` is an INPUT
+ *          [T][E] (x_bf16 and bias must then be NULL): only selection and
+ *          weights are computed.
+ * bias     [E] fp32 or NULL.
+ * logits   [T][E] fp32, written (or read, see above).  Must be finite.
+ * topk_ids [T][k] int32, topk_w [T][k] fp32: written.
+ * ws       workspace of at least moe_workspace_size(d_model, *, E, T, k) bytes,
+ *          256-byte aligned, zero-filled once by moe_workspace_init.
+ */
+moe_status moe_route(const uint16_t *x_bf16, const float *w_router, const float *bias,
+                     float *logits, int32_t T, int32_t d_model, int32_t E, int32_t k,
+                     int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_dispatch -- group the P = T*k token-expert pairs by expert.
+ * [forum] "Strata의 동작 원리": once the ids are known the experts are split
+ * among their executors; here every expert is resident, so the split becomes
+ * an expert-sorted permutation consumed by moe_expert_ffn.
+ *
+ * Pair p = t*k + j names token t and its j-th expert topk_ids[t][j].
+ *   offsets     [E+1] int32: offsets[e] = number of pairs with expert < e;
+ *               offsets[E] = P.
+ *   sorted_pair [P] int32: pairs ordered by expert, ascending p within an
+ *               expert (stable).   pair_pos [P] int32: inverse permutation,
+ *               sorted_pair[pair_pos[p]] == p.
+ * Every id must lie in [0, E) and a token's k ids must be distinct (as
+ * moe_route produces them); other input is a precondition violation.
+ */
+moe_status moe_dispatch(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k,
+                        int32_t *offsets, int32_t *sorted_pair, int32_t *pair_pos, void *ws,
+                        size_t ws_bytes, void *stream);
+
+/*
+ * moe_expert_ffn -- the selected experts and the shared expert.
+ * [forum] "Strata의 동작 원리" and [guide] "Strata, Qwen, GSQ-RCO…": 10 routed
+ * experts plus one shared expert per token per layer; [video] "픽업": the
+ * 2-3-bit expert weights are decompressed and computed on the GPU.
+ *
+ * For sorted position i (expert e with offsets[e] <= i < offsets[e+1], token
+ * t = sorted_pair[i] / k), and for the shared expert on every token t:
+ *   h = silu(x_t . Wg_e^T) * (x_t . Wu_e^T),  silu(z) = z / (1 + exp(-z))
+ *   y = h . Wd_e^T
+ * y_pairs  [T*k][d_model] fp32: row i = position i (expert-sorted order).
+ * y_shared [T][d_model] fp32: the shared expert on each token.
+ * offsets and sorted_pair as written by moe_dispatch for the same T, k, E.
+ * Weights are dequantised exactly in fp32 when few rows share an expert
+ * (decode); larger groups use fp16 matrix-core tiles with fp32 accumulation.
+ */
+moe_status moe_expert_ffn(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, int32_t k,
+                          const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
+                          float *y_shared, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_combine -- merge the expert outputs of each token.
+ * [forum] "Strata의 동작 원리": the GPU merges every expert's result, then the
+ * next layer starts.
+ *   out[t][:] = y_shared[t][:] + sum_{j<k} topk_w[t][j] * y_pairs[pair_pos[t*k+j]][:]
+ * out [T][d_model] fp32, overwritten.  Needs no workspace.
+ */
+moe_status moe_combine(const float *y_pairs, const float *y_shared, const int32_t *pair_pos,
+                       const float *topk_w, int32_t T, int32_t k, int32_t d_model, float *out,
+                       void *stream);
+
+/* Workspace bytes that suffice for every call above with these sizes. */
+size_t moe_workspace_size(int32_t d_model, int32_t d_ff, int32_t E, int32_t T, int32_t k);
+
+/* Zero-fill a workspace (enqueued on `stream`).  Needed once after
+ * allocation; every call leaves the workspace's counters zero again. */
+moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+const char *moe_status_string(moe_status s);
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

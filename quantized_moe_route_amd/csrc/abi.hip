@@ -1,0 +1,170 @@
+// abi.hip -- the extern "C" entry points of libmoe: host-side validation, then
+// the kernel launches.  Declarations and contracts: include/moe.h.
+#include <stdint.h>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxDim = 16384;
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+inline bool ok_dim(int v) { return v > 0 && v <= kMaxDim && v % 128 == 0; }
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline moe_status launched(hipError_t e) {
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+}
+
+bool check_qmat(const moe_qmat &m, int fmt) {
+    if (!m.lo || !m.scale) return false;
+    if (!aligned16(m.lo) || !aligned16(m.scale)) return false;
+    if (fmt == MOE_FMT_Q2_B32) {
+        if (m.hi || !m.min || !aligned16(m.min)) return false;
+    } else {
+        if (m.min || !m.hi || !aligned16(m.hi)) return false;
+    }
+    return true;
+}
+
+// route needs the header always (counters) plus its partial sums
+size_t route_need(int d, int E, int T) { return kWsHeader + route_ws_bytes(d, E, T); }
+size_t dispatch_need(int E, int T, int k) { return kWsHeader + dispatch_ws_bytes(E, T, k); }
+size_t ffn_need(int d, int f, int E, int T, int k) {
+    const size_t a = ffn_small_ws_bytes(d, f, E, T, k);
+    const size_t b = ffn_prefill_ws_bytes(d, f, E, T, k);
+    return kWsHeader + (T <= kSmallTMax ? a : b);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported format or shape";
+        case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+        case MOE_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+size_t moe_workspace_size(int32_t d_model, int32_t d_ff, int32_t E, int32_t T, int32_t k) {
+    if (d_model <= 0 || d_ff <= 0 || E <= 0 || T < 0 || k <= 0) return 0;
+    size_t need = route_need(d_model, E, T);
+    const size_t b = dispatch_need(E, T, k);
+    const size_t c = ffn_need(d_model, d_ff, E, T, k);
+    if (b > need) need = b;
+    if (c > need) need = c;
+    return (need + 255) & ~(size_t)255;
+}
+
+moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+    if (!ws || !aligned256(ws) || ws_bytes < kWsHeader) return MOE_ERR_WORKSPACE;
+    return launched(launch_fill_zero(ws, ws_bytes, as_stream(stream)));
+}
+
+moe_status moe_route(const uint16_t *x_bf16, const float *w_router, const float *bias,
+                     float *logits, int32_t T, int32_t d_model, int32_t E, int32_t k,
+                     int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+    if (T < 0 || E < 1 || E > kMaxE || k < 1 || k > E) return MOE_ERR_INVALID_ARGUMENT;
+    if ((int64_t)T * k >= INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
+    if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (w_router) {
+        if (!x_bf16 || !aligned16(x_bf16) || !aligned16(w_router)) return MOE_ERR_INVALID_ARGUMENT;
+        if (bias && !aligned16(bias)) return MOE_ERR_INVALID_ARGUMENT;
+        if (!ok_dim(d_model)) return MOE_ERR_UNSUPPORTED;
+    } else {
+        if (x_bf16 || bias) return MOE_ERR_INVALID_ARGUMENT;
+    }
+    if (!ws || !aligned256(ws)) return MOE_ERR_WORKSPACE;
+    if (w_router && ws_bytes < route_need(d_model, E, T)) return MOE_ERR_WORKSPACE;
+    if (T == 0) return MOE_OK;
+    hipStream_t s = as_stream(stream);
+    if (!w_router) return launched(launch_topk(logits, T, E, k, topk_ids, topk_w, s));
+    if (route_ws_bytes(d_model, E, T) > 0)
+        return launched(launch_route_small(x_bf16, w_router, bias, logits, T, d_model, E, k,
+                                           topk_ids, topk_w, ws, s));
+    hipError_t e = launch_router_gemm(x_bf16, w_router, bias, logits, T, d_model, E, s);
+    if (e != hipSuccess) return launched(e);
+    return launched(launch_topk(logits, T, E, k, topk_ids, topk_w, s));
+}
+
+moe_status moe_dispatch(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k,
+                        int32_t *offsets, int32_t *sorted_pair, int32_t *pair_pos, void *ws,
+                        size_t ws_bytes, void *stream) {
+    if (T < 0 || E < 1 || E > kMaxE || k < 1 || k > E) return MOE_ERR_INVALID_ARGUMENT;
+    if ((int64_t)T * k >= INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
+    if (!topk_ids || !offsets || !sorted_pair || !pair_pos) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(topk_ids) || !aligned16(offsets) || !aligned16(sorted_pair) ||
+        !aligned16(pair_pos))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (!ws || !aligned256(ws) || ws_bytes < dispatch_need(E, T, k)) return MOE_ERR_WORKSPACE;
+    if (T == 0) return MOE_OK;
+    return launched(launch_dispatch(topk_ids, T, E, k, offsets, sorted_pair, pair_pos, ws,
+                                    as_stream(stream)));
+}
+
+moe_status moe_expert_ffn(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, int32_t k,
+                          const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
+                          float *y_shared, void *ws, size_t ws_bytes, void *stream) {
+    if (!layer) return MOE_ERR_INVALID_ARGUMENT;
+    const moe_layer &L = *layer;
+    if (L.format != MOE_FMT_Q2_B32 && L.format != MOE_FMT_Q3_B32) return MOE_ERR_UNSUPPORTED;
+    if (!ok_dim(L.d_model) || !ok_dim(L.d_ff)) return MOE_ERR_UNSUPPORTED;
+    if (L.n_experts < 1 || L.n_experts > kMaxE) return MOE_ERR_INVALID_ARGUMENT;
+    if (T < 0 || k < 1 || k > L.n_experts) return MOE_ERR_INVALID_ARGUMENT;
+    if ((int64_t)T * k >= INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
+    if (!check_qmat(L.gate, L.format) || !check_qmat(L.up, L.format) ||
+        !check_qmat(L.down, L.format) || !check_qmat(L.sh_gate, L.format) ||
+        !check_qmat(L.sh_up, L.format) || !check_qmat(L.sh_down, L.format))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (!x_bf16 || !offsets || !sorted_pair || !y_pairs || !y_shared)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x_bf16) || !aligned16(offsets) || !aligned16(sorted_pair) ||
+        !aligned16(y_pairs) || !aligned16(y_shared))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (!ws || !aligned256(ws) ||
+        ws_bytes < ffn_need(L.d_model, L.d_ff, L.n_experts, T, k))
+        return MOE_ERR_WORKSPACE;
+    if (T == 0) return MOE_OK;
+    hipStream_t s = as_stream(stream);
+    if (T <= kSmallTMax)
+        return launched(launch_ffn_small(L, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared,
+                                         ws, s));
+    hipError_t e = launch_ffn_prefill(L, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, ws, s);
+    if (e == hipErrorNotSupported) return MOE_ERR_UNSUPPORTED;
+    return launched(e);
+}
+
+moe_status moe_combine(const float *y_pairs, const float *y_shared, const int32_t *pair_pos,
+                       const float *topk_w, int32_t T, int32_t k, int32_t d_model, float *out,
+                       void *stream) {
+    if (T < 0 || k < 1 || k > kMaxE) return MOE_ERR_INVALID_ARGUMENT;
+    if ((int64_t)T * k >= INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
+    if (!ok_dim(d_model)) return MOE_ERR_UNSUPPORTED;
+    if (!y_pairs || !y_shared || !pair_pos || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(y_pairs) || !aligned16(y_shared) || !aligned16(pair_pos) ||
+        !aligned16(topk_w) || !aligned16(out))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (T == 0) return MOE_OK;
+    return launched(launch_combine(y_pairs, y_shared, pair_pos, topk_w, T, k, d_model, out,
+                                   as_stream(stream)));
+}
+
+}  // extern "C"

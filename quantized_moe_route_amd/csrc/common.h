@@ -1,0 +1,211 @@
+// common.h -- internal helpers shared by the libmoe HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Workspace: the first 4 KiB hold int32 counters that are zero between
+// calls (each user restores them); scratch regions start after it.
+constexpr size_t kWsHeader = 4096;
+constexpr int kCntRouteSlice = 0;   // [0, 16): per 64-expert slice arrival counters
+constexpr int kCntRouteAll = 16;    // one counter: slices finished
+constexpr int kCntPrefillTicket = 32;  // persistent-GEMM tickets / exits (4 slots)
+
+struct QMatDev {
+    const uint8_t *lo;
+    const uint8_t *hi;
+    const uint16_t *scale;
+    const uint16_t *min;
+};
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+    _Float16 v = __builtin_bit_cast(_Float16, h);
+    return static_cast<float>(v);
+}
+
+// Packed fp4 (e2m1) -> two bf16/fp16.  A nibble 0b00qq read as e2m1 is q/2,
+// so with scale 2 a 2-bit code converts to exactly q.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4_bf16(uint32_t v, float scale) {
+    bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, SEL);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4_f16(uint32_t v, float scale) {
+    f16x2 r = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, scale, SEL);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// B operand (8 values, k = 8g..8g+7 of one 32-block) from the lane's lo dword
+// holding blocks (2*half, 2*half+1): HALF selects which 16 bits.  SCALE is 2
+// (exact codes) for lo bits; for Q3 hi bits use hi_operand below.
+template <int HALF, bool F16>
+__device__ __forceinline__ u32x4 lo_operand(uint32_t dw) {
+    const uint32_t a = dw & 0x33333333u;         // codes 0,1 of every byte
+    const uint32_t b = (dw >> 2) & 0x33333333u;  // codes 2,3 of every byte
+    u32x4 r;
+    if constexpr (F16) {
+        r[0] = cvt_fp4_f16<2 * HALF>(a, 2.0f);
+        r[1] = cvt_fp4_f16<2 * HALF>(b, 2.0f);
+        r[2] = cvt_fp4_f16<2 * HALF + 1>(a, 2.0f);
+        r[3] = cvt_fp4_f16<2 * HALF + 1>(b, 2.0f);
+    } else {
+        r[0] = cvt_fp4_bf16<2 * HALF>(a, 2.0f);
+        r[1] = cvt_fp4_bf16<2 * HALF>(b, 2.0f);
+        r[2] = cvt_fp4_bf16<2 * HALF + 1>(a, 2.0f);
+        r[3] = cvt_fp4_bf16<2 * HALF + 1>(b, 2.0f);
+    }
+    return r;
+}
+
+// Q3 code bit 2 of block j as an operand holding 4*bit: nibble s of
+// (H >> j) & 0x11111111 is 0 or 1 = fp4 0 or 0.5, scaled by 8.
+template <int J, bool F16>
+__device__ __forceinline__ u32x4 hi_operand(uint32_t H) {
+    const uint32_t v = (H >> J) & 0x11111111u;
+    u32x4 r;
+    if constexpr (F16) {
+        r[0] = cvt_fp4_f16<0>(v, 8.0f);
+        r[1] = cvt_fp4_f16<1>(v, 8.0f);
+        r[2] = cvt_fp4_f16<2>(v, 8.0f);
+        r[3] = cvt_fp4_f16<3>(v, 8.0f);
+    } else {
+        r[0] = cvt_fp4_bf16<0>(v, 8.0f);
+        r[1] = cvt_fp4_bf16<1>(v, 8.0f);
+        r[2] = cvt_fp4_bf16<2>(v, 8.0f);
+        r[3] = cvt_fp4_bf16<3>(v, 8.0f);
+    }
+    return r;
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Locate the group handled by `slot`: slot 0 = shared expert (rows 0..T-1 in
+// token order), slot s >= 1 = the (s-1)-th expert with a non-empty segment.
+// Executed by one wave; all lanes get the result.  Returns false if the slot
+// has no group.
+struct Group {
+    int expert;     // -1 = shared
+    int row0;       // first row in the expert-sorted pair order (routed) or 0
+    int nrows;
+    int hrow0;      // first row of this group in the h scratch buffer
+};
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int l = __lane_id();
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int t = __shfl_up(v, o, 64);
+        if (l >= o) v += t;
+    }
+    return v;
+}
+
+__device__ inline bool find_group(const int32_t *__restrict__ offsets, int E, int T, int P, int slot,
+                                  Group &g) {
+    if (slot == 0) {
+        g.expert = -1;
+        g.row0 = 0;
+        g.nrows = T;
+        g.hrow0 = P;
+        return T > 0;
+    }
+    const int target = slot - 1;  // index among non-empty experts
+    const int l = __lane_id();
+    const int per = (E + 63) / 64;
+    const int e0 = l * per;
+    int cnt = 0;
+    for (int i = 0; i < per; ++i) {
+        int e = e0 + i;
+        if (e < E && offsets[e + 1] > offsets[e]) ++cnt;
+    }
+    const int incl = wave_incl_scan(cnt);
+    const int excl = incl - cnt;
+    int found = -1;
+    if (target >= excl && target < incl) {
+        int c = excl;
+        for (int i = 0; i < per; ++i) {
+            int e = e0 + i;
+            if (e < E && offsets[e + 1] > offsets[e]) {
+                if (c == target) { found = e; break; }
+                ++c;
+            }
+        }
+    }
+    // exactly one lane (or none) found it
+    unsigned long long m = __ballot(found >= 0);
+    if (m == 0ull) return false;
+    const int src = __ffsll((long long)m) - 1;
+    const int e = __shfl(found, src, 64);
+    g.expert = e;
+    g.row0 = offsets[e];
+    g.nrows = offsets[e + 1] - offsets[e];
+    g.hrow0 = g.row0;
+    return true;
+}
+
+// silu(g) * u in fp32
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// ---------------------------------------------------------------- launchers
+// (defined in the .hip files; return hipError_t of the launch)
+hipError_t launch_route_small(const uint16_t *x, const float *wr, const float *bias, float *logits,
+                              int T, int d, int E, int k, int32_t *ids, float *w, void *ws,
+                              hipStream_t s);
+hipError_t launch_router_gemm(const uint16_t *x, const float *wr, const float *bias, float *logits,
+                              int T, int d, int E, hipStream_t s);
+hipError_t launch_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w,
+                       hipStream_t s);
+size_t route_ws_bytes(int d, int E, int T);
+
+hipError_t launch_dispatch(const int32_t *ids, int T, int E, int k, int32_t *offsets,
+                           int32_t *sorted_pair, int32_t *pair_pos, void *ws, hipStream_t s);
+size_t dispatch_ws_bytes(int E, int T, int k);
+
+hipError_t launch_ffn_small(const moe_layer &L, const uint16_t *x, int T, int k,
+                            const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
+                            float *y_shared, void *ws, hipStream_t s);
+size_t ffn_small_ws_bytes(int d, int f, int E, int T, int k);
+constexpr int kSmallTMax = 32;
+
+hipError_t launch_ffn_prefill(const moe_layer &L, const uint16_t *x, int T, int k,
+                              const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
+                              float *y_shared, void *ws, hipStream_t s);
+size_t ffn_prefill_ws_bytes(int d, int f, int E, int T, int k);
+
+hipError_t launch_combine(const float *y_pairs, const float *y_shared, const int32_t *pair_pos,
+                          const float *w, int T, int k, int d, float *out, hipStream_t s);
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,97 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function
+include/moe.h declares, and rejects bad arguments on the host before any
+HIP call (so these run without a GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def q():
+    import quantized_moe_route_amd as q
+    return q
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(q):
+    names = _declared()
+    assert {"moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine"} <= set(names)
+    lib = C.CDLL(q.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(q.ENTRY_POINTS)
+
+
+def test_version_and_status_strings(q):
+    assert q.moe_abi_version() == 1
+    for s in range(5):
+        assert isinstance(q.moe_status_string(s), str) and q.moe_status_string(s)
+
+
+A = 4096  # a 256-aligned fake device address; validation fails before it is used
+
+
+def test_route_validation(q):
+    E_ = q.MOE_ERR_INVALID_ARGUMENT
+    r = lambda *a: q.moe_route(*a, check=False)
+    assert r(A, A, None, A, 1, 2048, 0, 1, A, A, A, 1 << 20) == E_          # E < 1
+    assert r(A, A, None, A, 1, 2048, 1025, 1, A, A, A, 1 << 20) == E_       # E > 1024
+    assert r(A, A, None, A, 1, 2048, 16, 17, A, A, A, 1 << 20) == E_        # k > E
+    assert r(A, A, None, A, -1, 2048, 16, 2, A, A, A, 1 << 20) == E_        # T < 0
+    assert r(None, A, None, A, 1, 2048, 16, 2, A, A, A, 1 << 20) == E_      # x missing
+    assert r(A, None, A, A, 1, 2048, 16, 2, A, A, A, 1 << 20) == E_         # logits-in with bias
+    assert r(A + 4, A, None, A, 1, 2048, 16, 2, A, A, A, 1 << 20) == E_     # misaligned
+    assert r(A, A, None, A, 1, 2000, 16, 2, A, A, A, 1 << 20) == q.MOE_ERR_UNSUPPORTED
+    assert r(A, A, None, A, 1, 2048, 16, 2, A, A, None, 0) == q.MOE_ERR_WORKSPACE
+    assert r(A, A, None, A, 1, 2048, 16, 2, A, A, A + 16, 1 << 20) == q.MOE_ERR_WORKSPACE
+    assert r(A, A, None, A, 4, 2048, 512, 10, A, A, A, 4096) == q.MOE_ERR_WORKSPACE
+    assert r(A, A, None, A, 0, 2048, 16, 2, A, A, A, 1 << 20) == q.MOE_OK    # T = 0: no-op
+
+
+def test_dispatch_and_combine_validation(q):
+    d = lambda *a: q.moe_dispatch(*a, check=False)
+    assert d(None, 4, 16, 2, A, A, A, A, 1 << 20) == q.MOE_ERR_INVALID_ARGUMENT
+    assert d(A, 4, 16, 0, A, A, A, A, 1 << 20) == q.MOE_ERR_INVALID_ARGUMENT
+    assert d(A, 4, 16, 2, A, A, A, None, 0) == q.MOE_ERR_WORKSPACE
+    assert d(A, 0, 16, 2, A, A, A, A, 1 << 20) == q.MOE_OK
+    c = lambda *a: q.moe_combine(*a, check=False)
+    assert c(A, A, A, A, 3, 2, 2048, None) == q.MOE_ERR_INVALID_ARGUMENT
+    assert c(A, A, A, A, 3, 2, 100, A) == q.MOE_ERR_UNSUPPORTED
+    assert c(A, A, A, A, 3, 0, 2048, A) == q.MOE_ERR_INVALID_ARGUMENT
+    assert c(A, A, A, A, 0, 2, 2048, A) == q.MOE_OK
+
+
+def _layer(q, fmt=1, d=256, f=128, E=16, hi=None, mn=A):
+    qm = q.make_qmat(A, hi, A, mn)
+    return q.moe_layer(fmt, d, f, E, qm, qm, qm, qm, qm, qm)
+
+
+def test_ffn_validation(q):
+    f = lambda L, *a: q.moe_expert_ffn(L, *a, check=False)
+    ws = 1 << 24
+    assert f(_layer(q, fmt=3), A, 4, 2, A, A, A, A, A, ws) == q.MOE_ERR_UNSUPPORTED
+    assert f(_layer(q, d=200), A, 4, 2, A, A, A, A, A, ws) == q.MOE_ERR_UNSUPPORTED
+    assert f(_layer(q, hi=A), A, 4, 2, A, A, A, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT  # Q2 with hi
+    assert f(_layer(q, fmt=2, hi=None, mn=None), A, 4, 2, A, A, A, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert f(_layer(q, fmt=2, hi=A, mn=A), A, 4, 2, A, A, A, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert f(_layer(q), None, 4, 2, A, A, A, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert f(_layer(q), A, 4, 17, A, A, A, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert f(_layer(q), A, 4, 2, A, A, A, A, A, 16) == q.MOE_ERR_WORKSPACE
+    assert f(_layer(q), A, 0, 2, A, A, A, A, A, ws) == q.MOE_OK
+
+
+def test_workspace_size_monotone(q):
+    s1 = q.moe_workspace_size(2048, 768, 512, 1, 10)
+    s4 = q.moe_workspace_size(2048, 768, 512, 4, 10)
+    s8k = q.moe_workspace_size(2048, 768, 512, 8192, 10)
+    assert 0 < s1 <= s4 <= s8k and s1 % 256 == 0

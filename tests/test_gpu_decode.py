@@ -1,0 +1,245 @@
+"""GPU parity, decode / MTP-verify shapes (T <= 32): the HIP path through the
+C ABI against the CPU oracle on the same seeded inputs.
+
+Bars: ids, offsets, permutation bit-exact (on identical logits);
+float outputs max|gpu - oracle| <= 2e-3 * rms(oracle).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import packing
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def q():
+    _need_gpu()
+    import quantized_moe_route_amd as q
+    return q
+
+
+def _rel_err(gpu, ref):
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref ** 2))
+    return float(np.max(np.abs(np.asarray(gpu, np.float64) - ref)) / rms)
+
+
+def _upload(L, w):
+    from quantized_moe_route_amd.layer import DeviceLayer
+    return DeviceLayer.from_host(w.fmt, w.d_model, w.d_ff, w.n_experts, L, L.router, L.bias)
+
+
+def _x_dev(x_bits):
+    return torch.from_numpy(x_bits.view(np.int16)).cuda()
+
+
+def _run(q, dl, w, x_bits, T=None, logits=None):
+    from quantized_moe_route_amd.layer import alloc_buffers, run_layer
+    T = x_bits.shape[0] if T is None else T
+    b = alloc_buffers(dl, T, w.k)
+    if logits is not None:
+        b.logits[:T].copy_(torch.from_numpy(logits))
+    run_layer(dl, _x_dev(x_bits), b, logits_in=logits is not None)
+    torch.cuda.synchronize()
+    return b
+
+
+def _check_layer(q, w, L, x_bits, b):
+    """Full parity of one layer run against the oracle, routing on GPU logits."""
+    T, k, E, d = x_bits.shape[0], w.k, w.n_experts, w.d_model
+    lg_gpu = b.logits[:T].cpu().numpy()
+    lg_ref = oracle.router_logits(x_bits, L.router, L.bias)
+    assert _rel_err(lg_gpu, lg_ref) <= 1e-5
+    ids_ref, w_ref = oracle.topk_softmax(lg_gpu, k)
+    ids = b.ids[:T].cpu().numpy()
+    assert np.array_equal(ids, ids_ref)
+    assert np.max(np.abs(b.w[:T].cpu().numpy() - w_ref)) <= 1e-6
+    off_ref, sp_ref, pp_ref = oracle.dispatch(ids_ref, E)
+    assert np.array_equal(b.offsets.cpu().numpy(), off_ref)
+    assert np.array_equal(b.sorted_pair[:T * k].cpu().numpy(), sp_ref)
+    assert np.array_equal(b.pair_pos[:T * k].cpu().numpy(), pp_ref)
+    flat = ids_ref.ravel()
+    re = np.concatenate([flat[sp_ref], -np.ones(T, np.int32)]).astype(np.int32)
+    rt = np.concatenate([sp_ref // k, np.arange(T)]).astype(np.int32)
+    y_ref = oracle.expert_rows(L, w.fmt, d, w.d_ff, E, x_bits, re, rt)
+    P = T * k
+    assert _rel_err(b.y_pairs[:P].cpu().numpy(), y_ref[:P]) <= TOL
+    assert _rel_err(b.y_shared[:T].cpu().numpy(), y_ref[P:]) <= TOL
+    _, _, out_ref = oracle.layer(L, w.fmt, d, w.d_ff, E, k, x_bits, logits=lg_gpu)
+    err = _rel_err(b.out[:T].cpu().numpy(), out_ref)
+    assert err <= TOL, err
+    return err
+
+
+@pytest.mark.parametrize("wid", [0, 1, 2])
+def test_workload_layer_parity(q, wid):
+    w = synth.WORKLOADS[wid]
+    print(f"workload {w.name}", flush=True)
+    L = synth.gen_layer(w, layer=0)
+    x = synth.gen_x(w, layer=0)
+    dl = _upload(L, w)
+    b = _run(q, dl, w, x)
+    err = _check_layer(q, w, L, x, b)
+    print(f"max|err|/rms = {err:.3e}")
+
+
+@pytest.mark.parametrize("fmt,T,E,k,d,f", [
+    (1, 1, 16, 2, 256, 128), (2, 2, 64, 8, 256, 256), (1, 3, 64, 8, 384, 128),
+    (2, 5, 32, 4, 128, 384), (1, 17, 16, 2, 256, 128), (2, 32, 64, 10, 256, 128),
+    (1, 9, 1, 1, 128, 128), (2, 4, 8, 8, 128, 128), (1, 16, 512, 10, 128, 128),
+])
+def test_shape_sweep_parity(q, fmt, T, E, k, d, f):
+    w = synth.custom(d, f, E, k, T, fmt=fmt, zipf_s=1.3 if fmt == 2 else 0.0, wid=200 + T)
+    print(f"shape {w}", flush=True)
+    L = synth.gen_layer(w)
+    x = synth.gen_x(w)
+    b = _run(q, _upload(L, w), w, x)
+    _check_layer(q, w, L, x, b)
+
+
+def test_route_logits_input_ties(q):
+    """Forced ties (integer logits, signed zeros, all-equal rows): ids bit-exact."""
+    T, E, k = 8, 512, 10
+    rng = np.random.default_rng(3)
+    lg = np.round(rng.standard_normal((T, E)) * 2).astype(np.float32)
+    lg[1] = 0.0
+    lg[1, ::2] = -0.0
+    lg[2] = 7.0
+    lg[3, 100:110] = 50.0
+    lg_d = torch.from_numpy(lg).cuda()
+    ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    wt = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    q.moe_route(None, None, None, lg_d, T, 2048, E, k, ids, wt, ws, 4096)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = oracle.topk_softmax(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.max(np.abs(wt.cpu().numpy() - w_ref)) <= 1e-6
+
+
+@pytest.mark.parametrize("T,E,k,skew", [
+    (1, 512, 10, 0), (4, 512, 10, 1), (100, 64, 8, 0), (512, 512, 8, 0), (8192, 512, 10, 0),
+    (8192, 512, 10, 2), (300, 1024, 16, 0), (65, 16, 16, 0), (1000, 1, 1, 0),
+])
+def test_dispatch_parity(q, T, E, k, skew):
+    rng = np.random.default_rng(T * 7 + E + k)
+    if skew == 0:
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    elif skew == 1:
+        ids = np.tile(np.arange(k, dtype=np.int32), (T, 1))
+    else:  # Zipf-like skew: many tokens share a few experts
+        pr = 1.0 / np.arange(1, E + 1) ** 1.3
+        pr /= pr.sum()
+        ids = np.stack([rng.choice(E, size=k, replace=False, p=pr) for _ in range(T)]).astype(np.int32)
+    ws_bytes = q.moe_workspace_size(128, 128, E, T, k)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    q.moe_dispatch(torch.from_numpy(ids).cuda(), T, E, k, off, sp, pp, ws, ws_bytes)
+    torch.cuda.synchronize()
+    o_ref, sp_ref, pp_ref = oracle.dispatch(ids, E)
+    assert np.array_equal(off.cpu().numpy(), o_ref)
+    assert np.array_equal(sp.cpu().numpy(), sp_ref)
+    assert np.array_equal(pp.cpu().numpy(), pp_ref)
+
+
+def test_combine_parity(q):
+    rng = np.random.default_rng(9)
+    T, k, d = 33, 10, 2048
+    P = T * k
+    yp = rng.standard_normal((P, d)).astype(np.float32)
+    ys = rng.standard_normal((T, d)).astype(np.float32)
+    pp = rng.permutation(P).astype(np.int32)
+    wt = rng.random((T, k)).astype(np.float32)
+    out = torch.empty(T, d, device="cuda")
+    c = lambda a: torch.from_numpy(a).cuda()
+    q.moe_combine(c(yp), c(ys), c(pp), c(wt), T, k, d, out)
+    torch.cuda.synchronize()
+    ref = oracle.combine(yp, ys, pp, wt, T, k, d)
+    assert np.max(np.abs(out.cpu().numpy() - ref)) <= 1e-5 * np.sqrt(np.mean(ref.astype(np.float64) ** 2))
+
+
+def test_identical_experts_and_zero_experts(q):
+    """Pins that carry over to the GPU: identical routed experts make the output
+    independent of routing; zero routed weights leave the shared expert."""
+    from quantized_moe_route_amd.layer import DeviceLayer, alloc_buffers, run_layer
+    rng = np.random.default_rng(12)
+    d, f, E, k, T = 256, 128, 16, 4, 6
+    for mode in ("same", "zero"):
+        mats = {}
+        for name, (n, rows, K) in {"gate": (E, f, d), "up": (E, f, d), "down": (E, d, f),
+                                   "sh_gate": (1, f, d), "sh_up": (1, f, d), "sh_down": (1, d, f)}.items():
+            m, _ = packing.random_mat(rng, 1, n, rows, K, zero=(mode == "zero" and n == E))
+            if mode == "same" and n == E:
+                for pl in ("lo", "scale", "min"):
+                    a = getattr(m, pl)
+                    per = a.size // E
+                    a[:] = np.tile(a[:per], E)
+            mats[name] = m
+
+        class H:
+            pass
+        for n_, m in mats.items():
+            setattr(H, n_, m)
+        x = synth._f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+        outs = []
+        for s in range(2):
+            lg = rng.standard_normal((T, E)).astype(np.float32)
+            dl = DeviceLayer.from_host(1, d, f, E, H, np.zeros((d, E), np.float32))
+            b = alloc_buffers(dl, T, k)
+            b.logits.copy_(torch.from_numpy(lg))
+            run_layer(dl, _x_dev(x), b, logits_in=True)
+            torch.cuda.synchronize()
+            outs.append(b.out.cpu().numpy())
+            _, _, ref = oracle.layer(H, 1, d, f, E, k, x, logits=lg)
+            assert _rel_err(outs[-1], ref) <= TOL
+        if mode == "same":
+            assert _rel_err(outs[0], outs[1]) <= TOL
+
+
+def test_repeatable_bitwise(q):
+    w = synth.WORKLOADS[0]
+    L = synth.gen_layer(w)
+    x = synth.gen_x(w)
+    dl = _upload(L, w)
+    b1 = _run(q, dl, w, x)
+    o1, i1 = b1.out.cpu().numpy().copy(), b1.ids.cpu().numpy().copy()
+    b2 = _run(q, dl, w, x)
+    assert np.array_equal(o1, b2.out.cpu().numpy()) and np.array_equal(i1, b2.ids.cpu().numpy())
+
+
+def test_token_independence_gpu(q):
+    """A T=4 batch equals four T=1 runs within tolerance (MTP verify sanity)."""
+    w = synth.custom(256, 128, 16, 2, 4, wid=300)
+    L = synth.gen_layer(w)
+    x = synth.gen_x(w)
+    dl = _upload(L, w)
+    b = _run(q, dl, w, x)
+    full = b.out.cpu().numpy().copy()
+    for t in range(4):
+        bt = _run(q, dl, w, x[t:t + 1])
+        assert _rel_err(bt.out[:1].cpu().numpy(), full[t:t + 1]) <= TOL
+
+
+def test_t_zero_is_noop(q):
+    ws = torch.zeros(8192, dtype=torch.uint8, device="cuda")
+    lg = torch.full((1, 16), 3.0, device="cuda")
+    ids = torch.full((1, 2), -7, dtype=torch.int32, device="cuda")
+    wt = torch.full((1, 2), -7.0, device="cuda")
+    x = torch.zeros(1, 256, dtype=torch.int16, device="cuda")
+    wr = torch.zeros(256, 16, device="cuda")
+    q.moe_route(x, wr, None, lg, 0, 256, 16, 2, ids, wt, ws, 8192)
+    torch.cuda.synchronize()
+    assert torch.all(ids == -7) and torch.all(wt == -7.0) and torch.all(lg == 3.0)
