@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""MoE-layer throughput on one MI355X: routed, block-quantized experts.
+
+A step is one pass of the whole layer path over one batch of synthetic input:
+moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine (for the 48-layer
+workloads: all 48 layers in sequence).  Inputs are resident in HBM before the
+timed region.  The K timed steps (and the W warm-up steps) are captured into
+one HIP graph each and replayed once, bracketed by stream synchronisation and
+HIP events on the launch stream.  Per-call GPU durations come from one more
+graph per call (back-to-back launches of that call over consecutive steps'
+inputs), timed with HIP events on the same stream.
+
+Workloads (default 1):
+  1  decode, T=1, d=2048, f=768, E=512, top-10 + shared, Q2 block-32, 1 layer
+     (16 copies of the layer at distinct HBM addresses, cycled per step, and a
+     fresh x per step, so the selected experts are not cache-resident)
+  2  MTP verify, T=4 through 48 layers, Q3 block-32, Zipf(1.1) router bias
+  3  prefill, T=8192, Q2, 1 layer           4  prefill, T=8192, Q3, 48 layers
+
+Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix
+METRIC = "MoE-layer tokens/s (decode T=1/4, prefill 8192); % HBM BW or % MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def expert_bytes(w) -> int:
+    """Packed bytes of one expert (gate + up + down)."""
+    import synth
+    s = sum(synth.plane_sizes(w.fmt, r, K)["lo"] + synth.plane_sizes(w.fmt, r, K)["hi"] +
+            2 * (synth.plane_sizes(w.fmt, r, K)["scale"] + synth.plane_sizes(w.fmt, r, K)["min"])
+            for r, K in ((w.d_ff, w.d_model), (w.d_ff, w.d_model), (w.d_model, w.d_ff)))
+    return s
+
+
+def clone_layer(dl):
+    from quantized_moe_route_amd.layer import DeviceLayer
+    planes = {n: tuple(None if t is None else t.clone() for t in p) for n, p in dl.planes.items()}
+    return DeviceLayer(dl.fmt, dl.d_model, dl.d_ff, dl.n_experts, planes, dl.router.clone(),
+                       None if dl.bias is None else dl.bias.clone())
+
+
+def cpu_baseline(w, host_layer, router, bias, xs_host, seconds):
+    """The oracle, as is, on a bounded sample of the same workload."""
+    import oracle
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        x = xs_host[n % len(xs_host)]
+        oracle.layer(host_layer, w.fmt, w.d_model, w.d_ff, w.n_experts, w.k, x, wr=router, bias=bias)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return n, el
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--copies", type=int, default=16, help="layer copies cycled (workload 1)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import synth.device as sdev
+    import quantized_moe_route_amd as q
+    from quantized_moe_route_amd import hip
+    from quantized_moe_route_amd.layer import DeviceLayer, alloc_buffers, run_layer
+
+    w = synth.WORKLOADS[args.workload]
+    if w.T > 32:
+        raise SystemExit("prefill workloads are measured once the prefill path is built")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K = args.steps if args.steps is not None else (200 if w.layers == 1 else 20)
+    W = args.warmup if args.warmup is not None else (20 if w.layers == 1 else 3)
+    S = K + W
+    stream = torch.cuda.Stream(device=dev)
+    sh = stream.cuda_stream
+
+    # ---------------------------------------------------------------- inputs
+    t_setup = time.perf_counter()
+    if w.layers == 1:
+        L0 = synth.gen_layer(w, layer=0)
+        dl0 = DeviceLayer.from_host(w.fmt, w.d_model, w.d_ff, w.n_experts, L0, L0.router, L0.bias,
+                                    device=dev)
+        layers = [dl0] + [clone_layer(dl0) for _ in range(args.copies - 1)]
+        host_layer, host_router, host_bias = L0, L0.router, L0.bias
+    else:
+        layers = []
+        for li in range(w.layers):
+            planes = sdev.layer_planes(w, li, device=dev)
+            wr, bias = sdev.router(w, li, device=dev)
+            layers.append(DeviceLayer(w.fmt, w.d_model, w.d_ff, w.n_experts, planes, wr, bias))
+        host_layer = sdev.to_host(layers[0].planes)
+        host_router = layers[0].router.cpu().numpy()
+        host_bias = None if layers[0].bias is None else layers[0].bias.cpu().numpy()
+    n_lay = w.layers
+    # x[step][layer]
+    xs = [[sdev.x(w, li, s, device=dev) for li in range(n_lay)] for s in range(S)]
+    with torch.cuda.stream(stream):
+        buf = alloc_buffers(layers[0], w.T, w.k, device=dev, stream=stream)
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f}s: {w.name}, {len(layers)} layer buffers, "
+        f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
+
+    def layer_of(step, li):
+        return layers[li] if n_lay > 1 else layers[step % len(layers)]
+
+    # ------------------------------------------------- parity spot check (oracle)
+    import oracle
+    run_layer(layer_of(0, 0), xs[0][0], buf, stream=sh)
+    hip.stream_synchronize(sh)
+    x0 = xs[0][0].cpu().numpy().view(np.uint16)
+    lg = buf.logits[:w.T].cpu().numpy()
+    ids_ref, _ = oracle.topk_softmax(lg, w.k)
+    ids_ok = bool(np.array_equal(buf.ids[:w.T].cpu().numpy(), ids_ref))
+    _, _, out_ref = oracle.layer(host_layer, w.fmt, w.d_model, w.d_ff, w.n_experts, w.k, x0,
+                                 logits=lg)
+    rms = float(np.sqrt(np.mean(out_ref.astype(np.float64) ** 2)))
+    err = float(np.max(np.abs(buf.out[:w.T].cpu().numpy().astype(np.float64) - out_ref)) / rms)
+    log(f"parity step 0: ids exact={ids_ok} max|err|/rms={err:.3e}")
+
+    # ------------------------------------------------------------ capture
+    ev_start, ev_end = hip.Event(), hip.Event()
+
+    def call(c, s, li):
+        L = layer_of(s, li)
+        x = xs[s][li]
+        if c == "route":
+            q.moe_route(x, L.router, L.bias, buf.logits, w.T, w.d_model, w.n_experts, w.k,
+                        buf.ids, buf.w, buf.ws, buf.ws_bytes, sh)
+        elif c == "dispatch":
+            q.moe_dispatch(buf.ids, w.T, w.n_experts, w.k, buf.offsets, buf.sorted_pair,
+                           buf.pair_pos, buf.ws, buf.ws_bytes, sh)
+        elif c == "expert_ffn":
+            q.moe_expert_ffn(L.struct, x, w.T, w.k, buf.offsets, buf.sorted_pair, buf.y_pairs,
+                             buf.y_shared, buf.ws, buf.ws_bytes, sh)
+        else:
+            q.moe_combine(buf.y_pairs, buf.y_shared, buf.pair_pos, buf.w, w.T, w.k, w.d_model,
+                          buf.out, sh)
+
+    calls = ["route", "dispatch", "expert_ffn", "combine"]
+
+    def enqueue(step0, nsteps):
+        for s in range(step0, step0 + nsteps):
+            for li in range(n_lay):
+                for c in calls:
+                    call(c, s, li)
+
+    if args.eager:
+        enqueue(K, W)
+        hip.stream_synchronize(sh)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev_start.record(sh)
+        enqueue(0, K)
+        ev_end.record(sh)
+        hip.stream_synchronize(sh)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    else:
+        with hip.Graph(sh) as g_warm:
+            enqueue(K, W)
+        with hip.Graph(sh) as g_timed:
+            enqueue(0, K)
+        g_warm.launch()
+        hip.stream_synchronize(sh)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev_start.record(sh)
+        g_timed.launch()
+        ev_end.record(sh)
+        hip.stream_synchronize(sh)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3
+    gpu_ms = ev_start.elapsed_ms(ev_end)
+    out_graph = buf.out[:w.T].clone()
+
+    # replay check: the last timed step again, eagerly; deterministic kernels
+    enqueue(K - 1, 1)
+    hip.stream_synchronize(sh)
+    replay_ok = bool(torch.equal(out_graph, buf.out[:w.T]))
+
+    # per-call GPU durations: a graph of G back-to-back launches of one call
+    # (inputs of consecutive steps / layer copies), events around the graph
+    G = min(K, 64)
+    avg_us = {}
+    for c in calls:
+        with hip.Graph(sh) as gc:
+            for s in range(G):
+                call(c, s, s % n_lay if n_lay > 1 else 0)
+        gc.launch()
+        e0, e1 = hip.Event(), hip.Event()
+        e0.record(sh)
+        gc.launch()
+        e1.record(sh)
+        hip.stream_synchronize(sh)
+        avg_us[c] = 1e3 * e0.elapsed_ms(e1) / G
+
+    # algorithmic bytes of one moe_expert_ffn launch: distinct experts used + shared
+    eb = expert_bytes(w)
+    groups = []
+    for s in range(K):
+        for li in range(n_lay):
+            L = layer_of(s, li)
+            q.moe_route(xs[s][li], L.router, L.bias, buf.logits, w.T, w.d_model, w.n_experts,
+                        w.k, buf.ids, buf.w, buf.ws, buf.ws_bytes, sh)
+            q.moe_dispatch(buf.ids, w.T, w.n_experts, w.k, buf.offsets, buf.sorted_pair,
+                           buf.pair_pos, buf.ws, buf.ws_bytes, sh)
+            hip.stream_synchronize(sh)
+            off = buf.offsets.cpu().numpy()
+            groups.append(int(np.count_nonzero(np.diff(off))) + 1)
+    rows = w.T * w.k + w.T
+    act_bytes = rows * w.d_model * (2 + 4)                 # x row in, y row out
+    ffn_bytes = float(np.mean(groups)) * eb + act_bytes
+    achieved = ffn_bytes / (avg_us["expert_ffn"] * 1e-6) / 1e9
+    layer_bytes = ffn_bytes + w.d_model * w.n_experts * 4  # + router weights
+
+    ms_per_step = wall_ms / K
+    tokens_per_s = w.T * K / (wall_ms / 1e3)
+
+    # ------------------------------------------------------------ CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as orc
+        xs_host = [xs[s][0].cpu().numpy().view(np.uint16) for s in range(min(S, 64))]
+        n, el = cpu_baseline(w, host_layer, host_router, host_bias, xs_host, args.cpu_seconds)
+        cpu = {"value": n * w.T / el / n_lay if n_lay > 1 else n * w.T / el,
+               "unit": "tokens/s" + (" (48-layer stack)" if n_lay > 1 else ""),
+               "cores": orc.num_threads(), "kind": "oracle",
+               "sample": f"{n} oracle layer evaluations of T={w.T} tokens on layer 0 "
+                         f"({el:.1f} s); stack rate = per-layer rate / {n_lay}" if n_lay > 1 else
+                         f"{n} oracle layer evaluations of T={w.T} token(s) ({el:.1f} s)"}
+
+    res = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s" + (" (through the 48-layer stack)" if n_lay > 1 else ""),
+        "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded generator; random weights of the stated shape)",
+        "config": {"workload": w.name, "d_model": w.d_model, "d_ff": w.d_ff,
+                   "n_experts": w.n_experts, "top_k": w.k, "shared_experts": 1, "T": w.T,
+                   "layers": n_lay, "format": "Q2_B32" if w.fmt == 1 else "Q3_B32",
+                   "layer_copies": len(layers), "mode": "eager" if args.eager else "hip-graph"},
+        "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn (gateup_small + down_small)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": ffn_bytes, "avg_groups": float(np.mean(groups))},
+        "cpu_baseline": cpu,
+        "gpu_ms_per_step": gpu_ms / K,
+        "per_call_us": avg_us,
+        "layer_hbm_frac": layer_bytes * n_lay / (gpu_ms / K * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "parity": {"ids_exact": ids_ok, "max_err_over_rms": err, "graph_replay_bitwise": replay_ok},
+    }
+    print(json.dumps(res))
+    if not (ids_ok and err <= 2e-3 and replay_ok):
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

@@ -16,9 +16,14 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# small-batch expert kernels read every matrix-core result right away: keep
+# the results in VGPRs instead of accumulation registers
+EXTRA = {"ffn_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-    r = subprocess.run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj],
+    r = subprocess.run([HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj],
                        capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

@@ -131,6 +131,28 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     return v;
 }
 
+// The n-th (0-based) set bit of a 64-bit mask (wave-uniform), -1 if none.
+__device__ __forceinline__ int nth_set_bit(unsigned long long m, int n) {
+    int base = 0;
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) {
+        const unsigned long long lo = m & ((1ull << w) - 1ull);
+        const int c = __popcll(lo);
+        if (n >= c) {
+            n -= c;
+            m >>= w;
+            base += w;
+        } else {
+            m = lo;
+        }
+    }
+    return (m & 1ull) && n == 0 ? base : -1;
+}
+
+// Expert e is non-empty iff offsets[e+1] > offsets[e].  Lane l looks at
+// experts l, l+64, ...; all loads are issued before any is used.  One ballot
+// per row of 64 experts counts the non-empty ones in index order; the row
+// holding the target is kept and its set bit located once at the end.
 __device__ inline bool find_group(const int32_t *__restrict__ offsets, int E, int T, int P, int slot,
                                   Group &g) {
     if (slot == 0) {
@@ -142,34 +164,37 @@ __device__ inline bool find_group(const int32_t *__restrict__ offsets, int E, in
     }
     const int target = slot - 1;  // index among non-empty experts
     const int l = __lane_id();
-    const int per = (E + 63) / 64;
-    const int e0 = l * per;
-    int cnt = 0;
-    for (int i = 0; i < per; ++i) {
-        int e = e0 + i;
-        if (e < E && offsets[e + 1] > offsets[e]) ++cnt;
+    const int per = (E + 63) / 64;  // <= 16
+    // unconditional loads at clamped indices (a predicated load would be
+    // waited for inside its own branch); out-of-range experts read as empty
+    int lo[16], hi[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = l + 64 * i;
+        const int ec = e < E ? e : E - 1;
+        const int a = offsets[ec], b = offsets[ec + 1];
+        lo[i] = a;
+        hi[i] = e < E ? b : a;
     }
-    const int incl = wave_incl_scan(cnt);
-    const int excl = incl - cnt;
-    int found = -1;
-    if (target >= excl && target < incl) {
-        int c = excl;
-        for (int i = 0; i < per; ++i) {
-            int e = e0 + i;
-            if (e < E && offsets[e + 1] > offsets[e]) {
-                if (c == target) { found = e; break; }
-                ++c;
-            }
+    int cum = 0, sel_row = -1, sel_n = 0;
+    unsigned long long sel_m = 0ull;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (i < per) {
+            const unsigned long long m = __ballot(hi[i] > lo[i]);
+            const int c = __popcll(m);
+            const bool hit = sel_row < 0 && target < cum + c;
+            sel_m = hit ? m : sel_m;
+            sel_n = hit ? target - cum : sel_n;
+            sel_row = hit ? i : sel_row;
+            cum += c;
         }
     }
-    // exactly one lane (or none) found it
-    unsigned long long m = __ballot(found >= 0);
-    if (m == 0ull) return false;
-    const int src = __ffsll((long long)m) - 1;
-    const int e = __shfl(found, src, 64);
-    g.expert = e;
-    g.row0 = offsets[e];
-    g.nrows = offsets[e + 1] - offsets[e];
+    if (sel_row < 0) return false;
+    const int found = 64 * sel_row + nth_set_bit(sel_m, sel_n);
+    g.expert = found;
+    g.row0 = offsets[found];
+    g.nrows = offsets[found + 1] - g.row0;
     g.hrow0 = g.row0;
     return true;
 }

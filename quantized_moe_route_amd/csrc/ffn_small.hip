@@ -38,13 +38,104 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
 }
 
+// Everything one lane needs from one 16 x 128 unit of the gate and up
+// matrices, plus its activation pieces.  Loads of a batch of units are all
+// issued before the first is used, so a wave pays HBM latency once per batch.
 template <int FMT, int MT>
-__global__ __launch_bounds__(256) void gateup_small_kernel(
+struct GateUpUnit {
+    u32x2 lg, lu, sg, su, mg, mu;
+    uint32_t hg, hu;
+    u32x4 A[MT][4];
+};
+
+template <int FMT, int MT>
+__device__ __forceinline__ void gateup_load_w(GateUpUnit<FMT, MT> &U, const QMatDev &Wg,
+                                              const QMatDev &Wu, size_t unit, int lane, int rr) {
+    U.lg = *reinterpret_cast<const u32x2 *>(Wg.lo + unit * 512 + lane * 8);
+    U.lu = *reinterpret_cast<const u32x2 *>(Wu.lo + unit * 512 + lane * 8);
+    if constexpr (FMT == MOE_FMT_Q3_B32) {
+        U.hg = *reinterpret_cast<const uint32_t *>(Wg.hi + unit * 256 + lane * 4);
+        U.hu = *reinterpret_cast<const uint32_t *>(Wu.hi + unit * 256 + lane * 4);
+    }
+    U.sg = *reinterpret_cast<const u32x2 *>(Wg.scale + unit * 64 + rr * 4);
+    U.su = *reinterpret_cast<const u32x2 *>(Wu.scale + unit * 64 + rr * 4);
+    if constexpr (FMT == MOE_FMT_Q2_B32) {
+        U.mg = *reinterpret_cast<const u32x2 *>(Wg.min + unit * 64 + rr * 4);
+        U.mu = *reinterpret_cast<const u32x2 *>(Wu.min + unit * 64 + rr * 4);
+    }
+}
+
+template <int FMT, int MT>
+__device__ __forceinline__ void gateup_load_x(GateUpUnit<FMT, MT> &U, int u, int gq,
+                                              const uint16_t *const *xrow) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            U.A[mt][j] = *reinterpret_cast<const u32x4 *>(xrow[mt] + u * 128 + j * 32 + gq * 8);
+}
+
+template <int J, bool F16, int FMT>
+__device__ __forceinline__ void block_operands(uint32_t lo_dw, uint32_t hi_w, u32x4 &B, u32x4 &H) {
+    B = lo_operand<J & 1, F16>(lo_dw);
+    if constexpr (FMT == MOE_FMT_Q3_B32) H = hi_operand<J, F16>(hi_w);
+}
+
+__device__ __forceinline__ float half_of(const u32x2 &v, int j) {
+    return half_bits_to_float((uint16_t)(v[j >> 1] >> (16 * (j & 1))));
+}
+
+// IMAX = number of valid D rows per lane group i (compile time): 1 for a
+// single-token batch, 2 for two tokens, 4 otherwise.  The epilogue touches
+// only those rows, so small batches pay no selects.
+template <int FMT, int MT, int IMAX, int J>
+__device__ __forceinline__ void gateup_block(const GateUpUnit<FMT, MT> &U, f32x4 *ag, f32x4 *au) {
+    const u32x4 ones = {kOneBf16x2, kOneBf16x2, kOneBf16x2, kOneBf16x2};
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    u32x4 Bg, Bu, Hg, Hu;
+    block_operands<J, false, FMT>(U.lg[J >> 1], U.hg, Bg, Hg);
+    block_operands<J, false, FMT>(U.lu[J >> 1], U.hu, Bu, Hu);
+    const float dg = half_of(U.sg, J), du = half_of(U.su, J);
+    float mgv = 0.f, muv = 0.f;
+    if constexpr (FMT == MOE_FMT_Q2_B32) {
+        mgv = half_of(U.mg, J);
+        muv = half_of(U.mu, J);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        f32x4 pg = mfma_bf16(U.A[mt][J], Bg, zero);
+        f32x4 pu = mfma_bf16(U.A[mt][J], Bu, zero);
+        if constexpr (FMT == MOE_FMT_Q3_B32) {
+            pg = mfma_bf16(U.A[mt][J], Hg, pg);
+            pu = mfma_bf16(U.A[mt][J], Hu, pu);
+        }
+        const f32x4 xs = mfma_bf16(U.A[mt][J], ones, zero);
+#pragma unroll
+        for (int i = 0; i < IMAX; ++i) {
+            if constexpr (FMT == MOE_FMT_Q2_B32) {
+                ag[mt][i] = fmaf(dg, pg[i], fmaf(mgv, xs[i], ag[mt][i]));
+                au[mt][i] = fmaf(du, pu[i], fmaf(muv, xs[i], au[mt][i]));
+            } else {
+                ag[mt][i] = fmaf(dg, fmaf(-4.0f, xs[i], pg[i]), ag[mt][i]);
+                au[mt][i] = fmaf(du, fmaf(-4.0f, xs[i], pu[i]), au[mt][i]);
+            }
+        }
+    }
+}
+
+#ifndef MOE_DECODE_BATCH
+#define MOE_DECODE_BATCH 4
+#endif
+constexpr int kBatch = MOE_DECODE_BATCH;   // units prefetched per wave per batch
+
+// grid: (d_ff/16 row tiles, 1 + min(E, P) group slots); NW waves split K.
+template <int FMT, int MT, int IMAX, int NW>
+__global__ __launch_bounds__(64 * NW) void gateup_small_kernel(
     QMatDev gate, QMatDev up, QMatDev sgate, QMatDev sup, const uint16_t *__restrict__ x, int T,
     int k, int d, int f, int E, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ sorted_pair, uint16_t *__restrict__ h_hi,
     uint16_t *__restrict__ h_lo) {
-    __shared__ float red[4][MT][2][4][64];
+    __shared__ float red[NW][MT][2][IMAX][64];
     const int nt = blockIdx.x;
     const int slot = blockIdx.y;
     const int P = T * k;
@@ -60,18 +151,18 @@ __global__ __launch_bounds__(256) void gateup_small_kernel(
     const int KC = d / 128;
     const size_t ubase = ((size_t)e * (f / 16) + nt) * KC;
     const int nrows = grp.nrows;
-    const int imax = nrows >= 4 ? 4 : nrows;
 
-    // activation rows owned by this lane as A-operand row rr of each M tile
-    const uint16_t *xrow[MT];
+    // Token of the lane's A-operand row rr in each M tile.  Lanes past the
+    // group's last row use its last row (their D rows are never stored); the
+    // loads are unconditional so they are in flight together.  The
+    // sorted_pair loads go out first, then the first batch of weights; only
+    // the activation loads wait for the token ids.
+    int tok[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int r = mt * 16 + rr;
-        xrow[mt] = nullptr;
-        if (r < nrows) {
-            const int t = shared ? r : sorted_pair[grp.row0 + r] / k;
-            xrow[mt] = x + (size_t)t * d;
-        }
+        int r = mt * 16 + rr;
+        r = r < nrows ? r : nrows - 1;
+        tok[mt] = shared ? r : sorted_pair[grp.row0 + r];
     }
     f32x4 ag[MT], au[MT];
 #pragma unroll
@@ -79,106 +170,64 @@ __global__ __launch_bounds__(256) void gateup_small_kernel(
         ag[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         au[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const u32x4 ones = {kOneBf16x2, kOneBf16x2, kOneBf16x2, kOneBf16x2};
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-
-    for (int u = wv; u < KC; u += 4) {
-        const size_t U = ubase + u;
-        const u32x2 lg = *reinterpret_cast<const u32x2 *>(Wg.lo + U * 512 + lane * 8);
-        const u32x2 lu = *reinterpret_cast<const u32x2 *>(Wu.lo + U * 512 + lane * 8);
-        uint32_t hg = 0, hu = 0;
-        if constexpr (FMT == MOE_FMT_Q3_B32) {
-            hg = *reinterpret_cast<const uint32_t *>(Wg.hi + U * 256 + lane * 4);
-            hu = *reinterpret_cast<const uint32_t *>(Wu.hi + U * 256 + lane * 4);
+    const uint16_t *xrow[MT];
+    for (int u0 = wv; u0 < KC; u0 += NW * kBatch) {
+        GateUpUnit<FMT, MT> U[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int u = u0 + NW * b;
+            if (u < KC) gateup_load_w(U[b], Wg, Wu, ubase + u, lane, rr);
         }
-        const u32x2 sg = *reinterpret_cast<const u32x2 *>(Wg.scale + U * 64 + rr * 4);
-        const u32x2 su = *reinterpret_cast<const u32x2 *>(Wu.scale + U * 64 + rr * 4);
-        u32x2 mg = {0u, 0u}, mu = {0u, 0u};
-        if constexpr (FMT == MOE_FMT_Q2_B32) {
-            mg = *reinterpret_cast<const u32x2 *>(Wg.min + U * 64 + rr * 4);
-            mu = *reinterpret_cast<const u32x2 *>(Wu.min + U * 64 + rr * 4);
+        __asm__ volatile("" ::: "memory");
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) xrow[mt] = x + (size_t)(shared ? tok[mt] : tok[mt] / k) * d;
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int u = u0 + NW * b;
+            if (u < KC) gateup_load_x(U[b], u, gq, xrow);
         }
-        u32x4 A[MT][4];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                A[mt][j] = u32x4{0u, 0u, 0u, 0u};
-                if (xrow[mt])
-                    A[mt][j] = *reinterpret_cast<const u32x4 *>(xrow[mt] + u * 128 + j * 32 + gq * 8);
-            }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t dwg = lg[j >> 1], dwu = lu[j >> 1];
-            u32x4 Bg, Bu, Hg, Hu;
-            if (j & 1) {
-                Bg = lo_operand<1, false>(dwg);
-                Bu = lo_operand<1, false>(dwu);
-            } else {
-                Bg = lo_operand<0, false>(dwg);
-                Bu = lo_operand<0, false>(dwu);
-            }
-            if constexpr (FMT == MOE_FMT_Q3_B32) {
-                switch (j) {
-                    case 0: Hg = hi_operand<0, false>(hg); Hu = hi_operand<0, false>(hu); break;
-                    case 1: Hg = hi_operand<1, false>(hg); Hu = hi_operand<1, false>(hu); break;
-                    case 2: Hg = hi_operand<2, false>(hg); Hu = hi_operand<2, false>(hu); break;
-                    default: Hg = hi_operand<3, false>(hg); Hu = hi_operand<3, false>(hu); break;
-                }
-            }
-            const uint32_t sgw = sg[j >> 1] >> (16 * (j & 1));
-            const uint32_t suw = su[j >> 1] >> (16 * (j & 1));
-            const float dg = half_bits_to_float((uint16_t)sgw), du = half_bits_to_float((uint16_t)suw);
-            float mgv = 0.f, muv = 0.f;
-            if constexpr (FMT == MOE_FMT_Q2_B32) {
-                mgv = half_bits_to_float((uint16_t)(mg[j >> 1] >> (16 * (j & 1))));
-                muv = half_bits_to_float((uint16_t)(mu[j >> 1] >> (16 * (j & 1))));
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                f32x4 pg = mfma_bf16(A[mt][j], Bg, zero);
-                f32x4 pu = mfma_bf16(A[mt][j], Bu, zero);
-                if constexpr (FMT == MOE_FMT_Q3_B32) {
-                    pg = mfma_bf16(A[mt][j], Hg, pg);
-                    pu = mfma_bf16(A[mt][j], Hu, pu);
-                }
-                const f32x4 xs = mfma_bf16(A[mt][j], ones, zero);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (i < imax || mt > 0) {
-                        if constexpr (FMT == MOE_FMT_Q2_B32) {
-                            ag[mt][i] += dg * pg[i] + mgv * xs[i];
-                            au[mt][i] += du * pu[i] + muv * xs[i];
-                        } else {
-                            ag[mt][i] += dg * (pg[i] - 4.0f * xs[i]);
-                            au[mt][i] += du * (pu[i] - 4.0f * xs[i]);
-                        }
-                    }
-                }
+        for (int b = 0; b < kBatch; ++b) {
+            if (u0 + NW * b < KC) {
+                gateup_block<FMT, MT, IMAX, 0>(U[b], ag, au);
+                gateup_block<FMT, MT, IMAX, 1>(U[b], ag, au);
+                gateup_block<FMT, MT, IMAX, 2>(U[b], ag, au);
+                gateup_block<FMT, MT, IMAX, 3>(U[b], ag, au);
             }
         }
     }
+    if constexpr (NW > 1) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            red[wv][mt][0][i][lane] = ag[mt][i];
-            red[wv][mt][1][i][lane] = au[mt][i];
-        }
-    __syncthreads();
-    if (wv != 0) return;
+            for (int i = 0; i < IMAX; ++i) {
+                red[wv][mt][0][i][lane] = ag[mt][i];
+                red[wv][mt][1][i][lane] = au[mt][i];
+            }
+        __syncthreads();
+        if (wv != 0) return;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < IMAX; ++i) {
+                float gs = red[0][mt][0][i][lane], us = red[0][mt][1][i][lane];
+#pragma unroll
+                for (int w2 = 1; w2 < NW; ++w2) {
+                    gs += red[w2][mt][0][i][lane];
+                    us += red[w2][mt][1][i][lane];
+                }
+                ag[mt][i] = gs;
+                au[mt][i] = us;
+            }
+    }
     const int n = nt * 16 + rr;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < IMAX; ++i) {
             const int r = mt * 16 + gq * 4 + i;
             if (r >= nrows) continue;
-            const float gs = (red[0][mt][0][i][lane] + red[1][mt][0][i][lane]) +
-                             (red[2][mt][0][i][lane] + red[3][mt][0][i][lane]);
-            const float us = (red[0][mt][1][i][lane] + red[1][mt][1][i][lane]) +
-                             (red[2][mt][1][i][lane] + red[3][mt][1][i][lane]);
-            const float h = swiglu(gs, us);
+            const float h = swiglu(ag[mt][i], au[mt][i]);
             const _Float16 hh = static_cast<_Float16>(h);
             const float rem = h - static_cast<float>(hh);
             const size_t off = (size_t)(grp.hrow0 + r) * f + n;
@@ -188,11 +237,45 @@ __global__ __launch_bounds__(256) void gateup_small_kernel(
 }
 
 template <int FMT, int MT>
-__global__ __launch_bounds__(256) void down_small_kernel(
+struct DownUnit {
+    u32x2 lw, sw, mw;
+    uint32_t hw;
+    u32x4 A[MT][4];
+};
+
+template <int FMT, int MT, int IMAX, int J>
+__device__ __forceinline__ void down_block(const DownUnit<FMT, MT> &U, f32x4 *acc) {
+    const u32x4 ones = {kOneF16x2, kOneF16x2, kOneF16x2, kOneF16x2};
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    u32x4 B, H;
+    block_operands<J, true, FMT>(U.lw[J >> 1], U.hw, B, H);
+    const float dv = half_of(U.sw, J);
+    float mv = 0.f;
+    if constexpr (FMT == MOE_FMT_Q2_B32) mv = half_of(U.mw, J);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        f32x4 p = mfma_f16(U.A[mt][J], B, zero);
+        if constexpr (FMT == MOE_FMT_Q3_B32) p = mfma_f16(U.A[mt][J], H, p);
+        const f32x4 hs = mfma_f16(U.A[mt][J], ones, zero);
+#pragma unroll
+        for (int i = 0; i < IMAX; ++i) {
+            if constexpr (FMT == MOE_FMT_Q2_B32)
+                acc[mt][i] = fmaf(dv, p[i], fmaf(mv, hs[i], acc[mt][i]));
+            else
+                acc[mt][i] = fmaf(dv, fmaf(-4.0f, hs[i], p[i]), acc[mt][i]);
+        }
+    }
+}
+
+// grid: (d_model/16 row tiles, group slots); NW waves split K = d_ff.
+// A tile row rr < 8 holds h_hi of group row 8*mt + rr, row 8 + rr its h_lo;
+// D rows 4*gq + i: hi rows in lanes gq = 0, 1 and lo rows in gq = 2, 3.
+template <int FMT, int MT, int IMAX, int NW>
+__global__ __launch_bounds__(64 * NW) void down_small_kernel(
     QMatDev down, QMatDev sdown, const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
     int T, int k, int d, int f, int E, const int32_t *__restrict__ offsets,
     float *__restrict__ y_pairs, float *__restrict__ y_shared) {
-    __shared__ float red[4][MT][4][64];
+    __shared__ float red[NW][MT][IMAX][64];
     const int ot = blockIdx.x;
     const int slot = blockIdx.y;
     const int P = T * k;
@@ -207,89 +290,75 @@ __global__ __launch_bounds__(256) void down_small_kernel(
     const int KC = f / 128;
     const size_t ubase = ((size_t)e * (d / 16) + ot) * KC;
     const int nrows = grp.nrows;
-    const int imax = nrows >= 4 ? 4 : nrows;
 
-    // A-operand row rr: rows 0..7 = h_hi of group rows 8mt.., rows 8..15 = h_lo
+    // rows past the group's last read its last row (never stored; keeps the
+    // loads unconditional)
     const uint16_t *hrow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int r = mt * 8 + (rr & 7);
-        hrow[mt] = nullptr;
-        if (r < nrows) hrow[mt] = (rr < 8 ? h_hi : h_lo) + (size_t)(grp.hrow0 + r) * f;
+        int r = mt * 8 + (rr & 7);
+        r = r < nrows ? r : nrows - 1;
+        hrow[mt] = (rr < 8 ? h_hi : h_lo) + (size_t)(grp.hrow0 + r) * f;
     }
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const u32x4 ones = {kOneF16x2, kOneF16x2, kOneF16x2, kOneF16x2};
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-    for (int u = wv; u < KC; u += 4) {
-        const size_t U = ubase + u;
-        const u32x2 lw = *reinterpret_cast<const u32x2 *>(W.lo + U * 512 + lane * 8);
-        uint32_t hw = 0;
-        if constexpr (FMT == MOE_FMT_Q3_B32)
-            hw = *reinterpret_cast<const uint32_t *>(W.hi + U * 256 + lane * 4);
-        const u32x2 sw = *reinterpret_cast<const u32x2 *>(W.scale + U * 64 + rr * 4);
-        u32x2 mw = {0u, 0u};
-        if constexpr (FMT == MOE_FMT_Q2_B32)
-            mw = *reinterpret_cast<const u32x2 *>(W.min + U * 64 + rr * 4);
-        u32x4 A[MT][4];
+    for (int u0 = wv; u0 < KC; u0 += NW * kBatch) {
+        DownUnit<FMT, MT> U[kBatch];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int b = 0; b < kBatch; ++b) {
+            const int u = u0 + NW * b;
+            if (u < KC) {
+                const size_t unit = ubase + u;
+                U[b].lw = *reinterpret_cast<const u32x2 *>(W.lo + unit * 512 + lane * 8);
+                if constexpr (FMT == MOE_FMT_Q3_B32)
+                    U[b].hw = *reinterpret_cast<const uint32_t *>(W.hi + unit * 256 + lane * 4);
+                U[b].sw = *reinterpret_cast<const u32x2 *>(W.scale + unit * 64 + rr * 4);
+                if constexpr (FMT == MOE_FMT_Q2_B32)
+                    U[b].mw = *reinterpret_cast<const u32x2 *>(W.min + unit * 64 + rr * 4);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                A[mt][j] = u32x4{0u, 0u, 0u, 0u};
-                if (hrow[mt])
-                    A[mt][j] = *reinterpret_cast<const u32x4 *>(hrow[mt] + u * 128 + j * 32 + gq * 8);
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        U[b].A[mt][j] =
+                            *reinterpret_cast<const u32x4 *>(hrow[mt] + u * 128 + j * 32 + gq * 8);
             }
+        }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            u32x4 B = (j & 1) ? lo_operand<1, true>(lw[j >> 1]) : lo_operand<0, true>(lw[j >> 1]);
-            u32x4 H;
-            if constexpr (FMT == MOE_FMT_Q3_B32) {
-                switch (j) {
-                    case 0: H = hi_operand<0, true>(hw); break;
-                    case 1: H = hi_operand<1, true>(hw); break;
-                    case 2: H = hi_operand<2, true>(hw); break;
-                    default: H = hi_operand<3, true>(hw); break;
-                }
-            }
-            const float dv = half_bits_to_float((uint16_t)(sw[j >> 1] >> (16 * (j & 1))));
-            float mv = 0.f;
-            if constexpr (FMT == MOE_FMT_Q2_B32)
-                mv = half_bits_to_float((uint16_t)(mw[j >> 1] >> (16 * (j & 1))));
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                f32x4 p = mfma_f16(A[mt][j], B, zero);
-                if constexpr (FMT == MOE_FMT_Q3_B32) p = mfma_f16(A[mt][j], H, p);
-                const f32x4 hs = mfma_f16(A[mt][j], ones, zero);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (i < imax || mt > 0) {
-                        if constexpr (FMT == MOE_FMT_Q2_B32)
-                            acc[mt][i] += dv * p[i] + mv * hs[i];
-                        else
-                            acc[mt][i] += dv * (p[i] - 4.0f * hs[i]);
-                    }
-                }
+        for (int b = 0; b < kBatch; ++b) {
+            if (u0 + NW * b < KC) {
+                down_block<FMT, MT, IMAX, 0>(U[b], acc);
+                down_block<FMT, MT, IMAX, 1>(U[b], acc);
+                down_block<FMT, MT, IMAX, 2>(U[b], acc);
+                down_block<FMT, MT, IMAX, 3>(U[b], acc);
             }
         }
     }
+    if constexpr (NW > 1) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[wv][mt][i][lane] = acc[mt][i];
-    __syncthreads();
-    if (wv != 0) return;
-    // sum the four K slices, then hi (rows 0..7, lanes 0..31) + lo (rows 8..15, lanes 32..63)
+            for (int i = 0; i < IMAX; ++i) red[wv][mt][i][lane] = acc[mt][i];
+        __syncthreads();
+        if (wv != 0) return;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < IMAX; ++i) {
+                float v = red[0][mt][i][lane];
+#pragma unroll
+                for (int w2 = 1; w2 < NW; ++w2) v += red[w2][mt][i][lane];
+                acc[mt][i] = v;
+            }
+    }
+    // hi (rows 0..7, lanes 0..31) + lo (rows 8..15, lanes 32..63)
     const int o = ot * 16 + rr;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float part = (red[0][mt][i][lane] + red[1][mt][i][lane]) +
-                               (red[2][mt][i][lane] + red[3][mt][i][lane]);
-            const float y = part + __shfl_xor(part, 32, 64);
+        for (int i = 0; i < IMAX; ++i) {
+            const float y = acc[mt][i] + __shfl_xor(acc[mt][i], 32, 64);
             const int r = mt * 8 + gq * 4 + i;
             if (gq >= 2 || r >= nrows) continue;
             if (shared)
@@ -308,19 +377,43 @@ size_t ffn_small_ws_bytes(int d, int f, int E, int T, int k) {
     return 2 * rows * f * sizeof(uint16_t) + 256;
 }
 
-template <int FMT, int MTG, int MTD>
+template <int FMT, int MTG, int MTD, int IMAX>
 static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k,
                              const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
                              float *y_shared, uint16_t *h_hi, uint16_t *h_lo, hipStream_t s) {
     const int d = L.d_model, f = L.d_ff, E = L.n_experts;
     const int P = T * k;
     const int slots = 1 + (E < P ? E : P);
-    hipLaunchKernelGGL((gateup_small_kernel<FMT, MTG>), dim3(f / 16, slots), dim3(256), 0, s,
-                       qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up), x, T, k, d, f, E, offsets,
-                       sorted_pair, h_hi, h_lo);
-    hipLaunchKernelGGL((down_small_kernel<FMT, MTD>), dim3(d / 16, slots), dim3(256), 0, s,
-                       qm(L.down), qm(L.sh_down), h_hi, h_lo, T, k, d, f, E, offsets, y_pairs,
-                       y_shared);
+#ifndef MOE_GU_WAVES
+#define MOE_GU_WAVES 4
+#endif
+#ifndef MOE_DN_WAVES
+#define MOE_DN_WAVES 2
+#endif
+    constexpr int NWG = MOE_GU_WAVES, NWD = MOE_DN_WAVES;   // waves per workgroup (split K)
+    hipLaunchKernelGGL((gateup_small_kernel<FMT, MTG, IMAX, NWG>), dim3(f / 16, slots),
+                       dim3(64 * NWG), 0, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up), x,
+                       T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo);
+    hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD>), dim3(d / 16, slots),
+                       dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, T, k, d, f, E,
+                       offsets, y_pairs, y_shared);
+}
+
+template <int FMT>
+static void launch_small_t(const moe_layer &L, const uint16_t *x, int T, int k,
+                           const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
+                           float *y_shared, uint16_t *h_hi, uint16_t *h_lo, hipStream_t s) {
+    // M tiles: gate/up 16 rows per tile, down 8 rows (hi over lo) per tile
+    if (T == 1)
+        launch_small_fmt<FMT, 1, 1, 1>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
+    else if (T == 2)
+        launch_small_fmt<FMT, 1, 1, 2>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
+    else if (T <= 8)
+        launch_small_fmt<FMT, 1, 1, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
+    else if (T <= 16)
+        launch_small_fmt<FMT, 1, 2, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
+    else
+        launch_small_fmt<FMT, 2, 4, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
 }
 
 hipError_t launch_ffn_small(const moe_layer &L, const uint16_t *x, int T, int k,
@@ -329,22 +422,10 @@ hipError_t launch_ffn_small(const moe_layer &L, const uint16_t *x, int T, int k,
     const size_t rows = (size_t)T * k + T;
     uint16_t *h_hi = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + kWsHeader);
     uint16_t *h_lo = h_hi + ((rows * L.d_ff + 127) / 128) * 128;
-    // M tiles: gate/up 16 rows per tile, down 8 rows (hi over lo) per tile
-    if (L.format == MOE_FMT_Q2_B32) {
-        if (T <= 8)
-            launch_small_fmt<MOE_FMT_Q2_B32, 1, 1>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
-        else if (T <= 16)
-            launch_small_fmt<MOE_FMT_Q2_B32, 1, 2>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
-        else
-            launch_small_fmt<MOE_FMT_Q2_B32, 2, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
-    } else {
-        if (T <= 8)
-            launch_small_fmt<MOE_FMT_Q3_B32, 1, 1>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
-        else if (T <= 16)
-            launch_small_fmt<MOE_FMT_Q3_B32, 1, 2>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
-        else
-            launch_small_fmt<MOE_FMT_Q3_B32, 2, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
-    }
+    if (L.format == MOE_FMT_Q2_B32)
+        launch_small_t<MOE_FMT_Q2_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
+    else
+        launch_small_t<MOE_FMT_Q3_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
     return hipGetLastError();
 }
 

@@ -108,15 +108,19 @@ def test_shape_sweep_parity(q, fmt, T, E, k, d, f):
     _check_layer(q, w, L, x, b)
 
 
-def test_route_logits_input_ties(q):
-    """Forced ties (integer logits, signed zeros, all-equal rows): ids bit-exact."""
-    T, E, k = 8, 512, 10
-    rng = np.random.default_rng(3)
+@pytest.mark.parametrize("T,E,k", [(8, 512, 10), (5, 64, 64), (3, 1024, 32), (4, 16, 16),
+                                   (6, 100, 33), (257, 512, 10), (2, 1024, 1024)])
+def test_route_logits_input_ties(q, T, E, k):
+    """Forced ties (integer logits, signed zeros, all-equal rows): ids bit-exact,
+    for the ranking selection (k <= 32) and the serial one (k > 32)."""
+    rng = np.random.default_rng(3 + T + E + k)
     lg = np.round(rng.standard_normal((T, E)) * 2).astype(np.float32)
     lg[1] = 0.0
     lg[1, ::2] = -0.0
-    lg[2] = 7.0
-    lg[3, 100:110] = 50.0
+    if T > 2:
+        lg[2] = 7.0
+    if T > 3:
+        lg[3, E // 4:E // 4 + min(10, E // 2)] = 50.0
     lg_d = torch.from_numpy(lg).cuda()
     ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
     wt = torch.empty(T, k, dtype=torch.float32, device="cuda")
@@ -126,6 +130,30 @@ def test_route_logits_input_ties(q):
     ids_ref, w_ref = oracle.topk_softmax(lg, k)
     assert np.array_equal(ids.cpu().numpy(), ids_ref)
     assert np.max(np.abs(wt.cpu().numpy() - w_ref)) <= 1e-6
+
+
+@pytest.mark.parametrize("T,E,k,d", [(8, 1024, 32, 256), (7, 300, 40, 384), (1, 33, 33, 128),
+                                     (8, 512, 10, 2048)])
+def test_route_small_path_shapes(q, T, E, k, d):
+    """One-launch router (T <= 8): logits within tolerance, ids bit-exact on them."""
+    rng = np.random.default_rng(T * E + k)
+    x = synth._f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    wr = (rng.standard_normal((d, E)) / np.sqrt(d)).astype(np.float32)
+    bias = rng.standard_normal(E).astype(np.float32)
+    ws_bytes = q.moe_workspace_size(d, 128, E, T, k)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    lg = torch.empty(T, E, device="cuda")
+    ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    wt = torch.empty(T, k, device="cuda")
+    c = lambda a: torch.from_numpy(a).cuda()
+    for rep in range(2):      # second call checks the self-resetting arrival counter
+        q.moe_route(c(x.view(np.int16)), c(wr), c(bias), lg, T, d, E, k, ids, wt, ws, ws_bytes)
+        torch.cuda.synchronize()
+        lg_h = lg.cpu().numpy()
+        assert _rel_err(lg_h, oracle.router_logits(x, wr, bias)) <= 1e-5
+        ids_ref, w_ref = oracle.topk_softmax(lg_h, k)
+        assert np.array_equal(ids.cpu().numpy(), ids_ref)
+        assert np.max(np.abs(wt.cpu().numpy() - w_ref)) <= 1e-6
 
 
 @pytest.mark.parametrize("T,E,k,skew", [
