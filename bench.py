@@ -15,7 +15,11 @@ Workloads (default 1):
      (16 copies of the layer at distinct HBM addresses, cycled per step, and a
      fresh x per step, so the selected experts are not cache-resident)
   2  MTP verify, T=4 through 48 layers, Q3 block-32, Zipf(1.1) router bias
-  3  prefill, T=8192, Q2, 1 layer           4  prefill, T=8192, Q3, 48 layers
+  3  prefill, T=8192, Q2, 1 layer           4  prefill, T=8192, Q3, 48 layers,
+                                               Zipf(1.3) router bias
+Decode workloads report the expert FFN call against HBM bandwidth (bytes of
+the distinct experts selected + activations); prefill workloads against the
+dense fp16/bf16 matrix-core peak (2*M*N*K of the expert GEMMs).
 
 Prints one JSON line on stdout.
 """
@@ -78,7 +82,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
-    ap.add_argument("--copies", type=int, default=16, help="layer copies cycled (workload 1)")
+    ap.add_argument("--copies", type=int, default=None,
+                    help="layer copies cycled, single-layer workloads (default 16 decode, 1 prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
@@ -98,12 +103,17 @@ def main():
     from quantized_moe_route_amd.layer import DeviceLayer, alloc_buffers, run_layer
 
     w = synth.WORKLOADS[args.workload]
-    if w.T > 32:
-        raise SystemExit("prefill workloads are measured once the prefill path is built")
+    prefill = w.T > 32
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    K = args.steps if args.steps is not None else (200 if w.layers == 1 else 20)
-    W = args.warmup if args.warmup is not None else (20 if w.layers == 1 else 3)
+    if prefill:
+        K = args.steps if args.steps is not None else (20 if w.layers == 1 else 3)
+        W = args.warmup if args.warmup is not None else (3 if w.layers == 1 else 1)
+        n_copies = 1 if args.copies is None else args.copies
+    else:
+        K = args.steps if args.steps is not None else (200 if w.layers == 1 else 20)
+        W = args.warmup if args.warmup is not None else (20 if w.layers == 1 else 3)
+        n_copies = 16 if args.copies is None else args.copies
     S = K + W
     stream = torch.cuda.Stream(device=dev)
     sh = stream.cuda_stream
@@ -114,7 +124,7 @@ def main():
         L0 = synth.gen_layer(w, layer=0)
         dl0 = DeviceLayer.from_host(w.fmt, w.d_model, w.d_ff, w.n_experts, L0, L0.router, L0.bias,
                                     device=dev)
-        layers = [dl0] + [clone_layer(dl0) for _ in range(args.copies - 1)]
+        layers = [dl0] + [clone_layer(dl0) for _ in range(n_copies - 1)]
         host_layer, host_router, host_bias = L0, L0.router, L0.bias
     else:
         layers = []
@@ -138,18 +148,28 @@ def main():
         return layers[li] if n_lay > 1 else layers[step % len(layers)]
 
     # ------------------------------------------------- parity spot check (oracle)
+    # decode: every token; prefill: a seeded sample of tokens (the oracle
+    # evaluates them one by one from the GPU's logits).  ids and the
+    # permutation are checked in full either way.
     import oracle
     run_layer(layer_of(0, 0), xs[0][0], buf, stream=sh)
     hip.stream_synchronize(sh)
     x0 = xs[0][0].cpu().numpy().view(np.uint16)
     lg = buf.logits[:w.T].cpu().numpy()
     ids_ref, _ = oracle.topk_softmax(lg, w.k)
-    ids_ok = bool(np.array_equal(buf.ids[:w.T].cpu().numpy(), ids_ref))
-    _, _, out_ref = oracle.layer(host_layer, w.fmt, w.d_model, w.d_ff, w.n_experts, w.k, x0,
-                                 logits=lg)
+    off_ref, sp_ref, _ = oracle.dispatch(ids_ref, w.n_experts)
+    ids_ok = bool(np.array_equal(buf.ids[:w.T].cpu().numpy(), ids_ref)
+                  and np.array_equal(buf.offsets.cpu().numpy(), off_ref)
+                  and np.array_equal(buf.sorted_pair[:w.T * w.k].cpu().numpy(), sp_ref))
+    rows = (np.sort(np.random.default_rng(7).choice(w.T, size=16, replace=False))
+            if prefill else np.arange(w.T))
+    _, _, out_ref = oracle.layer(host_layer, w.fmt, w.d_model, w.d_ff, w.n_experts, w.k,
+                                 x0[rows], logits=lg[rows])
     rms = float(np.sqrt(np.mean(out_ref.astype(np.float64) ** 2)))
-    err = float(np.max(np.abs(buf.out[:w.T].cpu().numpy().astype(np.float64) - out_ref)) / rms)
-    log(f"parity step 0: ids exact={ids_ok} max|err|/rms={err:.3e}")
+    err = float(np.max(np.abs(buf.out[:w.T].cpu().numpy()[rows].astype(np.float64) - out_ref))
+                / rms)
+    log(f"parity step 0 ({len(rows)} tokens): ids/permutation exact={ids_ok} "
+        f"max|err|/rms={err:.3e}")
 
     # ------------------------------------------------------------ capture
     ev_start, ev_end = hip.Event(), hip.Event()
@@ -215,7 +235,7 @@ def main():
 
     # per-call GPU durations: a graph of G back-to-back launches of one call
     # (inputs of consecutive steps / layer copies), events around the graph
-    G = min(K, 64)
+    G = min(K, 8 if prefill else 64)
     avg_us = {}
     for c in calls:
         with hip.Graph(sh) as gc:
@@ -229,10 +249,12 @@ def main():
         hip.stream_synchronize(sh)
         avg_us[c] = 1e3 * e0.elapsed_ms(e1) / G
 
-    # algorithmic bytes of one moe_expert_ffn launch: distinct experts used + shared
+    # algorithmic work of one moe_expert_ffn launch.
+    #   decode: bytes = distinct experts used + shared, x rows in, y rows out
+    #   prefill: flops = (P + T) rows x (gate + up + down) = rows * 6*d*f
     eb = expert_bytes(w)
     groups = []
-    for s in range(K):
+    for s in range(min(K, 64)):
         for li in range(n_lay):
             L = layer_of(s, li)
             q.moe_route(xs[s][li], L.router, L.bias, buf.logits, w.T, w.d_model, w.n_experts,
@@ -242,10 +264,25 @@ def main():
             hip.stream_synchronize(sh)
             off = buf.offsets.cpu().numpy()
             groups.append(int(np.count_nonzero(np.diff(off))) + 1)
-    rows = w.T * w.k + w.T
-    act_bytes = rows * w.d_model * (2 + 4)                 # x row in, y row out
+    rows_ffn = w.T * w.k + w.T
+    act_bytes = rows_ffn * w.d_model * (2 + 4)             # x row in, y row out
     ffn_bytes = float(np.mean(groups)) * eb + act_bytes
-    achieved = ffn_bytes / (avg_us["expert_ffn"] * 1e-6) / 1e9
+    ffn_flops = float(rows_ffn) * 6.0 * w.d_model * w.d_ff
+    t_ffn = avg_us["expert_ffn"] * 1e-6
+    if prefill:
+        achieved = ffn_flops / t_ffn / 1e12
+        roof = {"bound": "mfma", "kernel": "moe_expert_ffn (pf_gemm gate/up + down, "
+                                           "routed + shared, item build, x to fp16)",
+                "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                "flops_per_launch": ffn_flops, "avg_groups": float(np.mean(groups)),
+                "hbm_gbs_algorithmic": ffn_bytes / t_ffn / 1e9}
+    else:
+        achieved = ffn_bytes / t_ffn / 1e9
+        roof = {"bound": "hbm", "kernel": "moe_expert_ffn (gateup_small + down_small)",
+                "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "bytes_per_launch": ffn_bytes, "avg_groups": float(np.mean(groups))}
     layer_bytes = ffn_bytes + w.d_model * w.n_experts * 4  # + router weights
 
     ms_per_step = wall_ms / K
@@ -255,14 +292,23 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle as orc
-        xs_host = [xs[s][0].cpu().numpy().view(np.uint16) for s in range(min(S, 64))]
+        if prefill:
+            # 256-token slices of the chunk, layer 0, until the time is up
+            chunk = 256
+            x_full = xs[0][0].cpu().numpy().view(np.uint16)
+            xs_host = [x_full[i:i + chunk] for i in range(0, w.T, chunk)]
+        else:
+            chunk = w.T
+            xs_host = [xs[s][0].cpu().numpy().view(np.uint16) for s in range(min(S, 64))]
         n, el = cpu_baseline(w, host_layer, host_router, host_bias, xs_host, args.cpu_seconds)
-        cpu = {"value": n * w.T / el / n_lay if n_lay > 1 else n * w.T / el,
-               "unit": "tokens/s" + (" (48-layer stack)" if n_lay > 1 else ""),
+        rate = n * chunk / el
+        what = (f"{n} oracle layer evaluations of {chunk}-token slices of the T={w.T} chunk"
+                if prefill else f"{n} oracle layer evaluations of T={w.T} token(s)")
+        cpu = {"value": rate / n_lay,
+               "unit": "tokens/s" + (" (through the 48-layer stack)" if n_lay > 1 else ""),
                "cores": orc.num_threads(), "kind": "oracle",
-               "sample": f"{n} oracle layer evaluations of T={w.T} tokens on layer 0 "
-                         f"({el:.1f} s); stack rate = per-layer rate / {n_lay}" if n_lay > 1 else
-                         f"{n} oracle layer evaluations of T={w.T} token(s) ({el:.1f} s)"}
+               "sample": f"{what} on layer 0 ({el:.1f} s)" +
+                         (f"; stack rate = per-layer rate / {n_lay}" if n_lay > 1 else "")}
 
     res = {
         "metric": METRIC,
@@ -271,21 +317,22 @@ def main():
         "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp16" if prefill else "bf16",
         "data": "synthetic (seeded generator; random weights of the stated shape)",
         "config": {"workload": w.name, "d_model": w.d_model, "d_ff": w.d_ff,
                    "n_experts": w.n_experts, "top_k": w.k, "shared_experts": 1, "T": w.T,
                    "layers": n_lay, "format": "Q2_B32" if w.fmt == 1 else "Q3_B32",
-                   "layer_copies": len(layers), "mode": "eager" if args.eager else "hip-graph"},
-        "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn (gateup_small + down_small)",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "bytes_per_launch": ffn_bytes, "avg_groups": float(np.mean(groups))},
+                   "layer_copies": len(layers) if n_lay == 1 else 1,
+                   "mode": "eager" if args.eager else "hip-graph"},
+        "roofline": roof,
         "cpu_baseline": cpu,
         "gpu_ms_per_step": gpu_ms / K,
         "per_call_us": avg_us,
-        "layer_hbm_frac": layer_bytes * n_lay / (gpu_ms / K * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "parity": {"ids_exact": ids_ok, "max_err_over_rms": err, "graph_replay_bitwise": replay_ok},
+        ("layer_mfma_frac" if prefill else "layer_hbm_frac"):
+            (ffn_flops * n_lay / (gpu_ms / K * 1e-3) / 1e12 / BF16_PEAK_TFLOPS) if prefill else
+            (layer_bytes * n_lay / (gpu_ms / K * 1e-3) / 1e9 / HBM_PEAK_GBS),
+        "parity": {"ids_exact": ids_ok, "max_err_over_rms": err, "tokens_checked": int(len(rows)),
+                   "graph_replay_bitwise": replay_ok},
     }
     print(json.dumps(res))
     if not (ids_ok and err <= 2e-3 and replay_ok):

@@ -6,22 +6,33 @@
 // plus the shared expert; [guide] tech.okbari.net "Strata와 Qwen3.8-Flash-Next…",
 // section "24GB에 들어가는 원리": a wide batch touches many experts at once.
 //
-// Grouped GEMM on the matrix cores (v_mfma_f32_16x16x32_f16, fp32 accumulate):
+// Grouped GEMM on the matrix cores (v_mfma_f32_32x32x16_f16, fp32 accumulate):
 //   gate/up:  [rows of group g] x d  .  (W_gate_g | W_up_g)^T   -> h = silu(g)*u
 //   down:     [rows of group g] x f  .  W_down_g^T              -> y (fp32)
-// Work items are (group, 128-row chunk, column tile).  A prepass builds the
-// item table on the device from the dispatch offsets (the shared expert's
-// chunks first, then every non-empty routed expert), so no host readback is
-// needed and heavily loaded experts simply contribute more items.
+//
+// Scheduling.  A prepass turns the dispatch offsets into work items (group,
+// 128-row chunk) on the device: groups are ordered by work, largest first
+// (the shared expert counts double: it runs two products per weight), and
+// dealt round-robin to the eight XCDs, so all chunks of one expert -- which
+// share its weights -- and all column tiles of one chunk -- which share its
+// activation rows -- land in one XCD's L2.  The GEMM kernels are persistent:
+// each workgroup takes (item, column tile) units by atomic ticket from its own
+// XCD's queue, largest first, then steals from the other queues once its own
+// is empty.  An expert with thousands of rows is just many units; a skewed
+// router costs no idle tail beyond one unit.
 //
 // Operands:
 //   A (activations): x converted once to fp16 (exact for bf16 values in fp16
-//     range), or h; a 128-row tile per K step goes global -> registers -> LDS.
-//   B (weights): never touches LDS.  The storage unit (16 rows x 128 columns,
-//     lane-major) gives each lane exactly its 16x16x32 B-fragment bytes; the
-//     lane turns codes into fp16 with the fp4 convert and applies the block
-//     scale with one packed fp16 FMA per two weights: fp16(d*q + m) rounded
-//     once (Q3: fp16(d*(q-4))).
+//     range), or h.  Each 128-row x 128-column stage is copied global -> LDS
+//     by the direct-to-LDS loads (no registers), two stages in flight; the
+//     16-byte chunks of a row are XOR-swizzled by the row index so the
+//     fragment reads are free of bank conflicts.
+//   B (weights): never touch LDS.  Two 16-row storage units give each lane the
+//     bytes of its 32x32x16 B fragments (two 8-byte code slots per unit pair
+//     and step); the lane turns codes into fp16 with the fp4 convert and
+//     applies the block scale with one packed fp16 FMA per two weights:
+//     fp16(d*q + m) rounded once (Q3: fp16(d*(q-4))).  Dequantisation for the
+//     next 16-column k-step overlaps the matrix ops of the current one.
 // Precision: routed experts use the fp16-rounded weights and fp16 h; the
 // shared expert (weight 1 in every token's output) uses exact weights as fp16
 // hi + lo and h as fp16 hi + lo (the product lo*lo, below 2^-22 relative, is
@@ -30,9 +41,11 @@
 
 namespace moe {
 
-constexpr int PF_MT = 128;           // rows per work item
-constexpr int PF_KS = 128;           // K per step (one storage unit per row tile)
-constexpr int PF_APITCH = PF_KS + 8; // fp16 elements per LDS row (16 B pad)
+constexpr int PF_MT = 128;                        // rows per work item
+constexpr int PF_KS = 128;                        // K per pipeline stage
+constexpr int PF_STAGE = PF_MT * PF_KS * 2;       // bytes of one A stage (32 KiB)
+constexpr int PF_NXCD = 8;                        // XCDs (L2 domains) per device
+constexpr int PF_SORT = 2048;                     // sort slots, >= E + 1
 
 struct PfItem {
     int32_t expert;  // -1 = shared
@@ -41,52 +54,103 @@ struct PfItem {
     int32_t hrow0;   // first row in the h buffer
 };
 
+// Scheduling block at the head of the prefill workspace.
+struct PfSched {
+    int32_t n_items;
+    int32_t xq[PF_NXCD + 1];         // items of XCD x: [xq[x], xq[x + 1])
+    int32_t ticket[2][PF_NXCD];      // per GEMM launch, per XCD queue
+};
+static_assert(sizeof(PfSched) <= 256, "PfSched must fit its 256-byte slot");
 
 // ---------------------------------------------------------------- prepass
-// One block of 1024 threads.  Shared-expert chunks first, then routed experts
-// in index order.
+// One block of 1024 threads.  Group 0 is the shared expert (T rows), group
+// 1 + e the routed expert e.  Sort key: (work desc, group asc), work = rows
+// (x2 for the shared expert); bitonic sort over PF_SORT slots in LDS.
 __global__ __launch_bounds__(1024) void pf_build_items_kernel(const int32_t *__restrict__ offsets,
                                                               int E, int T, int P,
                                                               PfItem *__restrict__ items,
-                                                              int32_t *__restrict__ n_items) {
-    __shared__ int cnt[1024];
-    __shared__ int wsum[16];
-    const int tid = threadIdx.x;
-    const int lane = __lane_id(), wv = tid >> 6;
-    const int shared_ch = (T + PF_MT - 1) / PF_MT;
-    int rows = 0, nch = 0;
-    if (tid < E) {
-        rows = offsets[tid + 1] - offsets[tid];
-        nch = (rows + PF_MT - 1) / PF_MT;
-    }
-    // exclusive scan of nch over experts
-    const int incl = wave_incl_scan(nch);
-    if (lane == 63) wsum[wv] = incl;
-    __syncthreads();
-    if (wv == 0) {
-        const int s = lane < 16 ? wsum[lane] : 0;
-        const int si = wave_incl_scan(s);
-        if (lane < 16) wsum[lane] = si - s;
+                                                              PfSched *__restrict__ sched) {
+    __shared__ unsigned long long key[PF_SORT];
+    __shared__ int start[PF_SORT / PF_NXCD * PF_NXCD];
+    __shared__ int xcount[PF_NXCD];
+    const int tid = threadIdx.x, lane = __lane_id(), wv = tid >> 6;
+    const int G = E + 1;
+    for (int g = tid; g < PF_SORT; g += 1024) {
+        unsigned long long kk = 0;
+        if (g < G) {
+            const long rows = g == 0 ? T : offsets[g] - offsets[g - 1];
+            const unsigned long long work = g == 0 ? 2ull * rows : (unsigned long long)rows;
+            if (rows > 0) kk = (work << 11) | (unsigned long long)(2047 - g);
+        }
+        key[g] = kk;
     }
     __syncthreads();
-    const int base = shared_ch + incl - nch + wsum[wv];
-    if (tid < E) {
-        const int r0 = offsets[tid];
-        for (int c = 0; c < nch; ++c) {
-            const int n = rows - c * PF_MT < PF_MT ? rows - c * PF_MT : PF_MT;
-            items[base + c] = PfItem{tid, r0 + c * PF_MT, n, r0 + c * PF_MT};
+    // bitonic sort, descending
+    for (int size = 2; size <= PF_SORT; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const int i = 2 * tid - (tid & (stride - 1));   // lower index of this thread's pair
+            const int j = i + stride;
+            const bool desc = ((i & size) == 0);
+            const unsigned long long a = key[i], b = key[j];
+            if ((a < b) == desc) {
+                key[i] = b;
+                key[j] = a;
+            }
+            __syncthreads();
         }
     }
-    for (int c = tid; c < shared_ch; c += 1024) {
-        const int n = T - c * PF_MT < PF_MT ? T - c * PF_MT : PF_MT;
-        items[c] = PfItem{-1, c * PF_MT, n, P + c * PF_MT};
+    // rank r -> XCD r % 8, position r / 8; per-XCD exclusive scan of chunk counts
+    auto nch_of = [&](int r) -> int {
+        const unsigned long long kk = key[r];
+        if (kk == 0) return 0;
+        const int g = 2047 - (int)(kk & 2047);
+        const int rows = g == 0 ? T : offsets[g] - offsets[g - 1];
+        return (rows + PF_MT - 1) / PF_MT;
+    };
+    if (wv < PF_NXCD) {
+        int carry = 0;
+        for (int c = 0; c * 64 * PF_NXCD < PF_SORT; ++c) {
+            const int r = (c * 64 + lane) * PF_NXCD + wv;
+            const int v = r < PF_SORT ? nch_of(r) : 0;
+            const int incl = wave_incl_scan(v) + carry;
+            if (r < PF_SORT) start[r] = incl - v;
+            carry = __shfl(incl, 63);
+        }
+        if (lane == 0) xcount[wv] = carry;
     }
-    cnt[tid] = tid < E ? nch : 0;
     __syncthreads();
     if (tid == 0) {
-        int tot = shared_ch;
-        for (int e = 0; e < E; ++e) tot += cnt[e];
-        n_items[0] = tot;
+        int acc = 0;
+        for (int x = 0; x < PF_NXCD; ++x) {
+            sched->xq[x] = acc;
+            acc += xcount[x];
+        }
+        sched->xq[PF_NXCD] = acc;
+        sched->n_items = acc;
+    }
+    if (tid < 2 * PF_NXCD) sched->ticket[tid / PF_NXCD][tid % PF_NXCD] = 0;
+    int xbase[PF_NXCD];
+    {
+        int acc = 0;
+#pragma unroll
+        for (int x = 0; x < PF_NXCD; ++x) {
+            xbase[x] = acc;
+            acc += xcount[x];
+        }
+    }
+    for (int r = tid; r < PF_SORT; r += 1024) {
+        const unsigned long long kk = key[r];
+        if (kk == 0) continue;
+        const int g = 2047 - (int)(kk & 2047);
+        const int rows = g == 0 ? T : offsets[g] - offsets[g - 1];
+        const int r0 = g == 0 ? 0 : offsets[g - 1];
+        const int nch = (rows + PF_MT - 1) / PF_MT;
+        const int base = xbase[r % PF_NXCD] + start[r];
+        for (int c = 0; c < nch; ++c) {
+            const int n = rows - c * PF_MT < PF_MT ? rows - c * PF_MT : PF_MT;
+            items[base + c] = g == 0 ? PfItem{-1, c * PF_MT, n, P + c * PF_MT}
+                                     : PfItem{g - 1, r0 + c * PF_MT, n, r0 + c * PF_MT};
+        }
     }
 }
 
@@ -108,22 +172,16 @@ __global__ __launch_bounds__(256) void pf_x_to_f16_kernel(const uint16_t *__rest
 }
 
 // ------------------------------------------------------------ B fragments
-// Lane (g = lane/16, rr = lane%16) holds, per storage unit, 8 bytes of codes
-// (blocks j = 0..3, 8 codes each), a Q3 hi word, and its row's 4 scales/mins.
+// Code bytes of one lane for one storage unit and one 16-column k-step pair:
+// a storage unit holds, for lane slot (g, rr), row rr's codes at columns
+// 32j + 8g .. +8 of each 32-block j (8 bytes); the sub-block scales/mins of
+// row rr; and for Q3 one word of third bits.
 template <int FMT>
 struct BRaw {
     u32x2 lo;
     uint32_t hi;
     u32x2 sc, mn;
 };
-
-template <int FMT>
-__device__ __forceinline__ void load_braw(BRaw<FMT> &b, const QMatDev &W, size_t unit, int lane, int rr) {
-    b.lo = *reinterpret_cast<const u32x2 *>(W.lo + unit * 512 + lane * 8);
-    if constexpr (FMT == MOE_FMT_Q3_B32) b.hi = *reinterpret_cast<const uint32_t *>(W.hi + unit * 256 + lane * 4);
-    b.sc = *reinterpret_cast<const u32x2 *>(W.scale + unit * 64 + rr * 4);
-    if constexpr (FMT == MOE_FMT_Q2_B32) b.mn = *reinterpret_cast<const u32x2 *>(W.min + unit * 64 + rr * 4);
-}
 
 __device__ __forceinline__ uint32_t half_pair(const u32x2 &v, int j) {
     const uint32_t h = (v[j >> 1] >> (16 * (j & 1))) & 0xffffu;
@@ -169,7 +227,8 @@ __device__ __forceinline__ u32x4 bfrag_f16(const BRaw<FMT> &b) {
 // exact weights split as fp16 hi + lo: w = fp32(d*q + m) (exact), hi = fp16(w),
 // lo = fp16(w - hi).  qword holds two fp16 codes (Q3: lo + 4*bit2).
 template <int FMT>
-__device__ __forceinline__ void split_pair(uint32_t qword, float d, float m, uint32_t &hi, uint32_t &lo) {
+__device__ __forceinline__ void split_pair(uint32_t qword, float d, float m, float lo_scale, uint32_t &hi,
+                                           uint32_t &lo) {
     const float q0 = static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)(qword & 0xffffu)));
     const float q1 = static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)(qword >> 16)));
     float w0, w1;
@@ -181,13 +240,15 @@ __device__ __forceinline__ void split_pair(uint32_t qword, float d, float m, uin
         w1 = d * (q1 - 4.0f);
     }
     const _Float16 h0 = (_Float16)w0, h1 = (_Float16)w1;
-    const _Float16 l0 = (_Float16)(w0 - (float)h0), l1 = (_Float16)(w1 - (float)h1);
+    const _Float16 l0 = (_Float16)((w0 - (float)h0) * lo_scale);
+    const _Float16 l1 = (_Float16)((w1 - (float)h1) * lo_scale);
     hi = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
     lo = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
 }
 
+// exact weights of block J as fp16 hi + lo (lo multiplied by lo_scale, 1 or 0)
 template <int FMT, int J>
-__device__ __forceinline__ void bfrag_split(const BRaw<FMT> &b, u32x4 &hi, u32x4 &lo) {
+__device__ __forceinline__ void bfrag_split(const BRaw<FMT> &b, float lo_scale, u32x4 &hi, u32x4 &lo) {
     u32x4 q = lo_operand<J & 1, true>(b.lo[J >> 1]);
     if constexpr (FMT == MOE_FMT_Q3_B32) {
         const u32x4 h4 = hi_operand<J, true>(b.hi);
@@ -200,208 +261,440 @@ __device__ __forceinline__ void bfrag_split(const BRaw<FMT> &b, u32x4 &hi, u32x4
     float m = 0.f;
     if constexpr (FMT == MOE_FMT_Q2_B32) m = half_bits_to_float((uint16_t)(b.mn[J >> 1] >> (16 * (J & 1))));
     uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-    split_pair<FMT>(q.x, d, m, h0, l0);
-    split_pair<FMT>(q.y, d, m, h1, l1);
-    split_pair<FMT>(q.z, d, m, h2, l2);
-    split_pair<FMT>(q.w, d, m, h3, l3);
+    split_pair<FMT>(q.x, d, m, lo_scale, h0, l0);
+    split_pair<FMT>(q.y, d, m, lo_scale, h1, l1);
+    split_pair<FMT>(q.z, d, m, lo_scale, h2, l2);
+    split_pair<FMT>(q.w, d, m, lo_scale, h3, l3);
     hi = u32x4{h0, h1, h2, h3};
     lo = u32x4{l0, l1, l2, l3};
 }
 
-// ------------------------------------------------------------- the GEMMs
-// MODE 0: gate/up (K = d).  Wave w of the workgroup owns h columns
-//   [n0 + 32w, n0 + 32w + 32): B subtiles 0,1 = gate rows, 2,3 = up rows.
-// MODE 1: down (K = f).  Wave w owns output columns [n0 + 64w, +64).
-// SPLIT: exact hi+lo weights (and for MODE 1, h hi+lo as A) -- shared expert.
-template <int FMT, int MODE, bool SPLIT>
-__global__ __launch_bounds__(256, 1) void pf_gemm_kernel(
-    QMatDev W0, QMatDev W1, const PfItem *__restrict__ items, const int32_t *__restrict__ n_items,
-    int item_base, int n_tiles, const uint16_t *__restrict__ a_src, const uint16_t *__restrict__ a_lo,
-    const int32_t *__restrict__ sorted_pair, int k, int d, int f, uint16_t *__restrict__ h_out,
-    uint16_t *__restrict__ h_lo_out, float *__restrict__ y_pairs, float *__restrict__ y_shared,
-    int T) {
-    constexpr int NA = (MODE == 1 && SPLIT) ? 2 : 1;   // A tiles (h hi, h lo)
-    __shared__ __attribute__((aligned(16))) _Float16 As[NA][PF_MT * PF_APITCH];
-    __shared__ int arow[PF_MT];
-    const int bid = blockIdx.x;
-    const int it = item_base + bid / n_tiles;
-    const int nt = bid % n_tiles;
-    PfItem item;
-    if (SPLIT) {
-        // shared expert: items are the first ceil(T/128) entries
-        if (it >= (T + PF_MT - 1) / PF_MT) return;
+// Fragment of 32-block J from one code slot: fp16-rounded weights (routed),
+// or exact weights as fp16 hi + lo (shared expert; lo scaled by lo_scale).
+template <int FMT, bool SPLIT>
+__device__ __forceinline__ void frag_j(const BRaw<FMT> &b, int J, float lo_scale, u32x4 &hi, u32x4 &lo) {
+    if constexpr (SPLIT) {
+        switch (J) {
+            case 0: bfrag_split<FMT, 0>(b, lo_scale, hi, lo); break;
+            case 1: bfrag_split<FMT, 1>(b, lo_scale, hi, lo); break;
+            case 2: bfrag_split<FMT, 2>(b, lo_scale, hi, lo); break;
+            default: bfrag_split<FMT, 3>(b, lo_scale, hi, lo); break;
+        }
     } else {
-        if (it >= n_items[0]) return;
+        switch (J) {
+            case 0: hi = bfrag_f16<FMT, 0>(b); break;
+            case 1: hi = bfrag_f16<FMT, 1>(b); break;
+            case 2: hi = bfrag_f16<FMT, 2>(b); break;
+            default: hi = bfrag_f16<FMT, 3>(b); break;
+        }
     }
-    item = items[it];
-    if (!SPLIT && item.expert < 0) return;
-    const int tid = threadIdx.x, lane = __lane_id();
-    const int wv = wave_uniform(tid >> 6);
-    const int gq = lane >> 4, rr = lane & 15;
-    const int K = MODE == 0 ? d : f;
-    const int KC = K / 128;
-    const int nrows = item.nrows;
-    const int e = item.expert < 0 ? 0 : item.expert;
-    // h_lo holds the shared rows only, indexed by token: row = h row - hrow0 + row0
-    const long lo_delta = (long)item.row0 - item.hrow0;
+}
 
-    // A row sources (rows past the item's end reuse its last row; never stored)
+__device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// 64 lanes x 16 bytes from global memory straight into LDS [dst, dst + 1 KiB),
+// lane l's bytes at dst + 16 l.
+__device__ __forceinline__ void copy_to_lds16(const void *src, void *dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(0) / vmcnt(8) (expcnt, lgkmcnt left alone)
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_vm8() { __builtin_amdgcn_s_waitcnt(0x0F78); }
+
+struct PfGemmArgs {
+    QMatDev w0, w1;            // routed experts: gate, up (gate/up) or down (down)
+    QMatDev s0, s1;            // shared expert, same roles
+    const PfItem *items;
+    PfSched *sched;
+    const uint16_t *a_hi;      // gate/up: x as fp16 [T][d]; down: h [(P + T)][f]
+    const uint16_t *a_lo;      // down: h_lo [T][f] (shared rows)
+    const int32_t *sorted_pair;
+    uint16_t *h_out;           // [(P + T)][f]
+    uint16_t *h_lo_out;        // [T][f]
+    float *y_pairs, *y_shared;
+    int k, d, f, nt, launch;
+};
+
+// Tile geometry, by n-tiles (of 32 weight rows) per wave, NTW:
+//   NTW = 4: one workgroup per CU (256 + 256 registers per lane), three A
+//            stages; a wave owns 64 h columns (gate/up) or 128 outputs (down).
+//   NTW = 2: two workgroups per CU (256 registers), two A stages; a wave owns
+//            32 h columns or 64 outputs.  The second workgroup's matrix ops
+//            fill the first one's epilogue, prologue and barrier time.
+template <int NTW>
+struct PfGeom {
+    static constexpr int NSTAGE = NTW == 4 ? 3 : 2;
+    static constexpr int OCC = NTW == 4 ? 1 : 2;
+    static constexpr int HCOLS = 16 * NTW;          // gate/up: h columns per wave
+    static constexpr int OCOLS = 32 * NTW;          // down: output columns per wave
+    // epilogue staging per wave (in the A stages); pitches put rows 4 apart
+    // (the two half-waves) in different banks
+    static constexpr int EP0_PITCH = HCOLS + 8;     // [gate | up][32][EP0_PITCH] floats
+    static constexpr int EP1_PITCH = OCOLS + 8;     // [32][EP1_PITCH] floats
+    static constexpr int EP_WAVE = (2 * 32 * EP0_PITCH > 32 * EP1_PITCH ? 2 * 32 * EP0_PITCH : 32 * EP1_PITCH) * 4;
+    static_assert(4 * EP_WAVE <= NSTAGE * PF_STAGE, "epilogue staging must fit in the A stages");
+};
+
+// silu(g) * u with the hardware reciprocal (about 1 ulp): h is rounded to
+// fp16 right after
+__device__ __forceinline__ float swiglu_fast(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+// One unit: 128 rows of one item x one column tile, all of K.
+// MODE 0 (gate/up, K = d): wave w owns h columns c0 = tile * 4 HCOLS + w HCOLS
+//   .. +HCOLS; n-tiles 0 .. NTW/2 - 1 are those gate rows, the rest the same
+//   up rows, so each SwiGLU pair sits in one lane and register.
+// MODE 1 (down, K = f): wave w owns outputs tile * 4 OCOLS + w OCOLS .. +OCOLS.
+// A wave's columns are all in range or all past the end (d, f are multiples
+// of 128); past the end it reads the last valid weights and stores nothing.
+// SH (shared expert): exact weights as hi + lo.  For MODE 1 the K loop runs
+//   twice: A = h_hi with B hi and lo, then A = h_lo with B hi.
+// MT: 32-row m-tiles that hold rows of the item (1..4).
+template <int FMT, int MODE, bool SH, int MT, int NTW>
+__device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item, int tile,
+                                        uint8_t *As, int *s_row) {
+    using G = PfGeom<NTW>;
+    const int tid = threadIdx.x, l = __lane_id();
+    const int wv = wave_uniform(tid >> 6);
+    const int h = l >> 5, uu = (l >> 4) & 1, rr = l & 15;
+    const int K = MODE == 0 ? a.d : a.f;
+    const int KC = K / PF_KS;
+    const int NSTEP = (MODE == 1 && SH) ? 2 * KC : KC;
+    const int nrows = item.nrows;
+    const int e = SH ? 0 : item.expert;
+
+    // source row (token, or h row) of each tile row; rows past the item's
+    // end repeat its last row and are never stored
     if (tid < PF_MT) {
         const int r = tid < nrows ? tid : nrows - 1;
         int src;
-        if (MODE == 0)
-            src = item.expert < 0 ? item.row0 + r : sorted_pair[item.row0 + r] / k;
+        if constexpr (MODE == 0)
+            src = SH ? item.row0 + r : a.sorted_pair[item.row0 + r] / a.k;
         else
             src = item.hrow0 + r;
-        arow[tid] = src;
-    }
-    // B row tiles of this wave: unit index base for each of the 4 subtiles
-    size_t ubase[4];
-    QMatDev Wsub[4];
-    if (MODE == 0) {
-        const int rows_per_exp = f / 16;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int tile = (nt * 128 + wv * 32) / 16 + (s & 1);
-            ubase[s] = ((size_t)e * rows_per_exp + tile) * KC;
-            Wsub[s] = s < 2 ? W0 : W1;
-        }
-    } else {
-        // d is a multiple of 128, so a wave's 64 columns are all in range or
-        // all past d; past d the wave reads the last tile and stores nothing
-        const int rows_per_exp = d / 16;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            int tile = (nt * 256 + wv * 64) / 16 + s;
-            tile = tile < rows_per_exp ? tile : rows_per_exp - 1;
-            ubase[s] = ((size_t)e * rows_per_exp + tile) * KC;
-            Wsub[s] = W0;
-        }
+        s_row[tid] = src;
     }
     __syncthreads();
 
-    // accumulators: 8 m-subtiles x 4 n-subtiles
-    f32x4 acc[8][4];
+    // A copy slots of this lane: instruction i covers tile rows 4 (8 wv + i)
+    // .. +4; lane l takes row R = 4 (8 wv + i) + l / 16 and stores physical
+    // chunk l % 16, which holds logical chunk (l % 16) ^ (R % 16)
+    int arow_i[8];
+    const char *abase = reinterpret_cast<const char *>(a.a_hi);
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int nsub = (nrows + 15) / 16;
-
-    // A staging: 128 rows x 128 fp16 = 2048 x 16 B; thread loads 8 chunks
-    u32x4 areg[NA][8];
-    auto load_a = [&](int kc) {
+    for (int i = 0; i < 8; ++i) arow_i[i] = s_row[4 * (8 * wv + i) + (l >> 4)];
+    auto switch_to_lo = [&]() {
+        abase = reinterpret_cast<const char *>(a.a_lo);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c >> 4, col = (c & 15) * 8;
-            const size_t off = (size_t)arow[row] * K + kc * 128 + col;
-            areg[0][i] = *reinterpret_cast<const u32x4 *>(a_src + off);
-            if constexpr (NA == 2)
-                areg[1][i] = *reinterpret_cast<const u32x4 *>(a_lo + off + lo_delta * K);
+            const int R = 4 * (8 * wv + i) + (l >> 4);
+            arow_i[i] = item.row0 + (R < nrows ? R : nrows - 1);
         }
     };
-    auto store_a = [&]() {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c >> 4, col = (c & 15) * 8;
-#pragma unroll
-            for (int t = 0; t < NA; ++t)
-                *reinterpret_cast<u32x4 *>(&As[t][row * PF_APITCH + col]) = areg[t][i];
-        }
+    auto issue_a_part = [&](int kc, int i) {
+        const int kk = kc < KC ? kc : kc - KC;
+        uint8_t *dst = As + (kc % G::NSTAGE) * PF_STAGE + wv * 8 * 1024;
+        const int R = 4 * (8 * wv + i) + (l >> 4);
+        const int c = (l & 15) ^ (R & 15);
+        copy_to_lds16(abase + (size_t)arow_i[i] * (K * 2) + (kk * (PF_KS * 2) + c * 16), dst + i * 1024);
     };
-    BRaw<FMT> braw[4];
-    auto load_b = [&](int kc) {
+    auto issue_a = [&](int kc) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) load_braw(braw[s], Wsub[s], ubase[s] + kc, lane, rr);
+        for (int i = 0; i < 8; ++i) issue_a_part(kc, i);
     };
 
-    load_a(0);
-    load_b(0);
-    for (int kc = 0; kc < KC; ++kc) {
-        store_a();
-        BRaw<FMT> bcur[4];
+    // B: storage-unit index (at kc = 0) of this lane's unit in n-tile n
+    const QMatDev W0 = SH ? a.s0 : a.w0;
+    const QMatDev W1 = SH ? a.s1 : a.w1;
+    size_t ub[NTW];
+    bool cols_valid;
+    if constexpr (MODE == 0) {
+        const int rpe = a.f / 16;
+        const int c0 = tile * 4 * G::HCOLS + wv * G::HCOLS;
+        cols_valid = c0 < a.f;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) bcur[s] = braw[s];
-        __syncthreads();
-        if (kc + 1 < KC) {
-            load_a(kc + 1);
-            load_b(kc + 1);
+        for (int n = 0; n < NTW; ++n) {
+            int t16 = (c0 + 32 * (n % (NTW / 2))) / 16 + uu;
+            t16 = t16 < rpe ? t16 : rpe - 1;
+            ub[n] = ((size_t)e * rpe + t16) * KC;
         }
+    } else {
+        const int rpe = a.d / 16;
+        const int c0 = tile * 4 * G::OCOLS + wv * G::OCOLS;
+        cols_valid = c0 < a.d;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            u32x4 bf[4], bl[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                if constexpr (SPLIT) {
-                    switch (j) {
-                        case 0: bfrag_split<FMT, 0>(bcur[s], bf[s], bl[s]); break;
-                        case 1: bfrag_split<FMT, 1>(bcur[s], bf[s], bl[s]); break;
-                        case 2: bfrag_split<FMT, 2>(bcur[s], bf[s], bl[s]); break;
-                        default: bfrag_split<FMT, 3>(bcur[s], bf[s], bl[s]); break;
-                    }
-                } else {
-                    switch (j) {
-                        case 0: bf[s] = bfrag_f16<FMT, 0>(bcur[s]); break;
-                        case 1: bf[s] = bfrag_f16<FMT, 1>(bcur[s]); break;
-                        case 2: bf[s] = bfrag_f16<FMT, 2>(bcur[s]); break;
-                        default: bf[s] = bfrag_f16<FMT, 3>(bcur[s]); break;
-                    }
-                }
-            }
-#pragma unroll
-            for (int ms = 0; ms < 8; ++ms) {
-                if (ms < nsub) {
-                    const int arow_l = ms * 16 + rr;
-                    const u32x4 af = *reinterpret_cast<const u32x4 *>(&As[0][arow_l * PF_APITCH + j * 32 + gq * 8]);
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        acc[ms][s] = mfma_f16(af, bf[s], acc[ms][s]);
-                        if constexpr (SPLIT) acc[ms][s] = mfma_f16(af, bl[s], acc[ms][s]);
-                    }
-                    if constexpr (NA == 2) {
-                        const u32x4 al = *reinterpret_cast<const u32x4 *>(&As[1][arow_l * PF_APITCH + j * 32 + gq * 8]);
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) acc[ms][s] = mfma_f16(al, bf[s], acc[ms][s]);
-                    }
-                }
-            }
+        for (int n = 0; n < NTW; ++n) {
+            int t16 = (c0 + 32 * n) / 16 + uu;
+            t16 = t16 < rpe ? t16 : rpe - 1;
+            ub[n] = ((size_t)e * rpe + t16) * KC;
         }
-        __syncthreads();
     }
+    // slot 0 = (h, rr) -> columns 32j + 8h; slot 1 = (2 + h, rr) -> 32j + 16 + 8h
+    auto load_b_tile = [&](BRaw<FMT> (&br)[NTW][2], int kc, int n) {
+        const QMatDev &W = (MODE == 0 && n >= NTW / 2) ? W1 : W0;
+        const size_t u = ub[n] + kc;
+        const uint8_t *lo = W.lo + u * 512;
+        br[n][0].lo = *reinterpret_cast<const u32x2 *>(lo + (h * 16 + rr) * 8);
+        br[n][1].lo = *reinterpret_cast<const u32x2 *>(lo + ((2 + h) * 16 + rr) * 8);
+        if constexpr (FMT == MOE_FMT_Q3_B32) {
+            const uint8_t *hp = W.hi + u * 256;
+            br[n][0].hi = *reinterpret_cast<const uint32_t *>(hp + (h * 16 + rr) * 4);
+            br[n][1].hi = *reinterpret_cast<const uint32_t *>(hp + ((2 + h) * 16 + rr) * 4);
+        }
+        const u32x2 sc = *reinterpret_cast<const u32x2 *>(W.scale + u * 64 + rr * 4);
+        br[n][0].sc = sc;
+        br[n][1].sc = sc;
+        if constexpr (FMT == MOE_FMT_Q2_B32) {
+            const u32x2 mn = *reinterpret_cast<const u32x2 *>(W.min + u * 64 + rr * 4);
+            br[n][0].mn = mn;
+            br[n][1].mn = mn;
+        }
+    };
 
-    // epilogue
+    f32x16 acc[MT][NTW];
 #pragma unroll
-    for (int ms = 0; ms < 8; ++ms) {
-        if (ms >= nsub) continue;
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = ms * 16 + gq * 4 + i;
-            if (r >= nrows) continue;
-            if constexpr (MODE == 0) {
+        for (int n = 0; n < NTW; ++n)
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const float hv = swiglu(acc[ms][s][i], acc[ms][s + 2][i]);
-                    const int col = nt * 128 + wv * 32 + s * 16 + rr;
-                    const size_t off = (size_t)(item.hrow0 + r) * f + col;
-                    const _Float16 hh = static_cast<_Float16>(hv);
-                    h_out[off] = __builtin_bit_cast(uint16_t, hh);
-                    if constexpr (SPLIT) {
-                        const _Float16 hl = static_cast<_Float16>(hv - static_cast<float>(hh));
-                        h_lo_out[(size_t)(item.row0 + r) * f + col] = __builtin_bit_cast(uint16_t, hl);
+            for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
+
+    // the 16-byte fragment chunk 2s + h of tile row m*32 + l%32, swizzled
+    const uint8_t *arow_base = As + (l & 31) * (PF_KS * 2);
+    auto read_a = [&](int stage, int m, int s) -> u32x4 {
+        const int pos = (2 * s + h) ^ (l & 15);
+        return *reinterpret_cast<const u32x4 *>(arow_base + stage * PF_STAGE + m * 32 * (PF_KS * 2) +
+                                                pos * 16);
+    };
+
+    // Loads return in issue order, so one vmcnt wait per step covers them:
+    //   3 stages: the weights of step kc + 1 load in sub-steps 0-1, the A copies
+    //     of step kc + 2 in sub-steps 2-5; vmcnt(8) leaves only the latter.
+    //   2 stages: the A copies and weights of step kc + 1 load in sub-steps
+    //     0-3; vmcnt(0).
+    BRaw<FMT> bcur[NTW][2], bnext[NTW][2];
+    issue_a(0);
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) load_b_tile(bcur, 0, n);
+    if (G::NSTAGE == 3 && NSTEP > 1) {
+        if (MODE == 1 && SH && KC == 1) switch_to_lo();
+        issue_a(1);
+        wait_vm8();
+    } else {
+        wait_vm0();
+    }
+    __syncthreads();
+    for (int kc = 0; kc < NSTEP; ++kc) {
+        const int st = kc % G::NSTAGE;
+        const bool more1 = kc + 1 < NSTEP, more2 = kc + 2 < NSTEP;
+        const int kb = kc + 1 < KC ? kc + 1 : kc + 1 - KC;
+        const int ka = G::NSTAGE == 3 ? kc + 2 : kc + 1;     // A stage copied during this step
+        const bool amore = G::NSTAGE == 3 ? more2 : more1;
+        if (amore && MODE == 1 && SH && ka == KC) switch_to_lo();
+        auto issue_part = [&](int s) {
+            if constexpr (G::NSTAGE == 3) {
+                if (s < 2) {
+                    if (more1) {
+#pragma unroll
+                        for (int n = s * NTW / 2; n < (s + 1) * NTW / 2; ++n) load_b_tile(bnext, kb, n);
+                    }
+                } else if (s < 6) {
+                    if (amore) {
+                        issue_a_part(ka, 2 * (s - 2));
+                        issue_a_part(ka, 2 * (s - 2) + 1);
                     }
                 }
             } else {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int col = nt * 256 + wv * 64 + s * 16 + rr;
-                    if (col >= d) continue;
-                    if (item.expert < 0)
-                        y_shared[(size_t)(item.row0 + r) * d + col] = acc[ms][s][i];
-                    else
-                        y_pairs[(size_t)(item.row0 + r) * d + col] = acc[ms][s][i];
+                if (s < 4 && more1) {
+                    issue_a_part(ka, 2 * s);
+                    issue_a_part(ka, 2 * s + 1);
+                    if (s < NTW) load_b_tile(bnext, kb, s);
                 }
+            }
+        };
+        // shared down, second pass (A = h_lo): weight lo fragments are zeroed
+        const float lo_scale = (MODE == 1 && SH && kc >= KC) ? 0.f : 1.f;
+        if constexpr (G::OCC == 1) {
+            // one wave per SIMD: fragments of sub-step s + 1 are read and
+            // dequantised while the matrix ops of sub-step s run
+            u32x4 af[2][MT], bf[2][NTW], bl[2][NTW];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) af[0][m] = read_a(st, m, 0);
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) frag_j<FMT, SH>(bcur[n][0], 0, lo_scale, bf[0][n], bl[0][n]);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int cb = s & 1, nb = cb ^ 1;
+                issue_part(s);
+                if (s < 7) {
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) af[nb][m] = read_a(st, m, s + 1);
+#pragma unroll
+                    for (int n = 0; n < NTW; ++n)
+                        frag_j<FMT, SH>(bcur[n][(s + 1) & 1], (s + 1) >> 1, lo_scale, bf[nb][n], bl[nb][n]);
+                }
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int n = 0; n < NTW; ++n) {
+                        acc[m][n] = mfma32(af[cb][m], bf[cb][n], acc[m][n]);
+                        if constexpr (SH) acc[m][n] = mfma32(af[cb][m], bl[cb][n], acc[m][n]);
+                    }
+                // keep the next step's reads and dequantisation within this step
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            // two waves per SIMD: the other wave covers the read latency
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                u32x4 af[MT], bf[NTW], bl[NTW];
+                issue_part(s);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) af[m] = read_a(st, m, s);
+#pragma unroll
+                for (int n = 0; n < NTW; ++n) frag_j<FMT, SH>(bcur[n][s & 1], s >> 1, lo_scale, bf[n], bl[n]);
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int n = 0; n < NTW; ++n) {
+                        acc[m][n] = mfma32(af[m], bf[n], acc[m][n]);
+                        if constexpr (SH) acc[m][n] = mfma32(af[m], bl[n], acc[m][n]);
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (G::NSTAGE == 3 && more2)
+            wait_vm8();
+        else
+            wait_vm0();
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < NTW; ++n)
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) bcur[n][sl] = bnext[n][sl];
+    }
+
+    // epilogue, one m-tile at a time through a wave-private LDS region (the A
+    // stages are free now): accumulators out as written by the matrix core
+    // (D row 8 (r / 4) + 4 h + r % 4, column l % 32), then read back along
+    // rows so each lane stores 16 contiguous bytes.
+    if (cols_valid) {
+        float *ep = reinterpret_cast<float *>(As + wv * G::EP_WAVE);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if constexpr (MODE == 0) {
+                // [gate | up][32 rows][EP0_PITCH]: the wave's HCOLS columns
+#pragma unroll
+                for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+                        ep[((n / (NTW / 2)) * 32 + row) * G::EP0_PITCH + (n % (NTW / 2)) * 32 + (l & 31)] =
+                            acc[m][n][r];
+                    }
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                constexpr int LPR = G::HCOLS / 8;    // lanes per row (8 columns each)
+                const int c0 = tile * 4 * G::HCOLS + wv * G::HCOLS + (l % LPR) * 8;
+#pragma unroll 1
+                for (int it = 0; it < 32 * LPR / 64; ++it) {
+                    const int row = it * (64 / LPR) + l / LPR;
+                    const int grow = m * 32 + row;
+                    const float *gp = ep + row * G::EP0_PITCH + (l % LPR) * 8;
+                    const float *up = gp + 32 * G::EP0_PITCH;
+                    const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp);
+                    const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gp + 4);
+                    const f32x4 u0 = *reinterpret_cast<const f32x4 *>(up);
+                    const f32x4 u1 = *reinterpret_cast<const f32x4 *>(up + 4);
+                    float hv[8] = {swiglu_fast(g0.x, u0.x), swiglu_fast(g0.y, u0.y), swiglu_fast(g0.z, u0.z),
+                                   swiglu_fast(g0.w, u0.w), swiglu_fast(g1.x, u1.x), swiglu_fast(g1.y, u1.y),
+                                   swiglu_fast(g1.z, u1.z), swiglu_fast(g1.w, u1.w)};
+                    uint32_t hw[4], lw[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const _Float16 a0 = static_cast<_Float16>(hv[2 * q]);
+                        const _Float16 a1 = static_cast<_Float16>(hv[2 * q + 1]);
+                        hw[q] = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+                        if constexpr (SH) {
+                            const _Float16 b0 = static_cast<_Float16>(hv[2 * q] - static_cast<float>(a0));
+                            const _Float16 b1 = static_cast<_Float16>(hv[2 * q + 1] - static_cast<float>(a1));
+                            lw[q] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+                        }
+                    }
+                    if (grow < nrows) {
+                        *reinterpret_cast<u32x4 *>(a.h_out + (size_t)(item.hrow0 + grow) * a.f + c0) =
+                            u32x4{hw[0], hw[1], hw[2], hw[3]};
+                        if constexpr (SH)
+                            *reinterpret_cast<u32x4 *>(a.h_lo_out + (size_t)(item.row0 + grow) * a.f + c0) =
+                                u32x4{lw[0], lw[1], lw[2], lw[3]};
+                    }
+                }
+            } else {
+                // [32 rows][EP1_PITCH]: the wave's OCOLS columns
+#pragma unroll
+                for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+                        ep[row * G::EP1_PITCH + n * 32 + (l & 31)] = acc[m][n][r];
+                    }
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                float *out = SH ? a.y_shared : a.y_pairs;
+                constexpr int LPR = G::OCOLS / 4;    // lanes per row (4 columns each)
+                const int c0 = tile * 4 * G::OCOLS + wv * G::OCOLS + (l % LPR) * 4;
+#pragma unroll 2
+                for (int it = 0; it < 32 * LPR / 64; ++it) {
+                    const int row = it * (64 / LPR) + l / LPR;
+                    const int grow = m * 32 + row;
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(ep + row * G::EP1_PITCH + (l % LPR) * 4);
+                    if (grow < nrows) *reinterpret_cast<f32x4 *>(out + (size_t)(item.row0 + grow) * a.d + c0) = v;
+                }
+            }
+            // the next m-tile overwrites the region: finish reading it first
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+        }
+    }
+    __syncthreads();
+}
+
+// Persistent grouped GEMM: workgroups take (item, column tile) units by
+// ticket from their XCD's queue, then from the others.
+template <int FMT, int MODE, int NTW>
+__global__ __launch_bounds__(256, PfGeom<NTW>::OCC) void pf_gemm_kernel(PfGemmArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t As[PfGeom<NTW>::NSTAGE * PF_STAGE];
+    __shared__ int s_row[PF_MT];
+    __shared__ int s_ticket;
+    unsigned xcd;
+    __asm__ volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcd));
+    xcd &= PF_NXCD - 1;
+    for (int q = 0; q < PF_NXCD;) {
+        const int x = (int)((xcd + q) & (PF_NXCD - 1));
+        if (threadIdx.x == 0) s_ticket = atomicAdd(&a.sched->ticket[a.launch][x], 1);
+        __syncthreads();
+        const int t = wave_uniform(s_ticket);
+        const int i0 = a.sched->xq[x];
+        const int n_units = (a.sched->xq[x + 1] - i0) * a.nt;
+        if (t >= n_units) {
+            ++q;
+            __syncthreads();
+            continue;
+        }
+        const PfItem item = a.items[i0 + t / a.nt];
+        const int tile = t % a.nt;
+        if (item.expert < 0) {
+            pf_unit<FMT, MODE, true, 4, NTW>(a, item, tile, As, s_row);
+        } else {
+            switch ((item.nrows + 31) >> 5) {
+                case 1: pf_unit<FMT, MODE, false, 1, NTW>(a, item, tile, As, s_row); break;
+                case 2: pf_unit<FMT, MODE, false, 2, NTW>(a, item, tile, As, s_row); break;
+                case 3: pf_unit<FMT, MODE, false, 3, NTW>(a, item, tile, As, s_row); break;
+                default: pf_unit<FMT, MODE, false, 4, NTW>(a, item, tile, As, s_row); break;
             }
         }
     }
@@ -409,8 +702,8 @@ __global__ __launch_bounds__(256, 1) void pf_gemm_kernel(
 
 // ------------------------------------------------------------------ host
 struct PfWs {
+    PfSched *sched;
     PfItem *items;
-    int32_t *n_items;
     uint16_t *x16;
     uint16_t *h;
     uint16_t *h_lo;
@@ -426,7 +719,7 @@ static size_t pf_max_items(int E, int T, int k) {
 static PfWs pf_carve(void *ws, int d, int f, int E, int T, int k) {
     char *p = static_cast<char *>(ws) + kWsHeader;
     PfWs w;
-    w.n_items = reinterpret_cast<int32_t *>(p);
+    w.sched = reinterpret_cast<PfSched *>(p);
     p += 256;
     w.items = reinterpret_cast<PfItem *>(p);
     p += align256(pf_max_items(E, T, k) * sizeof(PfItem));
@@ -443,41 +736,68 @@ size_t ffn_prefill_ws_bytes(int d, int f, int E, int T, int k) {
            align256(((size_t)T * k + T) * f * 2) + align256((size_t)T * f * 2);
 }
 
+// persistent grid: OCC workgroups per compute unit
+static int pf_grid(int occ) {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256 * occ;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev] * occ;
+}
+
+#ifndef MOE_PF_NTW
+#define MOE_PF_NTW 4
+#endif
+constexpr int kPfNtw = MOE_PF_NTW;
+
 template <int FMT>
 static void pf_launch_fmt(const moe_layer &L, const uint16_t *x, int T, int k, const int32_t *offsets,
                           const int32_t *sorted_pair, float *y_pairs, float *y_shared, const PfWs &w,
                           hipStream_t s) {
     const int d = L.d_model, f = L.d_ff, E = L.n_experts;
     const int P = T * k;
-    const QMatDev g{L.gate.lo, L.gate.hi, L.gate.scale, L.gate.min};
-    const QMatDev u{L.up.lo, L.up.hi, L.up.scale, L.up.min};
-    const QMatDev dn{L.down.lo, L.down.hi, L.down.scale, L.down.min};
-    const QMatDev sg{L.sh_gate.lo, L.sh_gate.hi, L.sh_gate.scale, L.sh_gate.min};
-    const QMatDev su{L.sh_up.lo, L.sh_up.hi, L.sh_up.scale, L.sh_up.min};
-    const QMatDev sd{L.sh_down.lo, L.sh_down.hi, L.sh_down.scale, L.sh_down.min};
-    const int sh_items = (T + PF_MT - 1) / PF_MT;
-    const int max_items = (int)pf_max_items(E, T, k);
-    const int nt_gu = f / 128, nt_dn = (d + 255) / 256;
     hipLaunchKernelGGL(pf_build_items_kernel, dim3(1), dim3(1024), 0, s, offsets, E, T, P, w.items,
-                       w.n_items);
+                       w.sched);
     const size_t n8 = (size_t)T * d / 8;
     size_t blocks = (n8 + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(pf_x_to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, w.x16, n8);
-    // gate/up: shared (exact), routed
-    hipLaunchKernelGGL((pf_gemm_kernel<FMT, 0, true>), dim3(sh_items * nt_gu), dim3(256), 0, s, sg, su,
-                       w.items, w.n_items, 0, nt_gu, w.x16, nullptr, sorted_pair, k, d, f, w.h, w.h_lo,
-                       y_pairs, y_shared, T);
-    hipLaunchKernelGGL((pf_gemm_kernel<FMT, 0, false>), dim3((max_items - sh_items) * nt_gu), dim3(256), 0,
-                       s, g, u, w.items, w.n_items, sh_items, nt_gu, w.x16, nullptr, sorted_pair, k, d, f,
-                       w.h, w.h_lo, y_pairs, y_shared, T);
-    // down: shared (exact weights, h hi + lo), routed
-    hipLaunchKernelGGL((pf_gemm_kernel<FMT, 1, true>), dim3(sh_items * nt_dn), dim3(256), 0, s, sd, sd,
-                       w.items, w.n_items, 0, nt_dn, w.h, w.h_lo, sorted_pair, k, d, f, w.h, w.h_lo,
-                       y_pairs, y_shared, T);
-    hipLaunchKernelGGL((pf_gemm_kernel<FMT, 1, false>), dim3((max_items - sh_items) * nt_dn), dim3(256), 0,
-                       s, dn, dn, w.items, w.n_items, sh_items, nt_dn, w.h, nullptr, sorted_pair, k, d, f,
-                       w.h, w.h_lo, y_pairs, y_shared, T);
+    PfGemmArgs a{};
+    a.items = w.items;
+    a.sched = w.sched;
+    a.sorted_pair = sorted_pair;
+    a.h_out = w.h;
+    a.h_lo_out = w.h_lo;
+    a.y_pairs = y_pairs;
+    a.y_shared = y_shared;
+    a.k = k;
+    a.d = d;
+    a.f = f;
+    using G = PfGeom<kPfNtw>;
+    const int grid = pf_grid(G::OCC);
+    // gate/up + SwiGLU
+    a.w0 = QMatDev{L.gate.lo, L.gate.hi, L.gate.scale, L.gate.min};
+    a.w1 = QMatDev{L.up.lo, L.up.hi, L.up.scale, L.up.min};
+    a.s0 = QMatDev{L.sh_gate.lo, L.sh_gate.hi, L.sh_gate.scale, L.sh_gate.min};
+    a.s1 = QMatDev{L.sh_up.lo, L.sh_up.hi, L.sh_up.scale, L.sh_up.min};
+    a.a_hi = w.x16;
+    a.a_lo = nullptr;
+    a.nt = (f + 4 * G::HCOLS - 1) / (4 * G::HCOLS);
+    a.launch = 0;
+    hipLaunchKernelGGL((pf_gemm_kernel<FMT, 0, kPfNtw>), dim3(grid), dim3(256), 0, s, a);
+    // down
+    a.w0 = a.w1 = QMatDev{L.down.lo, L.down.hi, L.down.scale, L.down.min};
+    a.s0 = a.s1 = QMatDev{L.sh_down.lo, L.sh_down.hi, L.sh_down.scale, L.sh_down.min};
+    a.a_hi = w.h;
+    a.a_lo = w.h_lo;
+    a.nt = (d + 4 * G::OCOLS - 1) / (4 * G::OCOLS);
+    a.launch = 1;
+    hipLaunchKernelGGL((pf_gemm_kernel<FMT, 1, kPfNtw>), dim3(grid), dim3(256), 0, s, a);
 }
 
 hipError_t launch_ffn_prefill(const moe_layer &L, const uint16_t *x, int T, int k,
