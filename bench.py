@@ -40,6 +40,27 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix
 METRIC = "MoE-layer tokens/s (decode T=1/4, prefill 8192); % HBM BW or % MFMA peak"
 
+# HBM bytes per moe_expert_ffn call, from two rocprofv3 --pmc runs (FETCH_SIZE,
+# WRITE_SIZE; each scaled by what it reads for a plain 1 GiB copy), keyed by
+# workload.  Each figure is tied to a hash of the kernel sources it was taken
+# on and is reported as null once those sources change.
+TRAFFIC = {
+    1: (("common.h", "ffn_small.hip"), "d6e564d79900dea8", 20168244),
+    3: (("common.h", "ffn_prefill.hip"), "b1cfc481a6f052cb", 2662221630),
+}
+
+
+def traffic_for(wid):
+    import hashlib
+    if wid not in TRAFFIC:
+        return None
+    files, digest, nbytes = TRAFFIC[wid]
+    m = hashlib.sha256()
+    for fn in files:
+        with open(os.path.join(ROOT, "quantized_moe_route_amd", "csrc", fn), "rb") as fh:
+            m.update(fh.read())
+    return float(nbytes) if m.hexdigest()[:16] == digest else None
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -87,6 +108,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (the reference kernel "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -95,6 +119,17 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
+        return
 
     import synth
     import synth.device as sdev
@@ -279,9 +314,9 @@ def main():
                 "hbm_gbs_algorithmic": ffn_bytes / t_ffn / 1e9}
     else:
         achieved = ffn_bytes / t_ffn / 1e9
-        roof = {"bound": "hbm", "kernel": "moe_expert_ffn (gateup_small + down_small)",
+        roof = {"bound": "hbm", "kernel": "moe_expert_ffn call: gateup_small, down_small",
                 "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(args.workload),
                 "bytes_per_launch": ffn_bytes, "avg_groups": float(np.mean(groups))}
     layer_bytes = ffn_bytes + w.d_model * w.n_experts * 4  # + router weights
 
