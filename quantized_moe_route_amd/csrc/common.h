@@ -22,7 +22,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr size_t kWsHeader = 4096;
 constexpr int kCntRouteSlice = 0;   // [0, 16): per 64-expert slice arrival counters
 constexpr int kCntRouteAll = 16;    // one counter: slices finished
-constexpr int kCntPrefillTicket = 32;  // persistent-GEMM tickets / exits (4 slots)
 
 struct QMatDev {
     const uint8_t *lo;
@@ -165,23 +164,27 @@ __device__ inline bool find_group(const int32_t *__restrict__ offsets, int E, in
     const int target = slot - 1;  // index among non-empty experts
     const int l = __lane_id();
     const int per = (E + 63) / 64;  // <= 16
-    // unconditional loads at clamped indices (a predicated load would be
-    // waited for inside its own branch); out-of-range experts read as empty
-    int lo[16], hi[16];
+    // One round trip: lane l loads the start offsets of experts l + 64 i
+    // (unconditional loads at clamped indices: a predicated load would be
+    // waited for inside its own branch); each end offset is the next
+    // expert's start, taken from the neighbouring lane.
+    int lo[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int e = l + 64 * i;
-        const int ec = e < E ? e : E - 1;
-        const int a = offsets[ec], b = offsets[ec + 1];
-        lo[i] = a;
-        hi[i] = e < E ? b : a;
+        lo[i] = offsets[e < E ? e : E];
     }
+    const int last = offsets[E < 1024 ? E : 1024];
     int cum = 0, sel_row = -1, sel_n = 0;
     unsigned long long sel_m = 0ull;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         if (i < per) {
-            const unsigned long long m = __ballot(hi[i] > lo[i]);
+            const int nxt = i + 1 < 16 ? __shfl(lo[i + 1], 0) : last;
+            int hi = __shfl(lo[i], (l + 1) & 63);
+            hi = l == 63 ? nxt : hi;
+            const bool valid = l + 64 * i < E;
+            const unsigned long long m = __ballot(valid && hi > lo[i]);
             const int c = __popcll(m);
             const bool hit = sel_row < 0 && target < cum + c;
             sel_m = hit ? m : sel_m;
@@ -191,11 +194,22 @@ __device__ inline bool find_group(const int32_t *__restrict__ offsets, int E, in
         }
     }
     if (sel_row < 0) return false;
-    const int found = 64 * sel_row + nth_set_bit(sel_m, sel_n);
+    const int bit = nth_set_bit(sel_m, sel_n);
+    const int found = 64 * sel_row + bit;
+    // start and end of the found expert: lane bit (and its successor) hold them
+    int a = lo[0], b = lo[0];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        if (i == sel_row) {
+            a = lo[i];
+            b = i + 1 < 16 ? lo[i + 1] : last;
+        }
+    const int row0 = __shfl(a, bit);
+    const int end = bit < 63 ? __shfl(a, bit + 1) : __shfl(b, 0);
     g.expert = found;
-    g.row0 = offsets[found];
-    g.nrows = offsets[found + 1] - g.row0;
-    g.hrow0 = g.row0;
+    g.row0 = row0;
+    g.nrows = end - row0;
+    g.hrow0 = row0;
     return true;
 }
 

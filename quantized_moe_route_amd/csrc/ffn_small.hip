@@ -128,19 +128,15 @@ __device__ __forceinline__ void gateup_block(const GateUpUnit<FMT, MT> &U, f32x4
 #endif
 constexpr int kBatch = MOE_DECODE_BATCH;   // units prefetched per wave per batch
 
-// grid: (d_ff/16 row tiles, 1 + min(E, P) group slots); NW waves split K.
+// One gate/up task: 16 h columns (row tile nt) of one expert group, for all
+// of the group's rows.  The NW waves of the workgroup split K and meet in LDS
+// (red); wave 0 applies SwiGLU and writes h as fp16 hi + lo.
 template <int FMT, int MT, int IMAX, int NW>
-__global__ __launch_bounds__(64 * NW) void gateup_small_kernel(
-    QMatDev gate, QMatDev up, QMatDev sgate, QMatDev sup, const uint16_t *__restrict__ x, int T,
-    int k, int d, int f, int E, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ sorted_pair, uint16_t *__restrict__ h_hi,
-    uint16_t *__restrict__ h_lo) {
-    __shared__ float red[NW][MT][2][IMAX][64];
-    const int nt = blockIdx.x;
-    const int slot = blockIdx.y;
-    const int P = T * k;
-    Group grp;
-    if (!find_group(offsets, E, T, P, slot, grp)) return;
+__device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &up, const QMatDev &sgate,
+                                            const QMatDev &sup, const uint16_t *__restrict__ x, int k, int d,
+                                            int f, const int32_t *__restrict__ sorted_pair, const Group &grp,
+                                            int nt, float (*red)[MT][2][IMAX][64], uint16_t *__restrict__ h_hi,
+                                            uint16_t *__restrict__ h_lo) {
     const int lane = __lane_id();
     const int wv = wave_uniform(threadIdx.x >> 6);
     const int gq = lane >> 4, rr = lane & 15;
@@ -205,35 +201,38 @@ __global__ __launch_bounds__(64 * NW) void gateup_small_kernel(
                 red[wv][mt][1][i][lane] = au[mt][i];
             }
         __syncthreads();
-        if (wv != 0) return;
+        if (wv == 0) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < IMAX; ++i) {
+                    float gs = red[0][mt][0][i][lane], us = red[0][mt][1][i][lane];
+#pragma unroll
+                    for (int w2 = 1; w2 < NW; ++w2) {
+                        gs += red[w2][mt][0][i][lane];
+                        us += red[w2][mt][1][i][lane];
+                    }
+                    ag[mt][i] = gs;
+                    au[mt][i] = us;
+                }
+        }
+    }
+    if (wv == 0) {
+        const int n = nt * 16 + rr;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < IMAX; ++i) {
-                float gs = red[0][mt][0][i][lane], us = red[0][mt][1][i][lane];
-#pragma unroll
-                for (int w2 = 1; w2 < NW; ++w2) {
-                    gs += red[w2][mt][0][i][lane];
-                    us += red[w2][mt][1][i][lane];
-                }
-                ag[mt][i] = gs;
-                au[mt][i] = us;
+                const int r = mt * 16 + gq * 4 + i;
+                if (r >= nrows) continue;
+                const float h = swiglu(ag[mt][i], au[mt][i]);
+                const _Float16 hh = static_cast<_Float16>(h);
+                const float rem = h - static_cast<float>(hh);
+                const size_t off = (size_t)(grp.hrow0 + r) * f + n;
+                h_hi[off] = __builtin_bit_cast(uint16_t, hh);
+                h_lo[off] = f32_to_f16_bits(rem);
             }
     }
-    const int n = nt * 16 + rr;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < IMAX; ++i) {
-            const int r = mt * 16 + gq * 4 + i;
-            if (r >= nrows) continue;
-            const float h = swiglu(ag[mt][i], au[mt][i]);
-            const _Float16 hh = static_cast<_Float16>(h);
-            const float rem = h - static_cast<float>(hh);
-            const size_t off = (size_t)(grp.hrow0 + r) * f + n;
-            h_hi[off] = __builtin_bit_cast(uint16_t, hh);
-            h_lo[off] = f32_to_f16_bits(rem);
-        }
 }
 
 template <int FMT, int MT>
@@ -267,32 +266,51 @@ __device__ __forceinline__ void down_block(const DownUnit<FMT, MT> &U, f32x4 *ac
     }
 }
 
-// grid: (d_model/16 row tiles, group slots); NW waves split K = d_ff.
-// A tile row rr < 8 holds h_hi of group row 8*mt + rr, row 8 + rr its h_lo;
-// D rows 4*gq + i: hi rows in lanes gq = 0, 1 and lo rows in gq = 2, 3.
-template <int FMT, int MT, int IMAX, int NW>
-__global__ __launch_bounds__(64 * NW) void down_small_kernel(
-    QMatDev down, QMatDev sdown, const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
-    int T, int k, int d, int f, int E, const int32_t *__restrict__ offsets,
-    float *__restrict__ y_pairs, float *__restrict__ y_shared) {
-    __shared__ float red[NW][MT][IMAX][64];
-    const int ot = blockIdx.x;
-    const int slot = blockIdx.y;
-    const int P = T * k;
-    Group grp;
-    if (!find_group(offsets, E, T, P, slot, grp)) return;
-    const int lane = __lane_id();
-    const int wv = wave_uniform(threadIdx.x >> 6);
-    const int gq = lane >> 4, rr = lane & 15;
+// Down-projection weights of one batch of a wave's units (units u0 + NW b),
+// loadable before h is needed: the weights do not depend on it.
+template <int FMT, int MT, int NW>
+struct DownW {
+    static constexpr int NB = kBatch;
+    u32x2 lw[NB], sw[NB], mw[NB];
+    uint32_t hw[NB];
+};
+
+template <int FMT, int MT, int NW>
+__device__ __forceinline__ void down_load_w(DownW<FMT, MT, NW> &Wt, const QMatDev &down, const QMatDev &sdown,
+                                            int d, int f, const Group &grp, int ot, int u0) {
+    const int lane = __lane_id(), rr = lane & 15;
     const bool shared = grp.expert < 0;
     const QMatDev W = shared ? sdown : down;
     const int e = shared ? 0 : grp.expert;
     const int KC = f / 128;
     const size_t ubase = ((size_t)e * (d / 16) + ot) * KC;
-    const int nrows = grp.nrows;
+#pragma unroll
+    for (int b = 0; b < DownW<FMT, MT, NW>::NB; ++b) {
+        int u = u0 + NW * b;
+        u = u < KC ? u : KC - 1;   // clamped: unconditional loads, unused past KC
+        const size_t unit = ubase + u;
+        Wt.lw[b] = *reinterpret_cast<const u32x2 *>(W.lo + unit * 512 + lane * 8);
+        if constexpr (FMT == MOE_FMT_Q3_B32) Wt.hw[b] = *reinterpret_cast<const uint32_t *>(W.hi + unit * 256 + lane * 4);
+        Wt.sw[b] = *reinterpret_cast<const u32x2 *>(W.scale + unit * 64 + rr * 4);
+        if constexpr (FMT == MOE_FMT_Q2_B32) Wt.mw[b] = *reinterpret_cast<const u32x2 *>(W.min + unit * 64 + rr * 4);
+    }
+}
 
-    // rows past the group's last read its last row (never stored; keeps the
-    // loads unconditional)
+// One down task: 16 outputs (row tile ot) of one expert group, all rows; the
+// NW waves of the task (index wq) split K = d_ff.  Wt holds the first batch
+// of weights (units wq + NW b), loaded by the caller.  A tile row rr < 8
+// holds h_hi of group row 8 mt + rr, row 8 + rr its h_lo; D rows 4 gq + i:
+// hi rows in lanes gq = 0, 1 and lo rows in gq = 2, 3.
+template <int FMT, int MT, int IMAX, int NW>
+__device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev &down, const QMatDev &sdown,
+                                          const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
+                                          int d, int f, const Group &grp, int ot, int wq,
+                                          float (*red)[MT][IMAX][64], float *__restrict__ y_pairs,
+                                          float *__restrict__ y_shared) {
+    const int lane = __lane_id();
+    const int gq = lane >> 4, rr = lane & 15;
+    const int KC = f / 128;
+    const int nrows = grp.nrows;
     const uint16_t *hrow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -303,30 +321,26 @@ __global__ __launch_bounds__(64 * NW) void down_small_kernel(
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int u0 = wv; u0 < KC; u0 += NW * kBatch) {
-        DownUnit<FMT, MT> U[kBatch];
+    constexpr int NB = DownW<FMT, MT, NW>::NB;
+    for (int u0 = wq; u0 < KC; u0 += NW * NB) {
+        if (u0 != wq) down_load_w<FMT, MT, NW>(Wt, down, sdown, d, f, grp, ot, u0);
+        DownUnit<FMT, MT> U[NB];
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int u = u0 + NW * b;
-            if (u < KC) {
-                const size_t unit = ubase + u;
-                U[b].lw = *reinterpret_cast<const u32x2 *>(W.lo + unit * 512 + lane * 8);
-                if constexpr (FMT == MOE_FMT_Q3_B32)
-                    U[b].hw = *reinterpret_cast<const uint32_t *>(W.hi + unit * 256 + lane * 4);
-                U[b].sw = *reinterpret_cast<const u32x2 *>(W.scale + unit * 64 + rr * 4);
-                if constexpr (FMT == MOE_FMT_Q2_B32)
-                    U[b].mw = *reinterpret_cast<const u32x2 *>(W.min + unit * 64 + rr * 4);
+        for (int b = 0; b < NB; ++b) {
+            int u = u0 + NW * b;
+            u = u < KC ? u : KC - 1;
+            U[b].lw = Wt.lw[b];
+            U[b].sw = Wt.sw[b];
+            if constexpr (FMT == MOE_FMT_Q2_B32) U[b].mw = Wt.mw[b];
+            if constexpr (FMT == MOE_FMT_Q3_B32) U[b].hw = Wt.hw[b];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        U[b].A[mt][j] =
-                            *reinterpret_cast<const u32x4 *>(hrow[mt] + u * 128 + j * 32 + gq * 8);
-            }
+                for (int j = 0; j < 4; ++j) U[b].A[mt][j] =
+                        *reinterpret_cast<const u32x4 *>(hrow[mt] + u * 128 + j * 32 + gq * 8);
         }
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
+        for (int b = 0; b < NB; ++b) {
             if (u0 + NW * b < KC) {
                 down_block<FMT, MT, IMAX, 0>(U[b], acc);
                 down_block<FMT, MT, IMAX, 1>(U[b], acc);
@@ -339,19 +353,21 @@ __global__ __launch_bounds__(64 * NW) void down_small_kernel(
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int i = 0; i < IMAX; ++i) red[wv][mt][i][lane] = acc[mt][i];
+            for (int i = 0; i < IMAX; ++i) red[wq][mt][i][lane] = acc[mt][i];
         __syncthreads();
-        if (wv != 0) return;
+        if (wq == 0) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int i = 0; i < IMAX; ++i) {
-                float v = red[0][mt][i][lane];
+                for (int i = 0; i < IMAX; ++i) {
+                    float v = red[0][mt][i][lane];
 #pragma unroll
-                for (int w2 = 1; w2 < NW; ++w2) v += red[w2][mt][i][lane];
-                acc[mt][i] = v;
-            }
+                    for (int w2 = 1; w2 < NW; ++w2) v += red[w2][mt][i][lane];
+                    acc[mt][i] = v;
+                }
+        }
     }
+    if (wq != 0) return;
     // hi (rows 0..7, lanes 0..31) + lo (rows 8..15, lanes 32..63)
     const int o = ot * 16 + rr;
 #pragma unroll
@@ -361,11 +377,42 @@ __global__ __launch_bounds__(64 * NW) void down_small_kernel(
             const float y = acc[mt][i] + __shfl_xor(acc[mt][i], 32, 64);
             const int r = mt * 8 + gq * 4 + i;
             if (gq >= 2 || r >= nrows) continue;
-            if (shared)
+            if (grp.expert < 0)
                 y_shared[(size_t)r * d + o] = y;
             else
                 y_pairs[(size_t)(grp.row0 + r) * d + o] = y;
         }
+}
+
+// ---------------------------------------------------------------- kernels
+// grid: (d_ff/16 row tiles, 1 + min(E, P) group slots); NW waves split K.
+template <int FMT, int MT, int IMAX, int NW>
+__global__ __launch_bounds__(64 * NW) void gateup_small_kernel(
+    QMatDev gate, QMatDev up, QMatDev sgate, QMatDev sup, const uint16_t *__restrict__ x, int T,
+    int k, int d, int f, int E, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ sorted_pair, uint16_t *__restrict__ h_hi,
+    uint16_t *__restrict__ h_lo) {
+    __shared__ float red[NW][MT][2][IMAX][64];
+    Group grp;
+    if (!find_group(offsets, E, T, T * k, blockIdx.y, grp)) return;
+    gateup_task<FMT, MT, IMAX, NW>(gate, up, sgate, sup, x, k, d, f, sorted_pair, grp, blockIdx.x, red,
+                                          h_hi, h_lo);
+}
+
+// grid: (d_model/16 row tiles, group slots); NW waves split K = d_ff.
+template <int FMT, int MT, int IMAX, int NW>
+__global__ __launch_bounds__(64 * NW) void down_small_kernel(
+    QMatDev down, QMatDev sdown, const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
+    int T, int k, int d, int f, int E, const int32_t *__restrict__ offsets,
+    float *__restrict__ y_pairs, float *__restrict__ y_shared) {
+    __shared__ float red[NW][MT][IMAX][64];
+    Group grp;
+    if (!find_group(offsets, E, T, T * k, blockIdx.y, grp)) return;
+    const int wq = wave_uniform(threadIdx.x >> 6);
+    DownW<FMT, MT, NW> Wt;
+    down_load_w<FMT, MT, NW>(Wt, down, sdown, d, f, grp, blockIdx.x, wq);
+    down_task<FMT, MT, IMAX, NW>(Wt, down, sdown, h_hi, h_lo, d, f, grp, blockIdx.x, wq, red, y_pairs,
+                                        y_shared);
 }
 
 static QMatDev qm(const moe_qmat &m) { return QMatDev{m.lo, m.hi, m.scale, m.min}; }

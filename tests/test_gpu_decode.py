@@ -98,6 +98,8 @@ def test_workload_layer_parity(q, wid):
     (1, 1, 16, 2, 256, 128), (2, 2, 64, 8, 256, 256), (1, 3, 64, 8, 384, 128),
     (2, 5, 32, 4, 128, 384), (1, 17, 16, 2, 256, 128), (2, 32, 64, 10, 256, 128),
     (1, 9, 1, 1, 128, 128), (2, 4, 8, 8, 128, 128), (1, 16, 512, 10, 128, 128),
+    # more than 512 groups: the two-kernel form; d_ff = 1536: several down batches
+    (2, 32, 1024, 20, 128, 128), (1, 2, 16, 2, 128, 1536),
 ])
 def test_shape_sweep_parity(q, fmt, T, E, k, d, f):
     w = synth.custom(d, f, E, k, T, fmt=fmt, zipf_s=1.3 if fmt == 2 else 0.0, wid=200 + T)
@@ -124,8 +126,9 @@ def test_route_logits_input_ties(q, T, E, k):
     lg_d = torch.from_numpy(lg).cuda()
     ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
     wt = torch.empty(T, k, dtype=torch.float32, device="cuda")
-    ws = torch.zeros(4096, dtype=torch.uint8, device="cuda")
-    q.moe_route(None, None, None, lg_d, T, 2048, E, k, ids, wt, ws, 4096)
+    n_ws = q.moe_workspace_size(2048, 128, E, T, k)
+    ws = torch.zeros(n_ws, dtype=torch.uint8, device="cuda")
+    q.moe_route(None, None, None, lg_d, T, 2048, E, k, ids, wt, ws, n_ws)
     torch.cuda.synchronize()
     ids_ref, w_ref = oracle.topk_softmax(lg, k)
     assert np.array_equal(ids.cpu().numpy(), ids_ref)
@@ -262,12 +265,57 @@ def test_token_independence_gpu(q):
 
 
 def test_t_zero_is_noop(q):
-    ws = torch.zeros(8192, dtype=torch.uint8, device="cuda")
+    n_ws = q.moe_workspace_size(256, 128, 16, 1, 2)
+    ws = torch.zeros(n_ws, dtype=torch.uint8, device="cuda")
     lg = torch.full((1, 16), 3.0, device="cuda")
     ids = torch.full((1, 2), -7, dtype=torch.int32, device="cuda")
     wt = torch.full((1, 2), -7.0, device="cuda")
     x = torch.zeros(1, 256, dtype=torch.int16, device="cuda")
     wr = torch.zeros(256, 16, device="cuda")
-    q.moe_route(x, wr, None, lg, 0, 256, 16, 2, ids, wt, ws, 8192)
+    q.moe_route(x, wr, None, lg, 0, 256, 16, 2, ids, wt, ws, n_ws)
     torch.cuda.synchronize()
     assert torch.all(ids == -7) and torch.all(wt == -7.0) and torch.all(lg == 3.0)
+
+
+def test_back_to_back_calls_share_workspace(q):
+    """Consecutive layers on one workspace: the in-kernel ticket and per-group
+    counters must be back at zero after every call."""
+    from quantized_moe_route_amd.layer import alloc_buffers, run_layer
+    w = synth.custom(256, 128, 64, 8, 4, fmt=2, zipf_s=1.3, wid=310)
+    L = synth.gen_layer(w)
+    dl = _upload(L, w)
+    b = alloc_buffers(dl, w.T, w.k)
+    for step in range(3):
+        x = synth.gen_x(w, stream=step)
+        run_layer(dl, _x_dev(x), b)
+        torch.cuda.synchronize()
+        _check_layer(q, w, L, x, b)
+
+
+def test_graph_replay_matches_eager(q):
+    """The layer captured once in a HIP graph and replayed, with eager calls
+    and host synchronisations between replays: every replay equals the eager
+    result bitwise."""
+    from quantized_moe_route_amd import hip
+    from quantized_moe_route_amd.layer import alloc_buffers, run_layer
+    w = synth.custom(256, 256, 64, 8, 4, fmt=1, wid=320)
+    L = synth.gen_layer(w)
+    dl = _upload(L, w)
+    stream = torch.cuda.Stream()
+    xs = [_x_dev(synth.gen_x(w, stream=s)) for s in range(3)]
+    x_in = xs[0].clone()
+    with torch.cuda.stream(stream):
+        b = alloc_buffers(dl, w.T, w.k, stream=stream)
+    torch.cuda.synchronize()
+    with hip.Graph(stream.cuda_stream) as g:
+        run_layer(dl, x_in, b, stream=stream.cuda_stream)
+    for rep in range(3):
+        x_in.copy_(xs[rep])
+        torch.cuda.synchronize()
+        # eager reference on separate buffers
+        be = alloc_buffers(dl, w.T, w.k)
+        run_layer(dl, xs[rep], be)
+        torch.cuda.synchronize()
+        g.launch()
+        hip.stream_synchronize(stream.cuda_stream)
+        assert torch.equal(b.out, be.out) and torch.equal(b.ids, be.ids), rep
