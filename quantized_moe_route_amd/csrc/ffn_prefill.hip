@@ -226,47 +226,56 @@ __device__ __forceinline__ u32x4 bfrag_f16(const BRaw<FMT> &b) {
 
 // exact weights split as fp16 hi + lo: w = fp32(d*q + m) (exact), hi = fp16(w),
 // lo = fp16(w - hi).  qword holds two fp16 codes (Q3: lo + 4*bit2).
-template <int FMT>
-__device__ __forceinline__ void split_pair(uint32_t qword, float d, float m, float lo_scale, uint32_t &hi,
-                                           uint32_t &lo) {
-    const float q0 = static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)(qword & 0xffffu)));
-    const float q1 = static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)(qword >> 16)));
-    float w0, w1;
-    if constexpr (FMT == MOE_FMT_Q2_B32) {
-        w0 = fmaf(q0, d, m);
-        w1 = fmaf(q1, d, m);
-    } else {
-        w0 = d * (q0 - 4.0f);
-        w1 = d * (q1 - 4.0f);
-    }
-    const _Float16 h0 = (_Float16)w0, h1 = (_Float16)w1;
-    const _Float16 l0 = (_Float16)((w0 - (float)h0) * lo_scale);
-    const _Float16 l1 = (_Float16)((w1 - (float)h1) * lo_scale);
-    hi = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-    lo = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+// Exact weights split into fp16 hi + lo.  hi = fp16(d*q + m) is one packed
+// fp16 FMA (one rounding).  lo = fp16(w - hi) with w = d*q + m from a
+// mixed-precision FMA on the fp16 inputs, exact in fp32 for block-32 codes
+// and fp16 scales; w - hi is exact in fp32 too.  For the second pass of the
+// shared down projection lo is zeroed: d and m are scaled by s = 0 (exact) and
+// the residual is -hi*s + w*s.
+template <int SEL>
+__device__ __forceinline__ float fma_mix_f32(uint32_t q2, uint32_t d2, uint32_t m2) {
+    float r;
+    if constexpr (SEL == 0)
+        __asm__("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,1,1]" : "=v"(r) : "v"(q2), "v"(d2), "v"(m2));
+    else
+        __asm__("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,1,1]" : "=v"(r) : "v"(q2), "v"(d2), "v"(m2));
+    return r;
+}
+// fp16 pair (fp16(w0s - hi.lo * s), fp16(w1s - hi.hi * s))
+__device__ __forceinline__ uint32_t residual_pair(uint32_t hi2, float w0s, float w1s, float s) {
+    uint32_t r = 0;
+    __asm__("v_fma_mixlo_f16 %0, -%1, %2, %3 op_sel_hi:[1,0,0]" : "+v"(r) : "v"(hi2), "v"(s), "v"(w0s));
+    __asm__("v_fma_mixhi_f16 %0, -%1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(hi2), "v"(s), "v"(w1s));
+    return r;
 }
 
 // exact weights of block J as fp16 hi + lo (lo multiplied by lo_scale, 1 or 0)
 template <int FMT, int J>
 __device__ __forceinline__ void bfrag_split(const BRaw<FMT> &b, float lo_scale, u32x4 &hi, u32x4 &lo) {
     u32x4 q = lo_operand<J & 1, true>(b.lo[J >> 1]);
+    const uint32_t d = half_pair(b.sc, J);
+    uint32_t m;
     if constexpr (FMT == MOE_FMT_Q3_B32) {
         const u32x4 h4 = hi_operand<J, true>(b.hi);
         q.x = pk_add_f16(q.x, h4.x);
         q.y = pk_add_f16(q.y, h4.y);
         q.z = pk_add_f16(q.z, h4.z);
         q.w = pk_add_f16(q.w, h4.w);
+        m = pk_fma_f16(d, 0xC400C400u /* -4.0, -4.0 */, 0u);   // -4d, exact
+    } else {
+        m = half_pair(b.mn, J);
     }
-    const float d = half_bits_to_float((uint16_t)(b.sc[J >> 1] >> (16 * (J & 1))));
-    float m = 0.f;
-    if constexpr (FMT == MOE_FMT_Q2_B32) m = half_bits_to_float((uint16_t)(b.mn[J >> 1] >> (16 * (J & 1))));
-    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-    split_pair<FMT>(q.x, d, m, lo_scale, h0, l0);
-    split_pair<FMT>(q.y, d, m, lo_scale, h1, l1);
-    split_pair<FMT>(q.z, d, m, lo_scale, h2, l2);
-    split_pair<FMT>(q.w, d, m, lo_scale, h3, l3);
-    hi = u32x4{h0, h1, h2, h3};
-    lo = u32x4{l0, l1, l2, l3};
+    const uint32_t s2 = lo_scale != 0.f ? 0x3C003C00u : 0u;   // (s, s) in fp16
+    const uint32_t ds = pk_fma_f16(d, s2, 0u), ms = pk_fma_f16(m, s2, 0u);
+    uint32_t hv[4], lv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t qi = i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
+        hv[i] = pk_fma_f16(qi, d, m);
+        lv[i] = residual_pair(hv[i], fma_mix_f32<0>(qi, ds, ms), fma_mix_f32<1>(qi, ds, ms), lo_scale);
+    }
+    hi = u32x4{hv[0], hv[1], hv[2], hv[3]};
+    lo = u32x4{lv[0], lv[1], lv[2], lv[3]};
 }
 
 // Fragment of 32-block J from one code slot: fp16-rounded weights (routed),
@@ -293,6 +302,15 @@ __device__ __forceinline__ void frag_j(const BRaw<FMT> &b, int J, float lo_scale
 __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 // 64 lanes x 16 bytes from global memory straight into LDS [dst, dst + 1 KiB),
@@ -472,11 +490,8 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
                                                 pos * 16);
     };
 
-    // Loads return in issue order, so one vmcnt wait per step covers them:
-    //   3 stages: the weights of step kc + 1 load in sub-steps 0-1, the A copies
-    //     of step kc + 2 in sub-steps 2-5; vmcnt(8) leaves only the latter.
-    //   2 stages: the A copies and weights of step kc + 1 load in sub-steps
-    //     0-3; vmcnt(0).
+    // Loads return in issue order, so one vmcnt wait and one barrier per step
+    // cover them (see issue_part).
     BRaw<FMT> bcur[NTW][2], bnext[NTW][2];
     issue_a(0);
 #pragma unroll
@@ -496,6 +511,10 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
         const int ka = G::NSTAGE == 3 ? kc + 2 : kc + 1;     // A stage copied during this step
         const bool amore = G::NSTAGE == 3 ? more2 : more1;
         if (amore && MODE == 1 && SH && ka == KC) switch_to_lo();
+        // the next stages' loads are spread over the sub-steps, between the
+        // matrix ops.  3 stages: the weights of step kc + 1 in sub-steps
+        // 0-1, the A copy of step kc + 2 in sub-steps 2-5, so vmcnt(8) at the
+        // end of the step leaves only the latter in flight.
         auto issue_part = [&](int s) {
             if constexpr (G::NSTAGE == 3) {
                 if (s < 2) {
@@ -527,11 +546,11 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
             for (int m = 0; m < MT; ++m) af[0][m] = read_a(st, m, 0);
 #pragma unroll
             for (int n = 0; n < NTW; ++n) frag_j<FMT, SH>(bcur[n][0], 0, lo_scale, bf[0][n], bl[0][n]);
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int cb = s & 1, nb = cb ^ 1;
+            static_for<0, 8>([&](auto s_) {
+                constexpr int s = decltype(s_)::value;
+                constexpr int cb = s & 1, nb = cb ^ 1;
                 issue_part(s);
-                if (s < 7) {
+                if constexpr (s < 7) {
 #pragma unroll
                     for (int m = 0; m < MT; ++m) af[nb][m] = read_a(st, m, s + 1);
 #pragma unroll
@@ -547,7 +566,7 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
                     }
                 // keep the next step's reads and dequantisation within this step
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            });
         } else {
             // two waves per SIMD: the other wave covers the read latency
 #pragma unroll
@@ -673,18 +692,24 @@ __global__ __launch_bounds__(256, PfGeom<NTW>::OCC) void pf_gemm_kernel(PfGemmAr
     unsigned xcd;
     __asm__ volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcd));
     xcd &= PF_NXCD - 1;
+    // the ticket for the next unit is taken at the start of the current one
+    if (threadIdx.x == 0) s_ticket = atomicAdd(&a.sched->ticket[a.launch][xcd], 1);
+    __syncthreads();
     for (int q = 0; q < PF_NXCD;) {
         const int x = (int)((xcd + q) & (PF_NXCD - 1));
-        if (threadIdx.x == 0) s_ticket = atomicAdd(&a.sched->ticket[a.launch][x], 1);
-        __syncthreads();
         const int t = wave_uniform(s_ticket);
         const int i0 = a.sched->xq[x];
         const int n_units = (a.sched->xq[x + 1] - i0) * a.nt;
         if (t >= n_units) {
             ++q;
             __syncthreads();
+            if (threadIdx.x == 0 && q < PF_NXCD)
+                s_ticket = atomicAdd(&a.sched->ticket[a.launch][(xcd + q) & (PF_NXCD - 1)], 1);
+            __syncthreads();
             continue;
         }
+        int nxt = 0;
+        if (threadIdx.x == 0) nxt = atomicAdd(&a.sched->ticket[a.launch][x], 1);
         const PfItem item = a.items[i0 + t / a.nt];
         const int tile = t % a.nt;
         if (item.expert < 0) {
@@ -697,6 +722,9 @@ __global__ __launch_bounds__(256, PfGeom<NTW>::OCC) void pf_gemm_kernel(PfGemmAr
                 default: pf_unit<FMT, MODE, false, 4, NTW>(a, item, tile, As, s_row); break;
             }
         }
+        // pf_unit ended with a barrier: every thread has read s_ticket
+        if (threadIdx.x == 0) s_ticket = nxt;
+        __syncthreads();
     }
 }
 
