@@ -11,7 +11,7 @@
 //   down:     [rows of group g] x f  .  W_down_g^T              -> y (fp32)
 //
 // Scheduling.  A prepass turns the dispatch offsets into work items (group,
-// 128-row chunk) on the device: groups are ordered by work, largest first
+// chunk of up to 192 rows) on the device: groups are ordered by work, largest first
 // (the shared expert counts double: it runs two products per weight), and
 // dealt round-robin to the eight XCDs, so all chunks of one expert -- which
 // share its weights -- and all column tiles of one chunk -- which share its
@@ -23,7 +23,7 @@
 //
 // Operands:
 //   A (activations): x converted once to fp16 (exact for bf16 values in fp16
-//     range), or h.  Each 128-row x 128-column stage is copied global -> LDS
+//     range), or h.  Each 192-row x 128-column stage is copied global -> LDS
 //     by the direct-to-LDS loads (no registers), two stages in flight; the
 //     16-byte chunks of a row are XOR-swizzled by the row index so the
 //     fragment reads are free of bank conflicts.
@@ -41,9 +41,15 @@
 
 namespace moe {
 
-constexpr int PF_MT = 128;                        // rows per work item
+#ifndef MOE_PF_ROWS
+#define MOE_PF_ROWS 192
+#endif
+constexpr int PF_MT = MOE_PF_ROWS;                // rows per work item (multiple of 64, <= 192)
 constexpr int PF_KS = 128;                        // K per pipeline stage
-constexpr int PF_STAGE = PF_MT * PF_KS * 2;       // bytes of one A stage (32 KiB)
+constexpr int PF_STAGE = PF_MT * PF_KS * 2;       // bytes of one A stage
+constexpr int PF_NSTAGE = 3;                      // A stages in flight
+constexpr int PF_NI = PF_MT / 16;                 // A copy instructions per wave per stage
+static_assert(PF_MT % 64 == 0 && PF_MT <= 192, "item rows: a multiple of 64, at most 192");
 constexpr int PF_NXCD = 8;                        // XCDs (L2 domains) per device
 constexpr int PF_SORT = 2048;                     // sort slots, >= E + 1
 
@@ -319,9 +325,12 @@ __device__ __forceinline__ void copy_to_lds16(const void *src, void *dst) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
 }
 
-// s_waitcnt vmcnt(0) / vmcnt(8) (expcnt, lgkmcnt left alone)
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-__device__ __forceinline__ void wait_vm8() { __builtin_amdgcn_s_waitcnt(0x0F78); }
+// s_waitcnt vmcnt(N) (expcnt, lgkmcnt left alone)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 struct PfGemmArgs {
     QMatDev w0, w1;            // routed experts: gate, up (gate/up) or down (down)
@@ -337,16 +346,16 @@ struct PfGemmArgs {
     int k, d, f, nt, launch;
 };
 
-// Tile geometry, by n-tiles (of 32 weight rows) per wave, NTW:
-//   NTW = 4: one workgroup per CU (256 + 256 registers per lane), three A
-//            stages; a wave owns 64 h columns (gate/up) or 128 outputs (down).
-//   NTW = 2: two workgroups per CU (256 registers), two A stages; a wave owns
-//            32 h columns or 64 outputs.  The second workgroup's matrix ops
-//            fill the first one's epilogue, prologue and barrier time.
+// Tile geometry.  A unit is PF_MT rows x (4 waves x NTW n-tiles of 32 weight
+// rows), all of K; one workgroup per CU (up to 256 + 256 registers per lane)
+// with three A stages.  Accumulators: PF_MT / 32 m-tiles x NTW n-tiles x 16.
+//   gate/up: a wave owns HCOLS = 16 NTW h columns (NTW/2 gate + NTW/2 up
+//   n-tiles); down: OCOLS = 32 NTW outputs.
+#ifndef MOE_PF_NTW
+#define MOE_PF_NTW 2
+#endif
 template <int NTW>
 struct PfGeom {
-    static constexpr int NSTAGE = NTW == 4 ? 3 : 2;
-    static constexpr int OCC = NTW == 4 ? 1 : 2;
     static constexpr int HCOLS = 16 * NTW;          // gate/up: h columns per wave
     static constexpr int OCOLS = 32 * NTW;          // down: output columns per wave
     // epilogue staging per wave (in the A stages); pitches put rows 4 apart
@@ -354,8 +363,13 @@ struct PfGeom {
     static constexpr int EP0_PITCH = HCOLS + 8;     // [gate | up][32][EP0_PITCH] floats
     static constexpr int EP1_PITCH = OCOLS + 8;     // [32][EP1_PITCH] floats
     static constexpr int EP_WAVE = (2 * 32 * EP0_PITCH > 32 * EP1_PITCH ? 2 * 32 * EP0_PITCH : 32 * EP1_PITCH) * 4;
-    static_assert(4 * EP_WAVE <= NSTAGE * PF_STAGE, "epilogue staging must fit in the A stages");
+    static_assert(4 * EP_WAVE <= PF_NSTAGE * PF_STAGE, "epilogue staging must fit in the A stages");
+    // sub-steps that issue the next stages' loads: weights in [0, NBS), A
+    // copies (two per sub-step) in [NBS, NBS + PF_NI / 2)
+    static constexpr int NBS = NTW / 2 > 0 ? NTW / 2 : 1;
+    static_assert(NBS + PF_NI / 2 <= 8, "loads must fit in the eight sub-steps");
 };
+constexpr int kPfNtw = MOE_PF_NTW;
 
 // silu(g) * u with the hardware reciprocal (about 1 ulp): h is rounded to
 // fp16 right after
@@ -363,7 +377,7 @@ __device__ __forceinline__ float swiglu_fast(float g, float u) {
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
-// One unit: 128 rows of one item x one column tile, all of K.
+// One unit: the rows of one item x one column tile, all of K.
 // MODE 0 (gate/up, K = d): wave w owns h columns c0 = tile * 4 HCOLS + w HCOLS
 //   .. +HCOLS; n-tiles 0 .. NTW/2 - 1 are those gate rows, the rest the same
 //   up rows, so each SwiGLU pair sits in one lane and register.
@@ -399,31 +413,31 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
     }
     __syncthreads();
 
-    // A copy slots of this lane: instruction i covers tile rows 4 (8 wv + i)
-    // .. +4; lane l takes row R = 4 (8 wv + i) + l / 16 and stores physical
+    // A copy slots of this lane: instruction i covers tile rows 4 (NI wv + i)
+    // .. +4; lane l takes row R = 4 (NI wv + i) + l / 16 and stores physical
     // chunk l % 16, which holds logical chunk (l % 16) ^ (R % 16)
-    int arow_i[8];
+    int arow_i[PF_NI];
     const char *abase = reinterpret_cast<const char *>(a.a_hi);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) arow_i[i] = s_row[4 * (8 * wv + i) + (l >> 4)];
+    for (int i = 0; i < PF_NI; ++i) arow_i[i] = s_row[4 * (PF_NI * wv + i) + (l >> 4)];
     auto switch_to_lo = [&]() {
         abase = reinterpret_cast<const char *>(a.a_lo);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int R = 4 * (8 * wv + i) + (l >> 4);
+        for (int i = 0; i < PF_NI; ++i) {
+            const int R = 4 * (PF_NI * wv + i) + (l >> 4);
             arow_i[i] = item.row0 + (R < nrows ? R : nrows - 1);
         }
     };
     auto issue_a_part = [&](int kc, int i) {
         const int kk = kc < KC ? kc : kc - KC;
-        uint8_t *dst = As + (kc % G::NSTAGE) * PF_STAGE + wv * 8 * 1024;
-        const int R = 4 * (8 * wv + i) + (l >> 4);
+        uint8_t *dst = As + (kc % PF_NSTAGE) * PF_STAGE + wv * PF_NI * 1024;
+        const int R = 4 * (PF_NI * wv + i) + (l >> 4);
         const int c = (l & 15) ^ (R & 15);
         copy_to_lds16(abase + (size_t)arow_i[i] * (K * 2) + (kk * (PF_KS * 2) + c * 16), dst + i * 1024);
     };
     auto issue_a = [&](int kc) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) issue_a_part(kc, i);
+        for (int i = 0; i < PF_NI; ++i) issue_a_part(kc, i);
     };
 
     // B: storage-unit index (at kc = 0) of this lane's unit in n-tile n
@@ -496,101 +510,74 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
     issue_a(0);
 #pragma unroll
     for (int n = 0; n < NTW; ++n) load_b_tile(bcur, 0, n);
-    if (G::NSTAGE == 3 && NSTEP > 1) {
+    if (NSTEP > 1) {
         if (MODE == 1 && SH && KC == 1) switch_to_lo();
         issue_a(1);
-        wait_vm8();
+        wait_vm<PF_NI>();
     } else {
-        wait_vm0();
+        wait_vm<0>();
     }
     __syncthreads();
     for (int kc = 0; kc < NSTEP; ++kc) {
-        const int st = kc % G::NSTAGE;
+        const int st = kc % PF_NSTAGE;
         const bool more1 = kc + 1 < NSTEP, more2 = kc + 2 < NSTEP;
         const int kb = kc + 1 < KC ? kc + 1 : kc + 1 - KC;
-        const int ka = G::NSTAGE == 3 ? kc + 2 : kc + 1;     // A stage copied during this step
-        const bool amore = G::NSTAGE == 3 ? more2 : more1;
+        const int ka = kc + 2;     // A stage copied during this step
+        const bool amore = more2;
         if (amore && MODE == 1 && SH && ka == KC) switch_to_lo();
         // the next stages' loads are spread over the sub-steps, between the
-        // matrix ops.  3 stages: the weights of step kc + 1 in sub-steps
-        // 0-1, the A copy of step kc + 2 in sub-steps 2-5, so vmcnt(8) at the
-        // end of the step leaves only the latter in flight.
+        // matrix ops: the weights of step kc + 1 first, then the A copy of
+        // step kc + 2, so vmcnt(NI) at the end of the step leaves only the
+        // latter in flight
         auto issue_part = [&](int s) {
-            if constexpr (G::NSTAGE == 3) {
-                if (s < 2) {
-                    if (more1) {
+            if (s < G::NBS) {
+                if (more1) {
 #pragma unroll
-                        for (int n = s * NTW / 2; n < (s + 1) * NTW / 2; ++n) load_b_tile(bnext, kb, n);
-                    }
-                } else if (s < 6) {
-                    if (amore) {
-                        issue_a_part(ka, 2 * (s - 2));
-                        issue_a_part(ka, 2 * (s - 2) + 1);
-                    }
+                    for (int n = s * NTW / G::NBS; n < (s + 1) * NTW / G::NBS; ++n) load_b_tile(bnext, kb, n);
                 }
-            } else {
-                if (s < 4 && more1) {
-                    issue_a_part(ka, 2 * s);
-                    issue_a_part(ka, 2 * s + 1);
-                    if (s < NTW) load_b_tile(bnext, kb, s);
+            } else if (s < G::NBS + PF_NI / 2) {
+                if (amore) {
+                    issue_a_part(ka, 2 * (s - G::NBS));
+                    issue_a_part(ka, 2 * (s - G::NBS) + 1);
                 }
             }
         };
         // shared down, second pass (A = h_lo): weight lo fragments are zeroed
         const float lo_scale = (MODE == 1 && SH && kc >= KC) ? 0.f : 1.f;
-        if constexpr (G::OCC == 1) {
-            // one wave per SIMD: fragments of sub-step s + 1 are read and
-            // dequantised while the matrix ops of sub-step s run
-            u32x4 af[2][MT], bf[2][NTW], bl[2][NTW];
+        {
+        // one wave per SIMD: fragments of sub-step s + 1 are read and
+        // dequantised while the matrix ops of sub-step s run
+        u32x4 af[2][MT], bf[2][NTW], bl[2][NTW];
 #pragma unroll
-            for (int m = 0; m < MT; ++m) af[0][m] = read_a(st, m, 0);
+        for (int m = 0; m < MT; ++m) af[0][m] = read_a(st, m, 0);
 #pragma unroll
-            for (int n = 0; n < NTW; ++n) frag_j<FMT, SH>(bcur[n][0], 0, lo_scale, bf[0][n], bl[0][n]);
-            static_for<0, 8>([&](auto s_) {
-                constexpr int s = decltype(s_)::value;
-                constexpr int cb = s & 1, nb = cb ^ 1;
-                issue_part(s);
-                if constexpr (s < 7) {
+        for (int n = 0; n < NTW; ++n) frag_j<FMT, SH>(bcur[n][0], 0, lo_scale, bf[0][n], bl[0][n]);
+        static_for<0, 8>([&](auto s_) {
+            constexpr int s = decltype(s_)::value;
+            constexpr int cb = s & 1, nb = cb ^ 1;
+            issue_part(s);
+            if constexpr (s < 7) {
 #pragma unroll
-                    for (int m = 0; m < MT; ++m) af[nb][m] = read_a(st, m, s + 1);
+                for (int m = 0; m < MT; ++m) af[nb][m] = read_a(st, m, s + 1);
 #pragma unroll
-                    for (int n = 0; n < NTW; ++n)
-                        frag_j<FMT, SH>(bcur[n][(s + 1) & 1], (s + 1) >> 1, lo_scale, bf[nb][n], bl[nb][n]);
-                }
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-#pragma unroll
-                    for (int n = 0; n < NTW; ++n) {
-                        acc[m][n] = mfma32(af[cb][m], bf[cb][n], acc[m][n]);
-                        if constexpr (SH) acc[m][n] = mfma32(af[cb][m], bl[cb][n], acc[m][n]);
-                    }
-                // keep the next step's reads and dequantisation within this step
-                __builtin_amdgcn_sched_barrier(0);
-            });
-        } else {
-            // two waves per SIMD: the other wave covers the read latency
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                u32x4 af[MT], bf[NTW], bl[NTW];
-                issue_part(s);
-#pragma unroll
-                for (int m = 0; m < MT; ++m) af[m] = read_a(st, m, s);
-#pragma unroll
-                for (int n = 0; n < NTW; ++n) frag_j<FMT, SH>(bcur[n][s & 1], s >> 1, lo_scale, bf[n], bl[n]);
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-#pragma unroll
-                    for (int n = 0; n < NTW; ++n) {
-                        acc[m][n] = mfma32(af[m], bf[n], acc[m][n]);
-                        if constexpr (SH) acc[m][n] = mfma32(af[m], bl[n], acc[m][n]);
-                    }
-                __builtin_amdgcn_sched_barrier(0);
+                for (int n = 0; n < NTW; ++n)
+                    frag_j<FMT, SH>(bcur[n][(s + 1) & 1], (s + 1) >> 1, lo_scale, bf[nb][n], bl[nb][n]);
             }
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int n = 0; n < NTW; ++n) {
+                    acc[m][n] = mfma32(af[cb][m], bf[cb][n], acc[m][n]);
+                    if constexpr (SH) acc[m][n] = mfma32(af[cb][m], bl[cb][n], acc[m][n]);
+                }
+            // keep the next step's reads and dequantisation within this step
+            __builtin_amdgcn_sched_barrier(0);
+        });
         }
-        if (G::NSTAGE == 3 && more2)
-            wait_vm8();
+        if (more2)
+            wait_vm<PF_NI>();
         else
-            wait_vm0();
+            wait_vm<0>();
         __syncthreads();
 #pragma unroll
         for (int n = 0; n < NTW; ++n)
@@ -685,8 +672,8 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
 // Persistent grouped GEMM: workgroups take (item, column tile) units by
 // ticket from their XCD's queue, then from the others.
 template <int FMT, int MODE, int NTW>
-__global__ __launch_bounds__(256, PfGeom<NTW>::OCC) void pf_gemm_kernel(PfGemmArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t As[PfGeom<NTW>::NSTAGE * PF_STAGE];
+__global__ __launch_bounds__(256, 1) void pf_gemm_kernel(PfGemmArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t As[PF_NSTAGE * PF_STAGE];
     __shared__ int s_row[PF_MT];
     __shared__ int s_ticket;
     unsigned xcd;
@@ -712,14 +699,17 @@ __global__ __launch_bounds__(256, PfGeom<NTW>::OCC) void pf_gemm_kernel(PfGemmAr
         if (threadIdx.x == 0) nxt = atomicAdd(&a.sched->ticket[a.launch][x], 1);
         const PfItem item = a.items[i0 + t / a.nt];
         const int tile = t % a.nt;
+        constexpr int MTX = PF_MT / 32;
         if (item.expert < 0) {
-            pf_unit<FMT, MODE, true, 4, NTW>(a, item, tile, As, s_row);
+            pf_unit<FMT, MODE, true, MTX, NTW>(a, item, tile, As, s_row);
         } else {
             switch ((item.nrows + 31) >> 5) {
                 case 1: pf_unit<FMT, MODE, false, 1, NTW>(a, item, tile, As, s_row); break;
                 case 2: pf_unit<FMT, MODE, false, 2, NTW>(a, item, tile, As, s_row); break;
                 case 3: pf_unit<FMT, MODE, false, 3, NTW>(a, item, tile, As, s_row); break;
-                default: pf_unit<FMT, MODE, false, 4, NTW>(a, item, tile, As, s_row); break;
+                case 4: pf_unit<FMT, MODE, false, 4 < MTX ? 4 : MTX, NTW>(a, item, tile, As, s_row); break;
+                case 5: pf_unit<FMT, MODE, false, 5 < MTX ? 5 : MTX, NTW>(a, item, tile, As, s_row); break;
+                default: pf_unit<FMT, MODE, false, MTX, NTW>(a, item, tile, As, s_row); break;
             }
         }
         // pf_unit ended with a barrier: every thread has read s_ticket
@@ -764,7 +754,7 @@ size_t ffn_prefill_ws_bytes(int d, int f, int E, int T, int k) {
            align256(((size_t)T * k + T) * f * 2) + align256((size_t)T * f * 2);
 }
 
-// persistent grid: OCC workgroups per compute unit
+// persistent grid: occ workgroups per compute unit
 static int pf_grid(int occ) {
     static int cached[64];
     int dev = 0;
@@ -778,10 +768,6 @@ static int pf_grid(int occ) {
     return cached[dev] * occ;
 }
 
-#ifndef MOE_PF_NTW
-#define MOE_PF_NTW 4
-#endif
-constexpr int kPfNtw = MOE_PF_NTW;
 
 template <int FMT>
 static void pf_launch_fmt(const moe_layer &L, const uint16_t *x, int T, int k, const int32_t *offsets,
@@ -807,7 +793,7 @@ static void pf_launch_fmt(const moe_layer &L, const uint16_t *x, int T, int k, c
     a.d = d;
     a.f = f;
     using G = PfGeom<kPfNtw>;
-    const int grid = pf_grid(G::OCC);
+    const int grid = pf_grid(1);
     // gate/up + SwiGLU
     a.w0 = QMatDev{L.gate.lo, L.gate.hi, L.gate.scale, L.gate.min};
     a.w1 = QMatDev{L.up.lo, L.up.hi, L.up.scale, L.up.min};
