@@ -97,10 +97,10 @@ moe_status moe_route(const uint16_t *x_bf16, const float *w_router, const float 
     if (T == 0) return MOE_OK;
     hipStream_t s = as_stream(stream);
     if (!w_router) return launched(launch_topk(logits, T, E, k, topk_ids, topk_w, s));
-    if (route_ws_bytes(d_model, E, T) > 0)
+    if (T <= kRouteSmallTMax)
         return launched(launch_route_small(x_bf16, w_router, bias, logits, T, d_model, E, k,
                                            topk_ids, topk_w, ws, s));
-    hipError_t e = launch_router_gemm(x_bf16, w_router, bias, logits, T, d_model, E, s);
+    hipError_t e = launch_router_gemm(x_bf16, w_router, bias, logits, T, d_model, E, ws, s);
     if (e != hipSuccess) return launched(e);
     return launched(launch_topk(logits, T, E, k, topk_ids, topk_w, s));
 }

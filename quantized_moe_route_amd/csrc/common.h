@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/moe.h"
 
 namespace moe {
@@ -108,6 +110,39 @@ __device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// 64 lanes x 16 bytes from global memory straight into LDS [dst, dst + 1 KiB),
+// lane l's bytes at dst + 16 l.
+__device__ __forceinline__ void copy_to_lds16(const void *src, void *dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (expcnt, lgkmcnt left alone)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that waits for nothing itself.  __syncthreads() makes the
+// compiler drain every outstanding vector-memory operation first (vmcnt(0))
+// when global->LDS copies are in flight, which empties a multi-stage copy
+// pipeline at each step.  Callers wait for exactly what the other waves must
+// see (wait_vm<N>: their own copies into the stage about to be read) and then
+// meet here; the memory clobber keeps the compiler from moving LDS or global
+// accesses across the barrier.  Each wave's reads of a stage are consumed by
+// its own matrix ops before it arrives, so a stage that is refilled after the
+// barrier has no reads pending.
+__device__ __forceinline__ void wg_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
 
 // Locate the group handled by `slot`: slot 0 = shared expert (rows 0..T-1 in
 // token order), slot s >= 1 = the (s-1)-th expert with a non-empty segment.
@@ -222,7 +257,9 @@ hipError_t launch_route_small(const uint16_t *x, const float *wr, const float *b
                               int T, int d, int E, int k, int32_t *ids, float *w, void *ws,
                               hipStream_t s);
 hipError_t launch_router_gemm(const uint16_t *x, const float *wr, const float *bias, float *logits,
-                              int T, int d, int E, hipStream_t s);
+                              int T, int d, int E, void *ws, hipStream_t s);
+size_t router_gemm_ws_bytes(int d, int E);
+constexpr int kRouteSmallTMax = 8;   // T above this: router GEMM + top-k kernel
 hipError_t launch_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w,
                        hipStream_t s);
 size_t route_ws_bytes(int d, int E, int T);

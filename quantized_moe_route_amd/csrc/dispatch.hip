@@ -110,6 +110,8 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t *__r
 }
 
 // ----------------------------------------------------------- three passes
+// 1. count: cnt[c][e] = pairs of expert e in chunk c (chunk-major, so a wave's
+//    64 lanes touch 64 consecutive experts).
 __global__ __launch_bounds__(64) void dispatch_count_kernel(const int32_t *__restrict__ ids, int T,
                                                             int E, int k,
                                                             int32_t *__restrict__ cnt) {
@@ -122,54 +124,121 @@ __global__ __launch_bounds__(64) void dispatch_count_kernel(const int32_t *__res
     for (int i = threadIdx.x; i < E; i += 64) cnt[(size_t)c * E + i] = __popcll(masks[i]);
 }
 
+// 2. scan, one workgroup per 64 experts (lane = expert), 16 waves splitting
+//    the chunks: cnt[c][e] := pairs of e in chunks before c, tot[e] := all
+//    pairs of e.  Loads go out 16 at a time.
+constexpr int kScanBatch = 16;
+
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t *__restrict__ cnt, int n_chunks,
-                                                             int E, int P,
-                                                             int32_t *__restrict__ offsets) {
-    __shared__ int32_t tot[1024];
-    __shared__ int wsum[16];
-    const int tid = threadIdx.x;
-    if (tid < E) {
-        int run = 0;
-        for (int c = 0; c < n_chunks; ++c) {
-            const int v = cnt[(size_t)c * E + tid];
-            cnt[(size_t)c * E + tid] = run;
-            run += v;
+                                                             int E, int32_t *__restrict__ tot) {
+    __shared__ int32_t seg[16][64];
+    const int l = __lane_id(), wv = threadIdx.x >> 6;
+    const int e = blockIdx.x * 64 + l;
+    const int per = (n_chunks + 15) / 16;
+    const int c0 = wv * per;
+    const int c1 = c0 + per < n_chunks ? c0 + per : n_chunks;
+    const bool ok = e < E;
+    int sum = 0;
+    if (ok) {
+        for (int cb = c0; cb < c1; cb += kScanBatch) {
+            int v[kScanBatch];
+#pragma unroll
+            for (int i = 0; i < kScanBatch; ++i) {
+                const int c = cb + i < c1 ? cb + i : c1 - 1;
+                v[i] = cnt[(size_t)c * E + e];
+            }
+#pragma unroll
+            for (int i = 0; i < kScanBatch; ++i) sum += cb + i < c1 ? v[i] : 0;
         }
-        tot[tid] = run;
     }
+    seg[wv][l] = sum;
     __syncthreads();
-    block_excl_scan_1024(tot, E, wsum);
-    __syncthreads();
-    if (tid < E) {
-        const int o = tot[tid];
-        offsets[tid] = o;
-        for (int c = 0; c < n_chunks; ++c) cnt[(size_t)c * E + tid] += o;
+    int run = 0, total = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int v = seg[q][l];
+        run += q < wv ? v : 0;
+        total += v;
     }
-    if (tid == 0) offsets[E] = P;
+    if (!ok) return;
+    if (wv == 0) tot[e] = total;
+    for (int cb = c0; cb < c1; cb += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i) {
+            const int c = cb + i < c1 ? cb + i : c1 - 1;
+            v[i] = cnt[(size_t)c * E + e];
+        }
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i) {
+            if (cb + i < c1) {
+                cnt[(size_t)(cb + i) * E + e] = run;
+                run += v[i];
+            }
+        }
+    }
 }
 
+// 3. place, one wave per chunk: expert offsets = exclusive scan of tot (each
+//    lane sums a run of up to 16 experts, then a wave scan), written out by
+//    chunk 0; position = offsets[e] + cnt[c][e] + earlier lanes of the chunk.
 __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *__restrict__ ids, int T,
                                                             int E, int k,
-                                                            const int32_t *__restrict__ cbase,
+                                                            const int32_t *__restrict__ cnt,
+                                                            const int32_t *__restrict__ tot,
+                                                            int32_t *__restrict__ offsets,
                                                             int32_t *__restrict__ sorted_pair,
                                                             int32_t *__restrict__ pair_pos) {
     __shared__ unsigned long long masks[1024];
+    __shared__ int32_t off[1024];
     const int c = blockIdx.x;
-    for (int i = threadIdx.x; i < E; i += 64) masks[i] = 0ull;
+    const int lane = __lane_id();
+    for (int i = lane; i < E; i += 64) masks[i] = 0ull;
+    const int per = (E + 63) / 64;   // <= 16
+    const int e0 = lane * per;
+    int v[16];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = e0 + i;
+        v[i] = (i < per && e < E) ? tot[e] : 0;
+        sum += v[i];
+    }
+    int run = wave_incl_scan(sum) - sum;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = e0 + i;
+        if (i < per && e < E) {
+            off[e] = run;
+            if (c == 0) offsets[e] = run;
+        }
+        run += v[i];
+    }
+    if (c == 0 && lane == 63) offsets[E] = run;
     __syncthreads();
     build_chunk_masks(ids, T, k, c, masks);
     __syncthreads();
-    write_chunk_positions(ids, T, k, c, masks, cbase + (size_t)c * E, sorted_pair, pair_pos);
+    const int t = c * 64 + lane;
+    if (t >= T) return;
+    const unsigned long long lt = below_mask(lane);
+    for (int j = 0; j < k; ++j) {
+        const int e = ids[(size_t)t * k + j];
+        const int pos = off[e] + cnt[(size_t)c * E + e] + __popcll(masks[e] & lt);
+        const int p = t * k + j;
+        sorted_pair[pos] = p;
+        pair_pos[p] = pos;
+    }
 }
 
 static bool dispatch_fits_small(int E, int T) {
     return (size_t)((T + 63) / 64) * E <= (size_t)kSmallMaskEntries;
 }
 
+// cnt [n_chunks][E], then tot [E]
 size_t dispatch_ws_bytes(int E, int T, int k) {
     (void)k;
     if (dispatch_fits_small(E, T)) return 0;
-    return (size_t)((T + 63) / 64) * E * sizeof(int32_t);
+    return ((size_t)((T + 63) / 64) * E + E) * sizeof(int32_t);
 }
 
 hipError_t launch_dispatch(const int32_t *ids, int T, int E, int k, int32_t *offsets,
@@ -181,11 +250,12 @@ hipError_t launch_dispatch(const int32_t *ids, int T, int E, int k, int32_t *off
     }
     const int n_chunks = (T + 63) / 64;
     int32_t *cnt = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + kWsHeader);
+    int32_t *tot = cnt + (size_t)n_chunks * E;
     hipLaunchKernelGGL(dispatch_count_kernel, dim3(n_chunks), dim3(64), 0, s, ids, T, E, k, cnt);
-    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, cnt, n_chunks, E, T * k,
-                       offsets);
-    hipLaunchKernelGGL(dispatch_place_kernel, dim3(n_chunks), dim3(64), 0, s, ids, T, E, k, cnt,
-                       sorted_pair, pair_pos);
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3((E + 63) / 64), dim3(1024), 0, s, cnt, n_chunks, E,
+                       tot);
+    hipLaunchKernelGGL(dispatch_place_kernel, dim3(n_chunks), dim3(64), 0, s, ids, T, E, k, cnt, tot,
+                       offsets, sorted_pair, pair_pos);
     return hipGetLastError();
 }
 

@@ -310,28 +310,6 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
-    }
-}
-
-// 64 lanes x 16 bytes from global memory straight into LDS [dst, dst + 1 KiB),
-// lane l's bytes at dst + 16 l.
-__device__ __forceinline__ void copy_to_lds16(const void *src, void *dst) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
-}
-
-// s_waitcnt vmcnt(N) (expcnt, lgkmcnt left alone)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
 struct PfGemmArgs {
     QMatDev w0, w1;            // routed experts: gate, up (gate/up) or down (down)
     QMatDev s0, s1;            // shared expert, same roles
@@ -517,6 +495,10 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
     } else {
         wait_vm<0>();
     }
+    // a full barrier here (it also drains stage 1): with no copy in flight at
+    // loop entry the compiler adds no vector-memory wait before the LDS reads
+    // of the steps, so the copy of step kc + 2 stays in flight through the
+    // barrier that ends step kc
     __syncthreads();
     for (int kc = 0; kc < NSTEP; ++kc) {
         const int st = kc % PF_NSTAGE;
@@ -578,13 +560,17 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
             wait_vm<PF_NI>();
         else
             wait_vm<0>();
-        __syncthreads();
+        wg_barrier();
 #pragma unroll
         for (int n = 0; n < NTW; ++n)
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl) bcur[n][sl] = bnext[n][sl];
     }
 
+    // every copy has landed (the last step waited for all); said once more
+    // outside the branch so the compiler knows it and does not make each LDS
+    // read of the epilogue wait for the stores before it
+    wait_vm<0>();
     // epilogue, one m-tile at a time through a wave-private LDS region (the A
     // stages are free now): accumulators out as written by the matrix core
     // (D row 8 (r / 4) + 4 h + r % 4, column l % 32), then read back along

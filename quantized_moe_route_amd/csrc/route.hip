@@ -179,6 +179,108 @@ __device__ __forceinline__ void wave_topk_any(const float *lg, int E, int k, int
         wave_topk<16, DEV_LOADS>(lg, E, k, ids, w, sel, seli);
 }
 
+// ------------------------------------------- top-k on ordered keys (wave)
+// For k <= 64, one wave per token.  Each logit becomes an unsigned key that
+// orders like the float (sign-magnitude mapped to offset binary; -0.0 read as
+// +0.0); 0 marks an empty or already taken entry, which no finite logit maps
+// to.  Lane l owns experts l, l + 64, ...; each round takes the wave maximum
+// key with six DPP max steps, finds the lanes holding it by ballot and, only
+// on a tie, the lowest expert among them by a second reduction.  The owner
+// clears the entry; lane j keeps the j-th selection in registers.
+__device__ __forceinline__ uint32_t ord_key(float v) {
+    uint32_t f = __float_as_uint(v);
+    if (f == 0x80000000u) f = 0u;
+    return (f & 0x80000000u) ? ~f : (f | 0x80000000u);
+}
+__device__ __forceinline__ float ord_value(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+    return o > v ? o : v;
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_min_u32(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+    return o < v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = dpp_max_u32<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    v = dpp_max_u32<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    v = dpp_max_u32<0x141, 0xF>(v);   // row_half_mirror
+    v = dpp_max_u32<0x140, 0xF>(v);   // row_mirror
+    v = dpp_max_u32<0x142, 0xA>(v);   // row_bcast:15 -> rows 1, 3
+    v = dpp_max_u32<0x143, 0xC>(v);   // row_bcast:31 -> rows 2, 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = dpp_min_u32<0xB1, 0xF>(v);
+    v = dpp_min_u32<0x4E, 0xF>(v);
+    v = dpp_min_u32<0x141, 0xF>(v);
+    v = dpp_min_u32<0x140, 0xF>(v);
+    v = dpp_min_u32<0x142, 0xA>(v);
+    v = dpp_min_u32<0x143, 0xC>(v);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+template <int PER>
+__device__ void wave_topk_ord(const float *__restrict__ lg, int E, int k, int32_t *__restrict__ ids,
+                              float *__restrict__ w) {
+    const int l = __lane_id();
+    uint32_t key[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = l + 64 * i;
+        const float v = lg[e < E ? e : 0];
+        key[i] = e < E ? ord_key(v) : 0u;
+    }
+    // lane's best: largest key, lowest slot among equals
+    auto local_best = [&](uint32_t &bk, int &bs) {
+        bk = key[0];
+        bs = 0;
+#pragma unroll
+        for (int i = 1; i < PER; ++i) {
+            const bool take = key[i] > bk;
+            bk = take ? key[i] : bk;
+            bs = take ? i : bs;
+        }
+    };
+    uint32_t bk;
+    int bs;
+    local_best(bk, bs);
+    uint32_t my_key = 0u;
+    int my_id = 0;
+    for (int j = 0; j < k; ++j) {
+        const uint32_t m = wave_max_u32(bk);
+        const unsigned long long hold = __ballot(bk == m);
+        int e;
+        if (__popcll(hold) == 1) {
+            const int owner = __builtin_ctzll(hold);
+            e = owner + 64 * __builtin_amdgcn_readlane(bs, owner);
+        } else {
+            e = (int)wave_min_u32(bk == m ? (uint32_t)(l + 64 * bs) : 0xffffffffu);
+        }
+        if (l == j) {
+            my_key = m;
+            my_id = e;
+        }
+        if (l == (e & 63)) {
+            const int slot = e >> 6;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) key[i] = i == slot ? 0u : key[i];
+        }
+        local_best(bk, bs);
+    }
+    const float l0 = ord_value((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
+    const float ev = l < k ? expf(ord_value(my_key) - l0) : 0.0f;
+    const float inv = 1.0f / wave_sum(ev);
+    if (l < k) {
+        w[l] = ev * inv;
+        ids[l] = my_id;
+    }
+}
+
 // -------------------------------------------------- top-k by ranking (block)
 // For k <= 32: every logit becomes a 64-bit key that orders exactly like
 // (larger value, then lower index): the float bits mapped to an unsigned
@@ -259,7 +361,7 @@ __device__ void block_topk_rank(const unsigned long long *keys, unsigned long lo
 // out at device scope; the last of all workgroups to arrive adds the d/128
 // partials of every (token, expert) in chunk order, writes the logits and
 // runs the top-k from LDS.
-constexpr int kMaxSmallT = 8;
+constexpr int kMaxSmallT = kRouteSmallTMax;
 
 __global__ __launch_bounds__(512) void route_small_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
@@ -355,7 +457,7 @@ __global__ __launch_bounds__(512) void route_small_kernel(
 }
 
 size_t route_ws_bytes(int d, int E, int T) {
-    if (T > kMaxSmallT) return 0;
+    if (T > kRouteSmallTMax) return router_gemm_ws_bytes(d, E);
     return (size_t)(d / 128) * T * E * sizeof(float);
 }
 
@@ -371,22 +473,29 @@ hipError_t launch_route_small(const uint16_t *x, const float *wr, const float *b
 }
 
 // ------------------------------------------------------------ top-k kernel
-// Logits given: two tokens per 256-thread workgroup ranked as above; for
-// k > 32 one wave per token selects serially.
-__global__ __launch_bounds__(256) void topk_rank_kernel(const float *__restrict__ logits, int T,
+// Logits given: one wave per token, four tokens per workgroup.  k <= 64 keeps
+// every selection in registers; larger k selects serially through LDS.
+constexpr int kWaveTopkMaxK = 64;
+
+__global__ __launch_bounds__(256) void topk_wave_kernel(const float *__restrict__ logits, int T,
                                                         int E, int k, int32_t *__restrict__ ids,
                                                         float *__restrict__ w) {
-    __shared__ unsigned long long keys[2 * 1024];
-    __shared__ unsigned long long cand[2 * 16 * kRankMaxK];
-    __shared__ unsigned long long selk[2 * kRankMaxK];
-    const int t0 = blockIdx.x * 2;
-    const int nt = (T - t0) < 2 ? (T - t0) : 2;
-    for (int i = threadIdx.x; i < nt * E; i += 256) {
-        const int t = i / E, e = i - t * E;
-        keys[i] = topk_key(logits[(size_t)(t0 + t) * E + e], e);
-    }
-    __syncthreads();
-    block_topk_rank<256>(keys, cand, nt, E, k, ids + (size_t)t0 * k, w + (size_t)t0 * k, selk);
+    const int wv = wave_uniform(threadIdx.x >> 6);
+    const int t = blockIdx.x * 4 + wv;
+    if (t >= T) return;
+    const float *lg = logits + (size_t)t * E;
+    int32_t *it = ids + (size_t)t * k;
+    float *wt = w + (size_t)t * k;
+    if (E <= 64)
+        wave_topk_ord<1>(lg, E, k, it, wt);
+    else if (E <= 128)
+        wave_topk_ord<2>(lg, E, k, it, wt);
+    else if (E <= 256)
+        wave_topk_ord<4>(lg, E, k, it, wt);
+    else if (E <= 512)
+        wave_topk_ord<8>(lg, E, k, it, wt);
+    else
+        wave_topk_ord<16>(lg, E, k, it, wt);
 }
 
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
@@ -403,8 +512,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 
 hipError_t launch_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w,
                        hipStream_t s) {
-    if (k <= kRankMaxK)
-        hipLaunchKernelGGL(topk_rank_kernel, dim3((T + 1) / 2), dim3(256), 0, s, logits, T, E, k,
+    if (k <= kWaveTopkMaxK)
+        hipLaunchKernelGGL(topk_wave_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k,
                            ids, w);
     else
         hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
@@ -412,112 +521,224 @@ hipError_t launch_topk(const float *logits, int T, int E, int k, int32_t *ids, f
 }
 
 // ------------------------------------------------------- large T: MFMA GEMM
-// Tile: 64 tokens x 64 experts per workgroup, K step 32.  Four waves in a 2x2
-// grid, each owning 32x32 = 2x2 MFMA 16x16 tiles.  LDS holds the x tile
-// (bf16, [64][32]) and the three bf16 terms of the router tile, transposed to
-// [n][k] so each lane reads 8 consecutive k with one 16-byte load.
-constexpr int RG_M = 64, RG_N = 64, RG_K = 32, RG_PAD = 8;
+// The fp32 router matrix is split exactly into three bf16 terms by truncation
+// (hi + mid + lo == w; the last remainder has at most 8 significant bits) and
+// stored transposed, [3][E][d], in the workspace.  x is bf16 already, so every
+// product is exact and only the fp32 accumulation order differs from a plain
+// fp32 dot product.
+//
+// GEMM: one workgroup of four waves (2 x 2) per 256 tokens x 64 experts; a
+// wave owns 128 tokens x 32 experts, four 32x32x16 MFMA tiles, each fed the
+// three weight terms.  K advances 32 at a time through a ring of five LDS
+// stages (140 KiB) filled by global->LDS DMA (28 KiB a stage: 256 rows of x and 3 x 64
+// rows of weight terms, 64 bytes each).  16-byte chunk c of row r is stored
+// at chunk c ^ ((r >> 1) & 3) of its row, so the 32 rows an operand read
+// touches fall on distinct banks.  Workgroups are dealt to the eight XCDs so
+// that the expert tiles of one token tile share an XCD, and its L2 serves x.
+constexpr int RG_TM = 256, RG_TN = 64, RG_KS = 32, RG_NS = 5;
+constexpr int RG_ABYTES = RG_TM * RG_KS * 2;        // 16 KiB of x
+constexpr int RG_BBYTES = 3 * RG_TN * RG_KS * 2;    // 12 KiB of weight terms
+constexpr int RG_STAGE = RG_ABYTES + RG_BBYTES;
+constexpr int RG_AI = RG_ABYTES / 1024 / 4;         // 1 KiB DMA copies per wave and stage: 4
+constexpr int RG_BI = RG_BBYTES / 1024 / 4;         // 3
+constexpr int RG_VM = RG_AI + RG_BI;                // vector-memory ops per stage and wave
 
 __device__ __forceinline__ void split3(float v, uint16_t &h, uint16_t &m, uint16_t &lo) {
-    uint32_t u = __float_as_uint(v);
+    const uint32_t u = __float_as_uint(v);
     h = (uint16_t)(u >> 16);
-    float r1 = v - __uint_as_float(u & 0xffff0000u);
-    uint32_t u1 = __float_as_uint(r1);
+    const float r1 = v - __uint_as_float(u & 0xffff0000u);
+    const uint32_t u1 = __float_as_uint(r1);
     m = (uint16_t)(u1 >> 16);
-    float r2 = r1 - __uint_as_float(u1 & 0xffff0000u);
-    lo = (uint16_t)(__float_as_uint(r2) >> 16);   // r2 has <= 8 significant bits: exact
+    const float r2 = r1 - __uint_as_float(u1 & 0xffff0000u);
+    lo = (uint16_t)(__float_as_uint(r2) >> 16);
 }
 
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__restrict__ x,
-                                                          const float *__restrict__ wr,
-                                                          const float *__restrict__ bias,
-                                                          float *__restrict__ logits, int T, int d,
-                                                          int E) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[RG_M][RG_K + RG_PAD];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[3][RG_N][RG_K + RG_PAD];
+// wr [d][E] fp32 -> wt [3][E][d] bf16 terms.  Block = 64 k x 64 experts.
+__global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ wr, int d,
+                                                           int E, uint16_t *__restrict__ wt) {
+    __shared__ float tile[64][65];
+    const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
     const int tid = threadIdx.x;
-    const int lane = __lane_id();
-    const int wv = wave_uniform(tid >> 6);
-    const int m0 = blockIdx.x * RG_M, n0 = blockIdx.y * RG_N;
-    const int wm = (wv >> 1) * 32, wn = (wv & 1) * 32;
-    f32x4 acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int k0 = 0; k0 < d; k0 += RG_K) {
-        // A: 64 rows x 32 bf16 = 256 x 16 B
-        {
-            const int r = tid >> 2, c = (tid & 3) * 8;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (m0 + r < T) v = *reinterpret_cast<const u32x4 *>(x + (size_t)(m0 + r) * d + k0 + c);
-            *reinterpret_cast<u32x4 *>(&As[r][c]) = v;
-        }
-        // B: 32 k-rows x 64 experts fp32 = 512 float4: two per thread
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int idx = tid + q * 256;
-            const int kr = idx >> 4, nc = (idx & 15) * 4;
-            float4 v = {0.f, 0.f, 0.f, 0.f};
-            const float *p = wr + (size_t)(k0 + kr) * E + n0 + nc;
-            if (n0 + nc + 3 < E) {
-                v = *reinterpret_cast<const float4 *>(p);
-            } else {
-                if (n0 + nc + 0 < E) v.x = p[0];
-                if (n0 + nc + 1 < E) v.y = p[1];
-                if (n0 + nc + 2 < E) v.z = p[2];
-            }
-            const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint16_t h, m, lo;
-                split3(vv[i], h, m, lo);
-                Bs[0][nc + i][kr] = h;
-                Bs[1][nc + i][kr] = m;
-                Bs[2][nc + i][kr] = lo;
-            }
-        }
-        __syncthreads();
-        const int g = lane >> 4, rr = lane & 15;
-        u32x4 af[2], bfr[3][2];
-#pragma unroll
-        for (int a = 0; a < 2; ++a) af[a] = *reinterpret_cast<const u32x4 *>(&As[wm + a * 16 + rr][g * 8]);
-#pragma unroll
-        for (int t3 = 0; t3 < 3; ++t3)
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-                bfr[t3][b] = *reinterpret_cast<const u32x4 *>(&Bs[t3][wn + b * 16 + rr][g * 8]);
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                acc[a][b] = mfma_bf16(af[a], bfr[2][b], acc[a][b]);
-                acc[a][b] = mfma_bf16(af[a], bfr[1][b], acc[a][b]);
-                acc[a][b] = mfma_bf16(af[a], bfr[0][b], acc[a][b]);
-            }
-        __syncthreads();
+    for (int i = tid; i < 64 * 64; i += 256) {
+        const int r = i >> 6, c = i & 63;
+        tile[r][c] = e0 + c < E ? wr[(size_t)(k0 + r) * E + e0 + c] : 0.0f;
     }
-    // D: lane holds rows 4*(lane/16)+i, column lane%16
+    __syncthreads();
+    const int el = tid >> 2, kq = (tid & 3) * 16;   // expert row, 16 consecutive k
+    if (e0 + el >= E) return;
+    uint32_t h[8], m[8], lo[8];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int i = 0; i < 8; ++i) {
+        uint16_t h0, m0, l0, h1, m1, l1;
+        split3(tile[kq + 2 * i][el], h0, m0, l0);
+        split3(tile[kq + 2 * i + 1][el], h1, m1, l1);
+        h[i] = h0 | ((uint32_t)h1 << 16);
+        m[i] = m0 | ((uint32_t)m1 << 16);
+        lo[i] = l0 | ((uint32_t)l1 << 16);
+    }
+    const size_t o = (size_t)(e0 + el) * d + k0 + kq;
+    const size_t term = (size_t)E * d;
+    u32x4 *p0 = reinterpret_cast<u32x4 *>(wt + o);
+    u32x4 *p1 = reinterpret_cast<u32x4 *>(wt + term + o);
+    u32x4 *p2 = reinterpret_cast<u32x4 *>(wt + 2 * term + o);
+    p0[0] = u32x4{h[0], h[1], h[2], h[3]};
+    p0[1] = u32x4{h[4], h[5], h[6], h[7]};
+    p1[0] = u32x4{m[0], m[1], m[2], m[3]};
+    p1[1] = u32x4{m[4], m[5], m[6], m[7]};
+    p2[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    p2[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
+}
+
+__device__ __forceinline__ f32x16 mfma32_bf16(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(256, 1) void router_mfma_kernel(const uint16_t *__restrict__ x,
+                                                             const uint16_t *__restrict__ wt,
+                                                             const float *__restrict__ bias,
+                                                             float *__restrict__ logits, int T,
+                                                             int d, int E, int n_n) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[RG_NS * RG_STAGE];
+    const int l = __lane_id();
+    const int wv = wave_uniform(threadIdx.x >> 6);
+    const int G = gridDim.x;
+    const int b = blockIdx.x;
+    const int t = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+    const int m0 = (t / n_n) * RG_TM, n0 = (t % n_n) * RG_TN;
+
+    // DMA sources of this lane: copy q covers 16 rows of 64 bytes; lane l
+    // fills physical chunk l % 4 of row 16 (q % 4) + l / 4 of its region
+    const char *asrc[RG_AI];
+    const char *bsrc[RG_BI];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int n = n0 + wn + b * 16 + (lane & 15);
-            if (n >= E) continue;
-            const float bb = bias ? bias[n] : 0.0f;
+    for (int i = 0; i < RG_AI; ++i) {
+        const int q = wv * RG_AI + i;
+        const int r = 16 * q + (l >> 2);
+        const int c = (l & 3) ^ ((r >> 1) & 3);
+        const int row = m0 + r < T ? m0 + r : T - 1;
+        asrc[i] = reinterpret_cast<const char *>(x + (size_t)row * d + c * 8);
+    }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = m0 + wm + a * 16 + 4 * (lane >> 4) + i;
-                if (m < T) logits[(size_t)m * E + n] = bias ? acc[a][b][i] + bb : acc[a][b][i];
-            }
+    for (int j = 0; j < RG_BI; ++j) {
+        const int q = wv * RG_BI + j;
+        const int term = q >> 2, n = 16 * (q & 3) + (l >> 2);
+        const int c = (l & 3) ^ ((n >> 1) & 3);
+        const int e = n0 + n < E ? n0 + n : E - 1;
+        bsrc[j] = reinterpret_cast<const char *>(wt + ((size_t)term * E + e) * d + c * 8);
+    }
+    auto issue = [&](int kc) {
+        uint8_t *sb = lds + (kc % RG_NS) * RG_STAGE;
+        const size_t ko = (size_t)kc * (RG_KS * 2);
+#pragma unroll
+        for (int i = 0; i < RG_AI; ++i) copy_to_lds16(asrc[i] + ko, sb + (wv * RG_AI + i) * 1024);
+#pragma unroll
+        for (int j = 0; j < RG_BI; ++j)
+            copy_to_lds16(bsrc[j] + ko, sb + RG_ABYTES + (wv * RG_BI + j) * 1024);
+    };
+
+    // operand reads: lane l reads row (l % 32) of a 32-row block, logical
+    // chunk 2 s + l / 32 for k sub-step s
+    const int wm = (wv >> 1) * 128, wn = (wv & 1) * 32;
+    int lane_off[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        lane_off[s] = (l & 31) * 64 + (((2 * s + (l >> 5)) ^ (((l & 31) >> 1) & 3)) * 16);
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+
+    struct Frags {
+        u32x4 a[4], b[3];
+    };
+    // Each read first waits for every LDS read in flight: those were issued a
+    // sub-step earlier, before the matrix ops just done, so the wait is short,
+    // and the compiler, which places one full wait before the first use of
+    // loop-carried LDS data, then has nothing left to wait for.  The
+    // scheduling fence keeps the reads ahead of the matrix ops that follow.
+    auto read = [&](Frags &f, int kc, int s) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        const uint8_t *sb = lds + (kc % RG_NS) * RG_STAGE;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            f.a[i] = *reinterpret_cast<const u32x4 *>(sb + (wm + 32 * i) * 64 + lane_off[s]);
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            f.b[j] = *reinterpret_cast<const u32x4 *>(sb + RG_ABYTES + j * (RG_TN * 64) + wn * 64 +
+                                                      lane_off[s]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto mma = [&](const Frags &f) {
+#pragma unroll
+        for (int j = 2; j >= 0; --j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = mfma32_bf16(f.a[i], f.b[j], acc[i]);
+    };
+    const int nk = d / RG_KS;
+    static_assert(RG_NS - 2 <= 3, "arrive() waits for at most three later stages");
+    // wait until stage kc has landed, when at most `ahead` later stages have
+    // been issued, then meet the other waves
+    auto arrive = [&](int kc, int ahead) {
+        const int after = (nk - 1 - kc) < ahead ? (nk - 1 - kc) : ahead;
+        if (after >= 3)
+            wait_vm<3 * RG_VM>();
+        else if (after == 2)
+            wait_vm<2 * RG_VM>();
+        else if (after == 1)
+            wait_vm<RG_VM>();
+        else
+            wait_vm<0>();
+        wg_barrier();
+    };
+
+    // Operand reads run one k sub-step ahead of the matrix ops.  The barrier
+    // for stage kc + 1 sits between the two sub-steps of stage kc; the stage
+    // refilled after it (kc + RG_NS - 1, in the ring slot of kc - 1) was last
+    // read in the previous iteration.
+    // the epilogue's kernel arguments are loaded here: a scalar load still in
+    // flight inside the loop would turn each LDS wait there into a full one
+    __asm__ volatile("" ::"s"(bias), "s"(logits));
+    for (int kc = 0; kc < RG_NS - 1 && kc < nk; ++kc) issue(kc);
+    arrive(0, RG_NS - 2);
+    Frags f0, f1;
+    read(f0, 0, 0);
+    for (int kc = 0; kc < nk - 1; ++kc) {
+        read(f1, kc, 1);
+        mma(f0);
+        arrive(kc + 1, RG_NS - 3);
+        if (kc + RG_NS - 1 < nk) issue(kc + RG_NS - 1);
+        read(f0, kc + 1, 0);
+        mma(f1);
+    }
+    read(f1, nk - 1, 1);
+    mma(f0);
+    mma(f1);
+    // D: lane l holds expert column l % 32, tokens 8 (r / 4) + 4 (l / 32) + r % 4
+    const int n = n0 + wn + (l & 31);
+    if (n >= E) return;
+    const float bb = bias ? bias[n] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+            if (m < T) logits[(size_t)m * E + n] = bias ? acc[i][r] + bb : acc[i][r];
         }
 }
+
+size_t router_gemm_ws_bytes(int d, int E) { return (size_t)3 * E * d * sizeof(uint16_t); }
 
 hipError_t launch_router_gemm(const uint16_t *x, const float *wr, const float *bias, float *logits,
-                              int T, int d, int E, hipStream_t s) {
-    dim3 grid((T + RG_M - 1) / RG_M, (E + RG_N - 1) / RG_N);
-    hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(256), 0, s, x, wr, bias, logits, T, d, E);
+                              int T, int d, int E, void *ws, hipStream_t s) {
+    uint16_t *wt = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + kWsHeader);
+    hipLaunchKernelGGL(router_split_kernel, dim3(d / 64, (E + 63) / 64), dim3(256), 0, s, wr, d, E,
+                       wt);
+    const int n_m = (T + RG_TM - 1) / RG_TM, n_n = (E + RG_TN - 1) / RG_TN;
+    hipLaunchKernelGGL(router_mfma_kernel, dim3(n_m * n_n), dim3(256), 0, s, x, wt, bias, logits, T,
+                       d, E, n_n);
     return hipGetLastError();
 }
 
