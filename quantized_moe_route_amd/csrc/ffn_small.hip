@@ -131,12 +131,19 @@ constexpr int kBatch = MOE_DECODE_BATCH;   // units prefetched per wave per batc
 // One gate/up task: 16 h columns (row tile nt) of one expert group, for all
 // of the group's rows.  The NW waves of the workgroup split K and meet in LDS
 // (red); wave 0 applies SwiGLU and writes h as fp16 hi + lo.
-template <int FMT, int MT, int IMAX, int NW>
+//
+// TOKROWS (batches of at most 16 tokens): the 16 matrix rows are the batch's
+// tokens themselves, not the group's rows, so the activation loads depend on
+// nothing and go out with the weights; a group row's token (its pair's entry
+// in sorted_pair) is needed only when wave 0 picks its row out of the sums.
+// Each output row is the same dot product either way.
+template <int FMT, int MT, int IMAX, int NW, bool TOKROWS>
 __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &up, const QMatDev &sgate,
-                                            const QMatDev &sup, const uint16_t *__restrict__ x, int k, int d,
+                                            const QMatDev &sup, const uint16_t *__restrict__ x, int T, int k, int d,
                                             int f, const int32_t *__restrict__ sorted_pair, const Group &grp,
                                             int nt, float (*red)[MT][2][IMAX][64], uint16_t *__restrict__ h_hi,
                                             uint16_t *__restrict__ h_lo) {
+    static_assert(!TOKROWS || (MT == 1 && NW > 1), "token rows: one 16-row tile, K split over waves");
     const int lane = __lane_id();
     const int wv = wave_uniform(threadIdx.x >> 6);
     const int gq = lane >> 4, rr = lane & 15;
@@ -154,11 +161,21 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
     // sorted_pair loads go out first, then the first batch of weights; only
     // the activation loads wait for the token ids.
     int tok[MT];
+    int otok[IMAX];   // TOKROWS: token of output row 4 gq + i
+    if constexpr (TOKROWS) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        int r = mt * 16 + rr;
-        r = r < nrows ? r : nrows - 1;
-        tok[mt] = shared ? r : sorted_pair[grp.row0 + r];
+        for (int i = 0; i < IMAX; ++i) {
+            int r = 4 * gq + i;
+            r = r < nrows ? r : nrows - 1;
+            otok[i] = shared ? r : sorted_pair[grp.row0 + r];
+        }
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            int r = mt * 16 + rr;
+            r = r < nrows ? r : nrows - 1;
+            tok[mt] = shared ? r : sorted_pair[grp.row0 + r];
+        }
     }
     f32x4 ag[MT], au[MT];
 #pragma unroll
@@ -175,8 +192,12 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
             if (u < KC) gateup_load_w(U[b], Wg, Wu, ubase + u, lane, rr);
         }
         __asm__ volatile("" ::: "memory");
+        if constexpr (TOKROWS) {
+            xrow[0] = x + (size_t)(rr < T ? rr : T - 1) * d;
+        } else {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) xrow[mt] = x + (size_t)(shared ? tok[mt] : tok[mt] / k) * d;
+            for (int mt = 0; mt < MT; ++mt) xrow[mt] = x + (size_t)(shared ? tok[mt] : tok[mt] / k) * d;
+        }
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
             const int u = u0 + NW * b;
@@ -191,6 +212,37 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
                 gateup_block<FMT, MT, IMAX, 3>(U[b], ag, au);
             }
         }
+    }
+    if constexpr (TOKROWS) {
+#pragma unroll
+        for (int i = 0; i < IMAX; ++i) {
+            red[wv][0][0][i][lane] = ag[0][i];
+            red[wv][0][1][i][lane] = au[0][i];
+        }
+        __syncthreads();
+        if (wv != 0) return;
+        // output row r = 4 gq + i takes the sums of its token's matrix row
+        const int n = nt * 16 + rr;
+#pragma unroll
+        for (int i = 0; i < IMAX; ++i) {
+            const int r = 4 * gq + i;
+            if (r >= nrows) continue;
+            const int t = shared ? otok[i] : otok[i] / k;
+            const int sl = (t >> 2) * 16 + rr, si = t & 3;
+            float gs = red[0][0][0][si][sl], us = red[0][0][1][si][sl];
+#pragma unroll
+            for (int w2 = 1; w2 < NW; ++w2) {
+                gs += red[w2][0][0][si][sl];
+                us += red[w2][0][1][si][sl];
+            }
+            const float h = swiglu(gs, us);
+            const _Float16 hh = static_cast<_Float16>(h);
+            const float rem = h - static_cast<float>(hh);
+            const size_t off = (size_t)(grp.hrow0 + r) * f + n;
+            h_hi[off] = __builtin_bit_cast(uint16_t, hh);
+            h_lo[off] = f32_to_f16_bits(rem);
+        }
+        return;
     }
     if constexpr (NW > 1) {
 #pragma unroll
@@ -395,8 +447,8 @@ __global__ __launch_bounds__(64 * NW) void gateup_small_kernel(
     __shared__ float red[NW][MT][2][IMAX][64];
     Group grp;
     if (!find_group(offsets, E, T, T * k, blockIdx.y, grp)) return;
-    gateup_task<FMT, MT, IMAX, NW>(gate, up, sgate, sup, x, k, d, f, sorted_pair, grp, blockIdx.x, red,
-                                          h_hi, h_lo);
+    gateup_task<FMT, MT, IMAX, NW, MT == 1>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp,
+                                            blockIdx.x, red, h_hi, h_lo);
 }
 
 // grid: (d_model/16 row tiles, group slots); NW waves split K = d_ff.
