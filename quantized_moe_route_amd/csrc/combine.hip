@@ -5,10 +5,14 @@
 // results of all experts, then the next layer starts.
 //   out[t] = y_shared[t] + sum_j w[t][j] * y_pairs[pair_pos[t*k+j]]
 // A pure streaming gather: one thread per 4 output columns, fp32, shared term
-// first then j = 0..k-1 (fixed order, deterministic).
+// first then j = 0..k-1 (fixed order, deterministic).  The pair positions and
+// weights of a batch of 8 j are loaded first, then the batch's 8 rows all at
+// once, so each thread keeps 8 row loads in flight instead of one.
 #include "common.h"
 
 namespace moe {
+
+constexpr int kCombineBatch = 8;
 
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y_pairs,
                                                       const float *__restrict__ y_shared,
@@ -18,15 +22,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     const int t = blockIdx.y;
     const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= d) return;
+    const int32_t *pp = pair_pos + (size_t)t * k;
+    const float *ww = w + (size_t)t * k;
     float4 acc = *reinterpret_cast<const float4 *>(y_shared + (size_t)t * d + c);
-    for (int j = 0; j < k; ++j) {
-        const int p = pair_pos[(size_t)t * k + j];
-        const float wj = w[(size_t)t * k + j];
-        const float4 v = *reinterpret_cast<const float4 *>(y_pairs + (size_t)p * d + c);
-        acc.x += wj * v.x;
-        acc.y += wj * v.y;
-        acc.z += wj * v.z;
-        acc.w += wj * v.w;
+    for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+        int p[kCombineBatch];
+        float wj[kCombineBatch];
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) {
+            const int j = j0 + i < k ? j0 + i : k - 1;   // clamped: loaded, not used
+            p[i] = pp[j];
+            wj[i] = ww[j];
+        }
+        float4 v[kCombineBatch];
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i)
+            v[i] = *reinterpret_cast<const float4 *>(y_pairs + (size_t)p[i] * d + c);
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) {
+            if (j0 + i < k) {
+                acc.x += wj[i] * v[i].x;
+                acc.y += wj[i] * v[i].y;
+                acc.z += wj[i] * v[i].z;
+                acc.w += wj[i] * v[i].w;
+            }
+        }
     }
     *reinterpret_cast<float4 *>(out + (size_t)t * d + c) = acc;
 }
