@@ -159,6 +159,30 @@ def test_route_small_path_shapes(q, T, E, k, d):
         assert np.max(np.abs(wt.cpu().numpy() - w_ref)) <= 1e-6
 
 
+@pytest.mark.parametrize("T,E,k,d", [(300, 300, 40, 384), (20, 1000, 70, 256), (9, 64, 8, 128),
+                                     (513, 17, 3, 2048)])
+def test_route_gemm_path_shapes(q, T, E, k, d):
+    """Router matrix-core path (T > 8) at ragged shapes: token and expert tiles
+    with tails, E not a multiple of 64, and k > 64 (top-k through LDS)."""
+    rng = np.random.default_rng(T * E + k + d)
+    x = synth._f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    wr = (rng.standard_normal((d, E)) / np.sqrt(d)).astype(np.float32)
+    bias = rng.standard_normal(E).astype(np.float32)
+    ws_bytes = q.moe_workspace_size(d, 128, E, T, k)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    lg = torch.empty(T, E, device="cuda")
+    ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    wt = torch.empty(T, k, device="cuda")
+    c = lambda a: torch.from_numpy(a).cuda()
+    q.moe_route(c(x.view(np.int16)), c(wr), c(bias), lg, T, d, E, k, ids, wt, ws, ws_bytes)
+    torch.cuda.synchronize()
+    lg_h = lg.cpu().numpy()
+    assert _rel_err(lg_h, oracle.router_logits(x, wr, bias)) <= 1e-5
+    ids_ref, w_ref = oracle.topk_softmax(lg_h, k)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.max(np.abs(wt.cpu().numpy() - w_ref)) <= 1e-6
+
+
 @pytest.mark.parametrize("T,E,k,skew", [
     (1, 512, 10, 0), (4, 512, 10, 1), (100, 64, 8, 0), (512, 512, 8, 0), (8192, 512, 10, 0),
     (8192, 512, 10, 2), (300, 1024, 16, 0), (65, 16, 16, 0), (1000, 1, 1, 0),
