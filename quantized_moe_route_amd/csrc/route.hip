@@ -281,78 +281,19 @@ __device__ void wave_topk_ord(const float *__restrict__ lg, int E, int k, int32_
     }
 }
 
-// -------------------------------------------------- top-k by ranking (block)
-// For k <= 32: every logit becomes a 64-bit key that orders exactly like
-// (larger value, then lower index): the float bits mapped to an unsigned
-// order (with -0.0 read as +0.0) in the high word, the complemented index in
-// the low word.  Keys are distinct, so ranks are a permutation.
-//   phase 1: each 64-expert chunk ranks its members against the chunk; the
-//            ones ranked < k are the chunk's candidates (slot chunk*k + rank);
-//   phase 2: each candidate's rank among its token's candidates is its
-//            position in the output.
-// No serial rounds: both phases are independent compares read from LDS.
-constexpr int kRankMaxK = 32;
+constexpr int kWaveTopkMaxK = 64;   // register top-k up to this k
 
-__device__ __forceinline__ unsigned long long topk_key(float v, int e) {
-    uint32_t f = __float_as_uint(v);
-    if (f == 0x80000000u) f = 0u;                        // -0.0 ties with +0.0
-    const uint32_t ord = (f & 0x80000000u) ? ~f : (f | 0x80000000u);
-    return ((unsigned long long)ord << 32) | (uint32_t)(~(uint32_t)e);
-}
-
-__device__ __forceinline__ float key_value(unsigned long long key) {
-    const uint32_t ord = (uint32_t)(key >> 32);
-    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
-}
-
-// keys [T][E] and cand [T][nch*k] in LDS; all threads of the block call this.
-template <int NT>
-__device__ void block_topk_rank(const unsigned long long *keys, unsigned long long *cand, int T, int E,
-                                int k, int32_t *__restrict__ ids, float *__restrict__ w,
-                                unsigned long long *sel /* LDS [T][k] */) {
-    const int tid = threadIdx.x;
-    const int nch = (E + 63) / 64;
-    const int nslot = nch * k;
-    // phase 1: task = (token, chunk, member)
-    for (int task = tid; task < T * nch * 64; task += NT) {
-        const int t = task / (nch * 64);
-        const int rem = task - t * nch * 64;
-        const int c = rem >> 6, m = rem & 63;
-        const int e = c * 64 + m;
-        const int clen = (E - c * 64) < 64 ? (E - c * 64) : 64;
-        if (m < clen) {
-            const unsigned long long my = keys[t * E + e];
-            const unsigned long long *ck = keys + t * E + c * 64;
-            int rank = 0;
-            for (int j = 0; j < clen; ++j) rank += ck[j] > my ? 1 : 0;
-            if (rank < k) cand[t * nslot + c * k + rank] = my;
-        }
-        if (m < k && m >= clen) cand[t * nslot + c * k + m] = 0ull;   // short last chunk
-    }
-    __syncthreads();
-    // phase 2: task = (token, slot)
-    for (int task = tid; task < T * nslot; task += NT) {
-        const int t = task / nslot;
-        const unsigned long long my = cand[task];
-        if (my == 0ull) continue;
-        const unsigned long long *tc = cand + t * nslot;
-        int rank = 0;
-        for (int j = 0; j < nslot; ++j) rank += tc[j] > my ? 1 : 0;
-        if (rank < k) sel[t * k + rank] = my;
-    }
-    __syncthreads();
-    // weights: softmax over the selected logits, one wave per token
-    const int wv = tid >> 6, l = __lane_id();
-    for (int t = wv; t < T; t += NT / 64) {
-        const float l0 = key_value(sel[t * k]);
-        float ev = 0.0f;
-        if (l < k) ev = expf(key_value(sel[t * k + l]) - l0);
-        const float inv = 1.0f / wave_sum(ev);
-        if (l < k) {
-            w[(size_t)t * k + l] = ev * inv;
-            ids[(size_t)t * k + l] = (int)~(uint32_t)sel[t * k + l];
-        }
-    }
+__device__ __forceinline__ void wave_topk_ord_any(const float *lg, int E, int k, int32_t *ids, float *w) {
+    if (E <= 64)
+        wave_topk_ord<1>(lg, E, k, ids, w);
+    else if (E <= 128)
+        wave_topk_ord<2>(lg, E, k, ids, w);
+    else if (E <= 256)
+        wave_topk_ord<4>(lg, E, k, ids, w);
+    else if (E <= 512)
+        wave_topk_ord<8>(lg, E, k, ids, w);
+    else
+        wave_topk_ord<16>(lg, E, k, ids, w);
 }
 
 // ------------------------------------------------------- small T: one launch
@@ -368,19 +309,15 @@ __global__ __launch_bounds__(512) void route_small_kernel(
     float *__restrict__ logits, int T, int d, int E, int k, int32_t *__restrict__ ids,
     float *__restrict__ w, int32_t *__restrict__ counters, float *__restrict__ partial) {
     __shared__ float red[8][kMaxSmallT][64];
-    // one LDS pool: ranking top-k (keys, candidates, selection) or, for k > 32,
-    // the serial top-k's per-wave scratch
-    constexpr int kKeyBytes = kMaxSmallT * 1024 * 8, kCandBytes = kMaxSmallT * 16 * kRankMaxK * 8;
-    constexpr int kSelBytes = kMaxSmallT * kRankMaxK * 8;
-    constexpr int kPoolBytes = kKeyBytes + kCandBytes + kSelBytes;
-    static_assert(kPoolBytes >= 2 * 8 * 1024 * 4, "pool too small for the serial top-k");
+    // one LDS pool: the logits [T][E] for the register top-k (k <= 64), or
+    // the serial top-k's per-wave scratch (k > 64)
+    constexpr int kPoolBytes = 2 * 8 * 1024 * 4;
+    static_assert(kMaxSmallT * 1024 * 4 <= kPoolBytes, "pool too small for the logits");
     __shared__ __attribute__((aligned(16))) unsigned char pool[kPoolBytes];
     __shared__ int last_flag;
-    unsigned long long *keys = reinterpret_cast<unsigned long long *>(pool);
-    unsigned long long *cand = reinterpret_cast<unsigned long long *>(pool + kKeyBytes);
-    unsigned long long *selk = reinterpret_cast<unsigned long long *>(pool + kKeyBytes + kCandBytes);
-    float *sel = reinterpret_cast<float *>(pool);                      // [8][1024], k > 32 only
-    int *seli = reinterpret_cast<int *>(pool + 8 * 1024 * 4);           // [8][1024], k > 32 only
+    float *lgs = reinterpret_cast<float *>(pool);                       // [T][E], k <= 64
+    float *sel = reinterpret_cast<float *>(pool);                       // [8][1024], k > 64
+    int *seli = reinterpret_cast<int *>(pool + 8 * 1024 * 4);           // [8][1024], k > 64
     const int cs = blockIdx.x;
     const int kc = blockIdx.y;
     const int n_kc = gridDim.y;
@@ -427,27 +364,47 @@ __global__ __launch_bounds__(512) void route_small_kernel(
     publish_then_count(&counters[kCntRouteAll], gridDim.x * gridDim.y, last_flag);
     if (!last_flag) return;
     if (tid == 0) store_dev_int(&counters[kCntRouteAll], 0);
-    // last workgroup: sum the partials of every (token, expert) in chunk order
-    for (int idx = tid; idx < T * E; idx += 512) {
-        const int t = idx / E, ee = idx - t * E;
-        float s_ = 0.0f;
+    // last workgroup: sum the partials of every (token, expert) in chunk
+    // order.  A thread takes up to four (token, expert) entries per pass, with
+    // all their partial loads in flight together.
+    for (int idx0 = tid; idx0 < T * E; idx0 += 4 * 512) {
+        const int left = (T * E - (idx0 - tid) + 511) / 512;   // uniform over the block
+        const int nu = left < 4 ? left : 4;
+        float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int q0 = 0; q0 < n_kc; q0 += 16) {
-            float v[16];
+            float v[4][16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int qc = q0 + i < n_kc ? q0 + i : n_kc - 1;
-                v[i] = load_dev(&partial[((size_t)qc * T + t) * E + ee]);
+            for (int u = 0; u < 4; ++u) {
+                if (u >= nu) break;
+                const int idx = idx0 + u * 512 < T * E ? idx0 + u * 512 : idx0;
+                const int t = idx / E, ee = idx - t * E;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int qc = q0 + i < n_kc ? q0 + i : n_kc - 1;
+                    v[u][i] = load_dev(&partial[((size_t)qc * T + t) * E + ee]);
+                }
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s_ += q0 + i < n_kc ? v[i] : 0.0f;
+            for (int u = 0; u < 4; ++u) {
+                if (u >= nu) break;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sum[u] += q0 + i < n_kc ? v[u][i] : 0.0f;
+            }
         }
-        if (bias) s_ = s_ + bias[ee];
-        logits[(size_t)t * E + ee] = s_;
-        keys[t * E + ee] = topk_key(s_, ee);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int idx = idx0 + u * 512;
+            if (u >= nu || idx >= T * E) continue;
+            const int ee = idx % E;
+            const float s_ = bias ? sum[u] + bias[ee] : sum[u];
+            logits[idx] = s_;
+            if (k <= kWaveTopkMaxK) lgs[idx] = s_;
+        }
     }
     __syncthreads();
-    if (k <= kRankMaxK) {
-        block_topk_rank<512>(keys, cand, T, E, k, ids, w, selk);
+    // one wave per token
+    if (k <= kWaveTopkMaxK) {
+        for (int t = wv; t < T; t += 8) wave_topk_ord_any(lgs + t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
         return;
     }
     // large k: serial selection per token from the logits just written
@@ -475,27 +432,13 @@ hipError_t launch_route_small(const uint16_t *x, const float *wr, const float *b
 // ------------------------------------------------------------ top-k kernel
 // Logits given: one wave per token, four tokens per workgroup.  k <= 64 keeps
 // every selection in registers; larger k selects serially through LDS.
-constexpr int kWaveTopkMaxK = 64;
-
 __global__ __launch_bounds__(256) void topk_wave_kernel(const float *__restrict__ logits, int T,
                                                         int E, int k, int32_t *__restrict__ ids,
                                                         float *__restrict__ w) {
     const int wv = wave_uniform(threadIdx.x >> 6);
     const int t = blockIdx.x * 4 + wv;
     if (t >= T) return;
-    const float *lg = logits + (size_t)t * E;
-    int32_t *it = ids + (size_t)t * k;
-    float *wt = w + (size_t)t * k;
-    if (E <= 64)
-        wave_topk_ord<1>(lg, E, k, it, wt);
-    else if (E <= 128)
-        wave_topk_ord<2>(lg, E, k, it, wt);
-    else if (E <= 256)
-        wave_topk_ord<4>(lg, E, k, it, wt);
-    else if (E <= 512)
-        wave_topk_ord<8>(lg, E, k, it, wt);
-    else
-        wave_topk_ord<16>(lg, E, k, it, wt);
+    wave_topk_ord_any(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
 }
 
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
