@@ -67,6 +67,7 @@ struct PfSched {
     int32_t ticket[2][PF_NXCD];      // per GEMM launch, per XCD queue
 };
 static_assert(sizeof(PfSched) <= 256, "PfSched must fit its 256-byte slot");
+static_assert(sizeof(PfItem) == 16, "items are read as one 16-byte vector");
 
 // ---------------------------------------------------------------- prepass
 // One block of 1024 threads.  Group 0 is the shared expert (T rows), group
@@ -367,7 +368,8 @@ __device__ __forceinline__ float swiglu_fast(float g, float u) {
 // MT: 32-row m-tiles that hold rows of the item (1..4).
 template <int FMT, int MODE, bool SH, int MT, int NTW>
 __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item, int tile,
-                                        uint8_t *As, int *s_row) {
+                                        uint8_t *As, int *s_row, const PfItem *pf_items, int pf_t, int pf_n,
+                                        PfItem *pf_dst) {
     using G = PfGeom<NTW>;
     const int tid = threadIdx.x, l = __lane_id();
     const int wv = wave_uniform(tid >> 6);
@@ -389,7 +391,9 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
             src = item.hrow0 + r;
         s_row[tid] = src;
     }
-    __syncthreads();
+    // LDS only: the previous unit's output stores may still be in flight
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    wg_barrier();
 
     // A copy slots of this lane: instruction i covers tile rows 4 (NI wv + i)
     // .. +4; lane l takes row R = 4 (NI wv + i) + l / 16 and stores physical
@@ -571,6 +575,16 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
     // outside the branch so the compiler knows it and does not make each LDS
     // read of the epilogue wait for the stores before it
     wait_vm<0>();
+    // the next unit's item (thread 0), loaded while the epilogue runs
+    // (thread 0: pf_t is the next ticket of this queue, pf_items its items,
+    // pf_n its unit count)
+    u32x4 pfv = {0u, 0u, 0u, 0u};
+    const int pt = pf_t;
+    const bool pf_on = tid == 0 && pt < pf_n;
+    if (pf_on) {
+        typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+        pfv = *(global_u32x4 *)(pf_items + pt / a.nt);
+    }
     // epilogue, one m-tile at a time through a wave-private LDS region (the A
     // stages are free now): accumulators out as written by the matrix core
     // (D row 8 (r / 4) + 4 h + r % 4, column l % 32), then read back along
@@ -652,7 +666,10 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
             __builtin_amdgcn_s_waitcnt(0xC07F);
         }
     }
-    __syncthreads();
+    if (pf_on) *reinterpret_cast<u32x4 *>(pf_dst) = pfv;
+    // LDS only: the output stores need not land before the next unit
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    wg_barrier();
 }
 
 // Persistent grouped GEMM: workgroups take (item, column tile) units by
@@ -662,17 +679,26 @@ __global__ __launch_bounds__(256, 1) void pf_gemm_kernel(PfGemmArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t As[PF_NSTAGE * PF_STAGE];
     __shared__ int s_row[PF_MT];
     __shared__ int s_ticket;
+    __shared__ int s_xq[PF_NXCD + 1];   // queue bounds (fixed for the launch)
+    __shared__ __attribute__((aligned(16))) PfItem s_next;   // item of ticket s_next_t in queue s_next_x
+    __shared__ int s_next_t, s_next_x;
     unsigned xcd;
     __asm__ volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcd));
     xcd &= PF_NXCD - 1;
-    // the ticket for the next unit is taken at the start of the current one
-    if (threadIdx.x == 0) s_ticket = atomicAdd(&a.sched->ticket[a.launch][xcd], 1);
+    // the ticket for the next unit is taken at the start of the current one,
+    // and its item is loaded during the current unit's epilogue
+    if (threadIdx.x == 0) {
+        s_ticket = atomicAdd(&a.sched->ticket[a.launch][xcd], 1);
+        s_next_t = -1;
+        s_next_x = -1;
+    }
+    if (threadIdx.x <= PF_NXCD) s_xq[threadIdx.x] = a.sched->xq[threadIdx.x];
     __syncthreads();
     for (int q = 0; q < PF_NXCD;) {
         const int x = (int)((xcd + q) & (PF_NXCD - 1));
         const int t = wave_uniform(s_ticket);
-        const int i0 = a.sched->xq[x];
-        const int n_units = (a.sched->xq[x + 1] - i0) * a.nt;
+        const int i0 = s_xq[x];
+        const int n_units = (s_xq[x + 1] - i0) * a.nt;
         if (t >= n_units) {
             ++q;
             __syncthreads();
@@ -683,23 +709,34 @@ __global__ __launch_bounds__(256, 1) void pf_gemm_kernel(PfGemmArgs a) {
         }
         int nxt = 0;
         if (threadIdx.x == 0) nxt = atomicAdd(&a.sched->ticket[a.launch][x], 1);
-        const PfItem item = a.items[i0 + t / a.nt];
+        const bool have = s_next_t == t && s_next_x == x;   // uniform
+        typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+        u32x4 iv;
+        if (have)
+            iv = *reinterpret_cast<const u32x4 *>(&s_next);
+        else
+            iv = *(global_u32x4 *)(a.items + i0 + t / a.nt);
+        const PfItem item{(int32_t)iv.x, (int32_t)iv.y, (int32_t)iv.z, (int32_t)iv.w};
         const int tile = t % a.nt;
         constexpr int MTX = PF_MT / 32;
         if (item.expert < 0) {
-            pf_unit<FMT, MODE, true, MTX, NTW>(a, item, tile, As, s_row);
+            pf_unit<FMT, MODE, true, MTX, NTW>(a, item, tile, As, s_row, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next);
         } else {
             switch ((item.nrows + 31) >> 5) {
-                case 1: pf_unit<FMT, MODE, false, 1, NTW>(a, item, tile, As, s_row); break;
-                case 2: pf_unit<FMT, MODE, false, 2, NTW>(a, item, tile, As, s_row); break;
-                case 3: pf_unit<FMT, MODE, false, 3, NTW>(a, item, tile, As, s_row); break;
-                case 4: pf_unit<FMT, MODE, false, 4 < MTX ? 4 : MTX, NTW>(a, item, tile, As, s_row); break;
-                case 5: pf_unit<FMT, MODE, false, 5 < MTX ? 5 : MTX, NTW>(a, item, tile, As, s_row); break;
-                default: pf_unit<FMT, MODE, false, MTX, NTW>(a, item, tile, As, s_row); break;
+                case 1: pf_unit<FMT, MODE, false, 1, NTW>(a, item, tile, As, s_row, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                case 2: pf_unit<FMT, MODE, false, 2, NTW>(a, item, tile, As, s_row, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                case 3: pf_unit<FMT, MODE, false, 3, NTW>(a, item, tile, As, s_row, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                case 4: pf_unit<FMT, MODE, false, 4 < MTX ? 4 : MTX, NTW>(a, item, tile, As, s_row, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                case 5: pf_unit<FMT, MODE, false, 5 < MTX ? 5 : MTX, NTW>(a, item, tile, As, s_row, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                default: pf_unit<FMT, MODE, false, MTX, NTW>(a, item, tile, As, s_row, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
             }
         }
         // pf_unit ended with a barrier: every thread has read s_ticket
-        if (threadIdx.x == 0) s_ticket = nxt;
+        if (threadIdx.x == 0) {
+            s_ticket = nxt;
+            s_next_t = nxt < n_units ? nxt : -1;
+            s_next_x = x;
+        }
         __syncthreads();
     }
 }
