@@ -340,6 +340,7 @@ struct PfGeom {
     // epilogue staging per wave (in the A stages); pitches put rows 4 apart
     // (the two half-waves) in different banks
     static constexpr int EP0_PITCH = HCOLS + 8;     // [gate | up][32][EP0_PITCH] floats
+    static constexpr int EP0H_PITCH = HCOLS + 8;    // gate/up: [h | h_lo][32][EP0H_PITCH] halves
     static constexpr int EP1_PITCH = OCOLS + 8;     // [32][EP1_PITCH] floats
     static constexpr int EP_WAVE = (2 * 32 * EP0_PITCH > 32 * EP1_PITCH ? 2 * 32 * EP0_PITCH : 32 * EP1_PITCH) * 4;
     static_assert(4 * EP_WAVE <= PF_NSTAGE * PF_STAGE, "epilogue staging must fit in the A stages");
@@ -594,51 +595,38 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             if constexpr (MODE == 0) {
-                // [gate | up][32 rows][EP0_PITCH]: the wave's HCOLS columns
+                // SwiGLU on the accumulators (a column's gate and up sums sit
+                // in the same lane and register), h as fp16 (and its residual
+                // for the shared expert) into [32 rows][EP0H_PITCH] halves,
+                // read back along rows for 16-byte stores
+                uint16_t *eh = reinterpret_cast<uint16_t *>(ep);
+                uint16_t *el = eh + 32 * G::EP0H_PITCH;
 #pragma unroll
-                for (int n = 0; n < NTW; ++n)
+                for (int n = 0; n < NTW / 2; ++n)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int row = 8 * (r >> 2) + 4 * h + (r & 3);
-                        ep[((n / (NTW / 2)) * 32 + row) * G::EP0_PITCH + (n % (NTW / 2)) * 32 + (l & 31)] =
-                            acc[m][n][r];
+                        const float hv = swiglu_fast(acc[m][n][r], acc[m][n + NTW / 2][r]);
+                        const _Float16 hh = static_cast<_Float16>(hv);
+                        eh[row * G::EP0H_PITCH + n * 32 + (l & 31)] = __builtin_bit_cast(uint16_t, hh);
+                        if constexpr (SH)
+                            el[row * G::EP0H_PITCH + n * 32 + (l & 31)] =
+                                __builtin_bit_cast(uint16_t, static_cast<_Float16>(hv - static_cast<float>(hh)));
                     }
                 __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
                 constexpr int LPR = G::HCOLS / 8;    // lanes per row (8 columns each)
                 const int c0 = tile * 4 * G::HCOLS + wv * G::HCOLS + (l % LPR) * 8;
-#pragma unroll 1
+#pragma unroll
                 for (int it = 0; it < 32 * LPR / 64; ++it) {
                     const int row = it * (64 / LPR) + l / LPR;
                     const int grow = m * 32 + row;
-                    const float *gp = ep + row * G::EP0_PITCH + (l % LPR) * 8;
-                    const float *up = gp + 32 * G::EP0_PITCH;
-                    const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp);
-                    const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gp + 4);
-                    const f32x4 u0 = *reinterpret_cast<const f32x4 *>(up);
-                    const f32x4 u1 = *reinterpret_cast<const f32x4 *>(up + 4);
-                    float hv[8] = {swiglu_fast(g0.x, u0.x), swiglu_fast(g0.y, u0.y), swiglu_fast(g0.z, u0.z),
-                                   swiglu_fast(g0.w, u0.w), swiglu_fast(g1.x, u1.x), swiglu_fast(g1.y, u1.y),
-                                   swiglu_fast(g1.z, u1.z), swiglu_fast(g1.w, u1.w)};
-                    uint32_t hw[4], lw[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const _Float16 a0 = static_cast<_Float16>(hv[2 * q]);
-                        const _Float16 a1 = static_cast<_Float16>(hv[2 * q + 1]);
-                        hw[q] = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
-                        if constexpr (SH) {
-                            const _Float16 b0 = static_cast<_Float16>(hv[2 * q] - static_cast<float>(a0));
-                            const _Float16 b1 = static_cast<_Float16>(hv[2 * q + 1] - static_cast<float>(a1));
-                            lw[q] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-                        }
-                    }
+                    const u32x4 hw = *reinterpret_cast<const u32x4 *>(eh + row * G::EP0H_PITCH + (l % LPR) * 8);
+                    u32x4 lw;
+                    if constexpr (SH) lw = *reinterpret_cast<const u32x4 *>(el + row * G::EP0H_PITCH + (l % LPR) * 8);
                     if (grow < nrows) {
-                        *reinterpret_cast<u32x4 *>(a.h_out + (size_t)(item.hrow0 + grow) * a.f + c0) =
-                            u32x4{hw[0], hw[1], hw[2], hw[3]};
+                        *reinterpret_cast<u32x4 *>(a.h_out + (size_t)(item.hrow0 + grow) * a.f + c0) = hw;
                         if constexpr (SH)
-                            *reinterpret_cast<u32x4 *>(a.h_lo_out + (size_t)(item.row0 + grow) * a.f + c0) =
-                                u32x4{lw[0], lw[1], lw[2], lw[3]};
+                            *reinterpret_cast<u32x4 *>(a.h_lo_out + (size_t)(item.row0 + grow) * a.f + c0) = lw;
                     }
                 }
             } else {
