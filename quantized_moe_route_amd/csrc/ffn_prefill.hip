@@ -72,7 +72,8 @@ static_assert(sizeof(PfItem) == 16, "items are read as one 16-byte vector");
 // ---------------------------------------------------------------- prepass
 // One block of 1024 threads.  Group 0 is the shared expert (T rows), group
 // 1 + e the routed expert e.  Sort key: (work desc, group asc), work = rows
-// (x2 for the shared expert); bitonic sort over PF_SORT slots in LDS.
+// (x2 for the shared expert); bitonic sort in LDS over the next power of two
+// >= E + 1 slots (at most PF_SORT).
 __global__ __launch_bounds__(1024) void pf_build_items_kernel(const int32_t *__restrict__ offsets,
                                                               int E, int T, int P,
                                                               PfItem *__restrict__ items,
@@ -80,30 +81,46 @@ __global__ __launch_bounds__(1024) void pf_build_items_kernel(const int32_t *__r
     __shared__ unsigned long long key[PF_SORT];
     __shared__ int start[PF_SORT / PF_NXCD * PF_NXCD];
     __shared__ int xcount[PF_NXCD];
+    __shared__ int g_rows[PF_SORT], g_row0[PF_SORT];   // per group, read from offsets once
     const int tid = threadIdx.x, lane = __lane_id(), wv = tid >> 6;
     const int G = E + 1;
+    int NS = 128;                 // sort width: a power of two >= G (at least 128)
+    while (NS < G) NS <<= 1;
     for (int g = tid; g < PF_SORT; g += 1024) {
         unsigned long long kk = 0;
+        int rows = 0, r0 = 0;
         if (g < G) {
-            const long rows = g == 0 ? T : offsets[g] - offsets[g - 1];
+            r0 = g == 0 ? 0 : offsets[g - 1];
+            rows = g == 0 ? T : offsets[g] - r0;
             const unsigned long long work = g == 0 ? 2ull * rows : (unsigned long long)rows;
             if (rows > 0) kk = (work << 11) | (unsigned long long)(2047 - g);
         }
         key[g] = kk;
+        g_rows[g] = rows;
+        g_row0[g] = r0;
     }
     __syncthreads();
-    // bitonic sort, descending
-    for (int size = 2; size <= PF_SORT; size <<= 1) {
+    // bitonic sort, descending.  With stride <= 64 the pairs of wave w lie in
+    // its own keys [128 w, 128 w + 128); between two such stages a wave only
+    // orders its own LDS accesses, and a block barrier is needed only where
+    // this stage or the next crosses waves (and after the last).
+    for (int size = 2; size <= NS; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const int i = 2 * tid - (tid & (stride - 1));   // lower index of this thread's pair
-            const int j = i + stride;
-            const bool desc = ((i & size) == 0);
-            const unsigned long long a = key[i], b = key[j];
-            if ((a < b) == desc) {
-                key[i] = b;
-                key[j] = a;
+            if (tid < NS / 2) {
+                const int i = 2 * tid - (tid & (stride - 1));   // lower index of this thread's pair
+                const int j = i + stride;
+                const bool desc = ((i & size) == 0);
+                const unsigned long long a = key[i], b = key[j];
+                if ((a < b) == desc) {
+                    key[i] = b;
+                    key[j] = a;
+                }
             }
-            __syncthreads();
+            const bool cross = stride > 64 || (stride == 1 && (size > 64 || size == NS));
+            if (cross)
+                __syncthreads();
+            else
+                __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
     }
     // rank r -> XCD r % 8, position r / 8; per-XCD exclusive scan of chunk counts
@@ -111,16 +128,15 @@ __global__ __launch_bounds__(1024) void pf_build_items_kernel(const int32_t *__r
         const unsigned long long kk = key[r];
         if (kk == 0) return 0;
         const int g = 2047 - (int)(kk & 2047);
-        const int rows = g == 0 ? T : offsets[g] - offsets[g - 1];
-        return (rows + PF_MT - 1) / PF_MT;
+        return (g_rows[g] + PF_MT - 1) / PF_MT;
     };
     if (wv < PF_NXCD) {
         int carry = 0;
-        for (int c = 0; c * 64 * PF_NXCD < PF_SORT; ++c) {
+        for (int c = 0; c * 64 * PF_NXCD < NS; ++c) {
             const int r = (c * 64 + lane) * PF_NXCD + wv;
-            const int v = r < PF_SORT ? nch_of(r) : 0;
+            const int v = r < NS ? nch_of(r) : 0;
             const int incl = wave_incl_scan(v) + carry;
-            if (r < PF_SORT) start[r] = incl - v;
+            if (r < NS) start[r] = incl - v;
             carry = __shfl(incl, 63);
         }
         if (lane == 0) xcount[wv] = carry;
@@ -145,12 +161,12 @@ __global__ __launch_bounds__(1024) void pf_build_items_kernel(const int32_t *__r
             acc += xcount[x];
         }
     }
-    for (int r = tid; r < PF_SORT; r += 1024) {
+    for (int r = tid; r < NS; r += 1024) {
         const unsigned long long kk = key[r];
         if (kk == 0) continue;
         const int g = 2047 - (int)(kk & 2047);
-        const int rows = g == 0 ? T : offsets[g] - offsets[g - 1];
-        const int r0 = g == 0 ? 0 : offsets[g - 1];
+        const int rows = g_rows[g];
+        const int r0 = g_row0[g];
         const int nch = (rows + PF_MT - 1) / PF_MT;
         const int base = xbase[r % PF_NXCD] + start[r];
         for (int c = 0; c < nch; ++c) {
