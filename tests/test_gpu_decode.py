@@ -301,11 +301,14 @@ def test_t_zero_is_noop(q):
     assert torch.all(ids == -7) and torch.all(wt == -7.0) and torch.all(lg == 3.0)
 
 
-def test_back_to_back_calls_share_workspace(q):
+@pytest.mark.parametrize("T,fmt", [(4, 2), (1, 1), (16, 2)])
+def test_back_to_back_calls_share_workspace(q, T, fmt):
     """Consecutive layers on one workspace: the in-kernel ticket and per-group
-    counters must be back at zero after every call."""
+    counters must be back at zero after every call (the workspace's 4 KiB
+    counter header reads all zero), and every layer matches the oracle."""
     from quantized_moe_route_amd.layer import alloc_buffers, run_layer
-    w = synth.custom(256, 128, 64, 8, 4, fmt=2, zipf_s=1.3, wid=310)
+    w = synth.custom(256, 128, 64, 8, T, fmt=fmt, zipf_s=1.3, wid=310 + T)
+    print(f"shape {w}", flush=True)
     L = synth.gen_layer(w)
     dl = _upload(L, w)
     b = alloc_buffers(dl, w.T, w.k)
@@ -313,6 +316,7 @@ def test_back_to_back_calls_share_workspace(q):
         x = synth.gen_x(w, stream=step)
         run_layer(dl, _x_dev(x), b)
         torch.cuda.synchronize()
+        assert int(torch.count_nonzero(b.ws[:4096])) == 0, step
         _check_layer(q, w, L, x, b)
 
 
