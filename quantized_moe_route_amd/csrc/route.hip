@@ -195,14 +195,16 @@ __device__ __forceinline__ uint32_t ord_key(float v) {
 __device__ __forceinline__ float ord_value(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
+// The lanes a row mask leaves out read the operation's identity (0 for max,
+// all ones for min), so the move folds into one max/min with a DPP operand.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
-    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
     return o > v ? o : v;
 }
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ uint32_t dpp_min_u32(uint32_t v) {
-    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, CTRL, ROW_MASK, 0xF, false);
     return o < v ? o : v;
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
@@ -235,41 +237,48 @@ __device__ void wave_topk_ord(const float *__restrict__ lg, int E, int k, int32_
         const float v = lg[e < E ? e : 0];
         key[i] = e < E ? ord_key(v) : 0u;
     }
-    // lane's best: largest key, lowest slot among equals
+    // lane's best: largest key, lowest slot among equals (a pairwise tree,
+    // the right half taken only when strictly larger)
     auto local_best = [&](uint32_t &bk, int &bs) {
-        bk = key[0];
-        bs = 0;
+        uint32_t kk[PER];
+        int ss[PER];
 #pragma unroll
-        for (int i = 1; i < PER; ++i) {
-            const bool take = key[i] > bk;
-            bk = take ? key[i] : bk;
-            bs = take ? i : bs;
+        for (int i = 0; i < PER; ++i) {
+            kk[i] = key[i];
+            ss[i] = i;
         }
+#pragma unroll
+        for (int h = 1; h < PER; h *= 2)
+#pragma unroll
+            for (int i = 0; i + h < PER; i += 2 * h) {
+                const bool take = kk[i + h] > kk[i];
+                kk[i] = take ? kk[i + h] : kk[i];
+                ss[i] = take ? ss[i + h] : ss[i];
+            }
+        bk = kk[0];
+        bs = ss[0];
     };
     uint32_t bk;
     int bs;
     local_best(bk, bs);
-    uint32_t my_key = 0u;
+    uint32_t my_key = 0u;   // lane j: the j-th pick
     int my_id = 0;
     for (int j = 0; j < k; ++j) {
         const uint32_t m = wave_max_u32(bk);
         const unsigned long long hold = __ballot(bk == m);
         int e;
-        if (__popcll(hold) == 1) {
+        if (__builtin_expect(__popcll(hold) != 1, 0))
+            e = (int)wave_min_u32(bk == m ? (uint32_t)(l + 64 * bs) : 0xffffffffu);
+        else {
             const int owner = __builtin_ctzll(hold);
             e = owner + 64 * __builtin_amdgcn_readlane(bs, owner);
-        } else {
-            e = (int)wave_min_u32(bk == m ? (uint32_t)(l + 64 * bs) : 0xffffffffu);
         }
-        if (l == j) {
-            my_key = m;
-            my_id = e;
-        }
-        if (l == (e & 63)) {
-            const int slot = e >> 6;
-#pragma unroll
-            for (int i = 0; i < PER; ++i) key[i] = i == slot ? 0u : key[i];
-        }
+        my_key = l == j ? m : my_key;
+        my_id = l == j ? e : my_id;
+        // the owner clears its pick; every lane rescans (same issue cost as
+        // the owner alone, and no branch)
+        const int slot = wave_uniform(e >> 6);
+        key[slot] = l == (e & 63) ? 0u : key[slot];
         local_best(bk, bs);
     }
     const float l0 = ord_value((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
