@@ -17,6 +17,8 @@ Workloads (default 1):
   2  MTP verify, T=4 through 48 layers, Q3 block-32, Zipf(1.1) router bias
   3  prefill, T=8192, Q2, 1 layer           4  prefill, T=8192, Q3, 48 layers,
                                                Zipf(1.3) router bias
+  5, 6  the "coder" variant (E=256 routed experts): decode T=1 as 1, prefill
+        T=8192 as 3
 Decode workloads report the expert FFN call against HBM bandwidth (bytes of
 the distinct experts selected + activations); prefill workloads against the
 dense fp16/bf16 matrix-core peak (2*M*N*K of the expert GEMMs).
@@ -102,7 +104,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="override the workload's T (tokens per layer), e.g. the mid-size batches")
     ap.add_argument("--copies", type=int, default=None,
                     help="layer copies cycled, single-layer workloads (default 16 decode, 1 prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -138,7 +142,11 @@ def main():
     from quantized_moe_route_amd.layer import DeviceLayer, alloc_buffers, run_layer
 
     w = synth.WORKLOADS[args.workload]
-    prefill = w.T > 32
+    if args.tokens is not None:
+        import dataclasses
+        import re
+        w = dataclasses.replace(w, T=args.tokens, name=re.sub(r"T\d+", f"T{args.tokens}", w.name, count=1))
+    prefill = w.T > 16   # the grouped matrix-core path
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if prefill:
@@ -304,19 +312,21 @@ def main():
     ffn_bytes = float(np.mean(groups)) * eb + act_bytes
     ffn_flops = float(rows_ffn) * 6.0 * w.d_model * w.d_ff
     t_ffn = avg_us["expert_ffn"] * 1e-6
+    # counters were taken at the workload's own T only
+    traffic = traffic_for(args.workload) if args.tokens is None else None
     if prefill:
         achieved = ffn_flops / t_ffn / 1e12
         roof = {"bound": "mfma", "kernel": "moe_expert_ffn (pf_gemm gate/up + down, "
                                            "routed + shared, item build, x to fp16)",
                 "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic,
                 "flops_per_launch": ffn_flops, "avg_groups": float(np.mean(groups)),
                 "hbm_gbs_algorithmic": ffn_bytes / t_ffn / 1e9}
     else:
         achieved = ffn_bytes / t_ffn / 1e9
         roof = {"bound": "hbm", "kernel": "moe_expert_ffn call: gateup_small, down_small",
                 "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(args.workload),
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "bytes_per_launch": ffn_bytes, "avg_groups": float(np.mean(groups))}
     layer_bytes = ffn_bytes + w.d_model * w.n_experts * 4  # + router weights
 

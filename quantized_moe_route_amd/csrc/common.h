@@ -20,10 +20,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Workspace: the first 4 KiB hold int32 counters that are zero between
-// calls (each user restores them); scratch regions start after it.
+// calls (each user restores them); scratch regions start after it.  A
+// counter that many workgroups hit sits on a 128-byte line of its own:
+// device-scope atomics on one line are served one after another.
 constexpr size_t kWsHeader = 4096;
-constexpr int kCntRouteSlice = 0;   // [0, 16): per 64-expert slice arrival counters
-constexpr int kCntRouteAll = 16;    // one counter: slices finished
+constexpr int kCntLine = 32;        // int32 counters per 128-byte line
+constexpr int kRouteTile = 8;       // tokens per tile of the one-launch router
+// the one-launch router's tile tt counts its arrivals at counters[kCntLine * tt]
 
 struct QMatDev {
     const uint8_t *lo;
@@ -259,7 +262,8 @@ hipError_t launch_route_small(const uint16_t *x, const float *wr, const float *b
 hipError_t launch_router_gemm(const uint16_t *x, const float *wr, const float *bias, float *logits,
                               int T, int d, int E, void *ws, hipStream_t s);
 size_t router_gemm_ws_bytes(int d, int E);
-constexpr int kRouteSmallTMax = 8;   // T above this: router GEMM + top-k kernel
+constexpr int kRouteSmallTMax = 128;   // T above this: router GEMM + top-k kernel
+static_assert(kRouteSmallTMax / kRouteTile * kCntLine * 4 <= (int)kWsHeader, "tile counters exceed the header");
 hipError_t launch_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w,
                        hipStream_t s);
 size_t route_ws_bytes(int d, int E, int T);
@@ -272,7 +276,7 @@ hipError_t launch_ffn_small(const moe_layer &L, const uint16_t *x, int T, int k,
                             const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
                             float *y_shared, void *ws, hipStream_t s);
 size_t ffn_small_ws_bytes(int d, int f, int E, int T, int k);
-constexpr int kSmallTMax = 32;
+constexpr int kSmallTMax = 16;   // above: the grouped matrix-core path
 
 hipError_t launch_ffn_prefill(const moe_layer &L, const uint16_t *x, int T, int k,
                               const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,

@@ -1,5 +1,5 @@
 // ffn_small.hip -- expert FFN when every expert group has few rows (decode,
-// MTP verify: T <= 32 tokens).
+// MTP verify: T <= 16 tokens).
 //
 // [forum] discuss.pytorch.kr "Strata: 12GB 그래픽카드 PC에서 125B 모델 …", section
 // "Strata의 동작 원리": 10 routed experts plus the always-resident shared expert
@@ -509,10 +509,8 @@ static void launch_small_t(const moe_layer &L, const uint16_t *x, int T, int k,
         launch_small_fmt<FMT, 1, 1, 2>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
     else if (T <= 8)
         launch_small_fmt<FMT, 1, 1, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
-    else if (T <= 16)
+    else   // T <= 16
         launch_small_fmt<FMT, 1, 2, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
-    else
-        launch_small_fmt<FMT, 2, 4, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
 }
 
 hipError_t launch_ffn_small(const moe_layer &L, const uint16_t *x, int T, int k,

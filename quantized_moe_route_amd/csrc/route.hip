@@ -306,12 +306,13 @@ __device__ __forceinline__ void wave_topk_ord_any(const float *lg, int E, int k,
 }
 
 // ------------------------------------------------------- small T: one launch
-// grid: (ceil(E/64) column slices, d/128 row chunks), 512 threads: wave w of
-// a workgroup owns 16 router rows, lane = one expert column.  Partial sums go
-// out at device scope; the last of all workgroups to arrive adds the d/128
-// partials of every (token, expert) in chunk order, writes the logits and
-// runs the top-k from LDS.
-constexpr int kMaxSmallT = kRouteSmallTMax;
+// grid: (ceil(E/64) column slices, d/128 row chunks, ceil(T/8) token tiles),
+// 512 threads: wave w of a workgroup owns 16 router rows, lane = one expert
+// column, for the tile's (up to) 8 tokens.  Partial sums go out at device
+// scope; the last workgroup of a tile to arrive adds the d/128 partials of
+// every (token, expert) of the tile in chunk order, writes the logits and
+// runs the top-k from LDS.  Tiles are independent (a counter line each).
+constexpr int kMaxSmallT = kRouteTile;
 
 __global__ __launch_bounds__(512) void route_small_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
@@ -330,6 +331,15 @@ __global__ __launch_bounds__(512) void route_small_kernel(
     const int cs = blockIdx.x;
     const int kc = blockIdx.y;
     const int n_kc = gridDim.y;
+    // this workgroup's token tile: tokens [t0, t0 + T)
+    const int t0 = blockIdx.z * kRouteTile;
+    T = T - t0 < kRouteTile ? T - t0 : kRouteTile;
+    x += (size_t)t0 * d;
+    logits += (size_t)t0 * E;
+    ids += (size_t)t0 * k;
+    w += (size_t)t0 * k;
+    partial += (size_t)blockIdx.z * n_kc * kRouteTile * E;
+    int32_t *const counter = counters + kCntLine * blockIdx.z;
     const int tid = threadIdx.x;
     const int col = tid & 63;
     const int wv = wave_uniform(tid >> 6);
@@ -370,9 +380,9 @@ __global__ __launch_bounds__(512) void route_small_kernel(
             store_dev(&partial[((size_t)kc * T + t) * E + e], s_);
         }
     }
-    publish_then_count(&counters[kCntRouteAll], gridDim.x * gridDim.y, last_flag);
+    publish_then_count(counter, gridDim.x * gridDim.y, last_flag);
     if (!last_flag) return;
-    if (tid == 0) store_dev_int(&counters[kCntRouteAll], 0);
+    if (tid == 0) store_dev_int(counter, 0);
     // last workgroup: sum the partials of every (token, expert) in chunk
     // order.  A thread takes up to four (token, expert) entries per pass, with
     // all their partial loads in flight together.
@@ -424,7 +434,8 @@ __global__ __launch_bounds__(512) void route_small_kernel(
 
 size_t route_ws_bytes(int d, int E, int T) {
     if (T > kRouteSmallTMax) return router_gemm_ws_bytes(d, E);
-    return (size_t)(d / 128) * T * E * sizeof(float);
+    const size_t tiles = (size_t)(T + kRouteTile - 1) / kRouteTile;
+    return (size_t)(d / 128) * tiles * kRouteTile * E * sizeof(float);
 }
 
 hipError_t launch_route_small(const uint16_t *x, const float *wr, const float *bias, float *logits,
@@ -432,7 +443,7 @@ hipError_t launch_route_small(const uint16_t *x, const float *wr, const float *b
                               hipStream_t s) {
     int32_t *counters = reinterpret_cast<int32_t *>(ws);
     float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + kWsHeader);
-    dim3 grid((E + 63) / 64, d / 128);
+    dim3 grid((E + 63) / 64, d / 128, (T + kRouteTile - 1) / kRouteTile);
     hipLaunchKernelGGL(route_small_kernel, grid, dim3(512), 0, s, x, wr, bias, logits, T, d, E, k,
                        ids, w, counters, partial);
     return hipGetLastError();

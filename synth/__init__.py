@@ -67,6 +67,9 @@ WORKLOADS = {
     2: Workload(2, "mtp-verify-T4-48L-d2048-f768-E512-top10-Q3-zipf1.1", 2048, 768, 512, 10, 4, 48, FMT_Q3, 1.1),
     3: Workload(3, "prefill-T8192-d2048-f768-E512-top10-Q2", 2048, 768, 512, 10, 8192, 1, FMT_Q2, 0.0),
     4: Workload(4, "prefill-T8192-48L-d2048-f768-E512-top10-Q3-zipf1.3", 2048, 768, 512, 10, 8192, 48, FMT_Q3, 1.3),
+    # the "coder" variant: 256 of the 512 routed experts kept per layer
+    5: Workload(5, "coder-decode-T1-d2048-f768-E256-top10-Q2", 2048, 768, 256, 10, 1, 1, FMT_Q2, 0.0),
+    6: Workload(6, "coder-prefill-T8192-d2048-f768-E256-top10-Q2", 2048, 768, 256, 10, 8192, 1, FMT_Q2, 0.0),
 }
 
 

@@ -1,4 +1,4 @@
-"""GPU parity, decode / MTP-verify shapes (T <= 32): the HIP path through the
+"""GPU parity, decode / MTP-verify shapes (T <= 16): the HIP path through the
 C ABI against the CPU oracle on the same seeded inputs.
 
 Bars: ids, offsets, permutation bit-exact (on identical logits);
@@ -82,7 +82,7 @@ def _check_layer(q, w, L, x_bits, b):
     return err
 
 
-@pytest.mark.parametrize("wid", [0, 1, 2])
+@pytest.mark.parametrize("wid", [0, 1, 2, 5])
 def test_workload_layer_parity(q, wid):
     w = synth.WORKLOADS[wid]
     print(f"workload {w.name}", flush=True)
@@ -96,10 +96,10 @@ def test_workload_layer_parity(q, wid):
 
 @pytest.mark.parametrize("fmt,T,E,k,d,f", [
     (1, 1, 16, 2, 256, 128), (2, 2, 64, 8, 256, 256), (1, 3, 64, 8, 384, 128),
-    (2, 5, 32, 4, 128, 384), (1, 17, 16, 2, 256, 128), (2, 32, 64, 10, 256, 128),
+    (2, 5, 32, 4, 128, 384), (1, 16, 16, 2, 256, 128), (2, 12, 64, 10, 256, 128),
     (1, 9, 1, 1, 128, 128), (2, 4, 8, 8, 128, 128), (1, 16, 512, 10, 128, 128),
-    # more than 512 groups: the two-kernel form; d_ff = 1536: several down batches
-    (2, 32, 1024, 20, 128, 128), (1, 2, 16, 2, 128, 1536),
+    # 321 expert groups; d_ff = 1536: several down batches
+    (2, 16, 1024, 20, 128, 128), (1, 2, 16, 2, 128, 1536),
 ])
 def test_shape_sweep_parity(q, fmt, T, E, k, d, f):
     w = synth.custom(d, f, E, k, T, fmt=fmt, zipf_s=1.3 if fmt == 2 else 0.0, wid=200 + T)
@@ -136,9 +136,11 @@ def test_route_logits_input_ties(q, T, E, k):
 
 
 @pytest.mark.parametrize("T,E,k,d", [(8, 1024, 32, 256), (7, 300, 40, 384), (1, 33, 33, 128),
-                                     (8, 512, 10, 2048)])
+                                     (8, 512, 10, 2048), (9, 512, 10, 2048), (20, 1000, 70, 256),
+                                     (63, 300, 40, 384), (100, 1024, 32, 128), (128, 512, 10, 2048)])
 def test_route_small_path_shapes(q, T, E, k, d):
-    """One-launch router (T <= 8): logits within tolerance, ids bit-exact on them."""
+    """One-launch router (T <= 128, tiles of 8 tokens, the last one ragged):
+    logits within tolerance, ids bit-exact on them."""
     rng = np.random.default_rng(T * E + k)
     x = synth._f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
     wr = (rng.standard_normal((d, E)) / np.sqrt(d)).astype(np.float32)
@@ -159,11 +161,11 @@ def test_route_small_path_shapes(q, T, E, k, d):
         assert np.max(np.abs(wt.cpu().numpy() - w_ref)) <= 1e-6
 
 
-@pytest.mark.parametrize("T,E,k,d", [(300, 300, 40, 384), (20, 1000, 70, 256), (9, 64, 8, 128),
-                                     (513, 17, 3, 2048)])
+@pytest.mark.parametrize("T,E,k,d", [(300, 300, 40, 384), (257, 1000, 70, 256), (1000, 64, 8, 128),
+                                     (513, 17, 3, 2048), (129, 512, 10, 2048)])
 def test_route_gemm_path_shapes(q, T, E, k, d):
-    """Router matrix-core path (T > 8) at ragged shapes: token and expert tiles
-    with tails, E not a multiple of 64, and k > 64 (top-k through LDS)."""
+    """Router matrix-core path (T > 128) at ragged shapes: token and expert
+    tiles with tails, E not a multiple of 64, and k > 64 (top-k through LDS)."""
     rng = np.random.default_rng(T * E + k + d)
     x = synth._f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
     wr = (rng.standard_normal((d, E)) / np.sqrt(d)).astype(np.float32)

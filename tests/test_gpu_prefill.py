@@ -1,4 +1,4 @@
-"""GPU parity, large-batch (prefill) shapes: T > 32 tokens take the grouped
+"""GPU parity, large-batch (prefill) shapes: T > 16 tokens take the grouped
 matrix-core path.  Same inputs as the oracle; bars:
   - ids, offsets, sorted_pair, pair_pos: bit-exact (ids judged on the GPU's
     own logits, which must match the oracle's within tolerance);
@@ -77,6 +77,8 @@ def _check(w, L, x, b, sample=None):
     (1, 33, 16, 2, 256, 128), (2, 100, 64, 8, 256, 256), (1, 257, 32, 4, 384, 128),
     (2, 1000, 512, 10, 256, 128), (1, 2048, 16, 2, 128, 384), (2, 300, 8, 8, 128, 128),
     (1, 129, 1, 1, 128, 128), (2, 640, 64, 10, 512, 256),
+    # the smallest batches on this path (T = 17 .. 32)
+    (1, 17, 16, 2, 256, 128), (2, 32, 64, 10, 256, 128), (2, 32, 1024, 20, 128, 128),
 ])
 def test_prefill_shape_sweep(q, fmt, T, E, k, d, f):
     w = synth.custom(d, f, E, k, T, fmt=fmt, zipf_s=1.3 if fmt == 2 else 0.0, wid=400 + T)
@@ -88,10 +90,11 @@ def test_prefill_shape_sweep(q, fmt, T, E, k, d, f):
     print(f"max|err|/rms = {err:.3e}")
 
 
-@pytest.mark.parametrize("wid", [3, 4])
+@pytest.mark.parametrize("wid", [3, 4, 6])
 def test_prefill_full_workload_sampled(q, wid):
-    """T = 8,192 at d=2048, f=768, E=512, top-10 (+ shared); Q2 uniform routing
-    and Q3 Zipf(1.3) routing (layer 0).  64 sampled tokens against the oracle."""
+    """T = 8,192 at d=2048, f=768, top-10 (+ shared): E=512 with Q2 uniform
+    routing and Q3 Zipf(1.3) routing (layer 0), and the E=256 variant with Q2.
+    64 sampled tokens against the oracle."""
     w = synth.WORKLOADS[wid]
     print(f"workload {w.name}", flush=True)
     L = synth.gen_layer(w, layer=0)
