@@ -9,7 +9,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "_lib", "libmoe.so")
-SOURCES = ["route.hip", "dispatch.hip", "ffn_small.hip", "ffn_prefill.hip", "combine.hip", "abi.hip"]
+# (source, object, extra flags): the grouped GEMM is built twice, for large
+# chunks and for mid-size batches
+SOURCES = [("route.hip", "route.o", []), ("dispatch.hip", "dispatch.o", []),
+           ("ffn_small.hip", "ffn_small.o", []), ("ffn_prefill.hip", "ffn_prefill.o", []),
+           ("ffn_prefill.hip", "ffn_prefill_mid.o", ["-DMOE_PF_MID"]),
+           ("combine.hip", "combine.o", []), ("abi.hip", "abi.o", [])]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # packed fp32 VALU forms are disabled for all device code
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -21,9 +26,10 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
 EXTRA = {"ffn_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-    r = subprocess.run([HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj],
+def _compile(entry) -> str:
+    src, obj_name, extra = entry
+    obj = os.path.join(OBJ, obj_name)
+    r = subprocess.run([HIPCC, *FLAGS, *EXTRA.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj],
                        capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

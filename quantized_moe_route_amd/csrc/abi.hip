@@ -40,9 +40,9 @@ bool check_qmat(const moe_qmat &m, int fmt) {
 size_t route_need(int d, int E, int T) { return kWsHeader + route_ws_bytes(d, E, T); }
 size_t dispatch_need(int E, int T, int k) { return kWsHeader + dispatch_ws_bytes(E, T, k); }
 size_t ffn_need(int d, int f, int E, int T, int k) {
-    const size_t a = ffn_small_ws_bytes(d, f, E, T, k);
-    const size_t b = ffn_prefill_ws_bytes(d, f, E, T, k);
-    return kWsHeader + (T <= kSmallTMax ? a : b);
+    if (T <= kSmallTMax) return kWsHeader + ffn_small_ws_bytes(d, f, E, T, k);
+    if (T <= kPfMidTMax) return kWsHeader + ffn_prefill_mid_ws_bytes(d, f, E, T, k);
+    return kWsHeader + ffn_prefill_ws_bytes(d, f, E, T, k);
 }
 
 }  // namespace
@@ -147,7 +147,9 @@ moe_status moe_expert_ffn(const moe_layer *layer, const uint16_t *x_bf16, int32_
     if (T <= kSmallTMax)
         return launched(launch_ffn_small(L, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared,
                                          ws, s));
-    hipError_t e = launch_ffn_prefill(L, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, ws, s);
+    hipError_t e = T <= kPfMidTMax
+                       ? launch_ffn_prefill_mid(L, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, ws, s)
+                       : launch_ffn_prefill(L, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, ws, s);
     if (e == hipErrorNotSupported) return MOE_ERR_UNSUPPORTED;
     return launched(e);
 }

@@ -282,6 +282,13 @@ hipError_t launch_ffn_prefill(const moe_layer &L, const uint16_t *x, int T, int 
                               const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
                               float *y_shared, void *ws, hipStream_t s);
 size_t ffn_prefill_ws_bytes(int d, int f, int E, int T, int k);
+// the same grouped GEMM built for mid-size batches (64-row items, two
+// workgroups per compute unit)
+hipError_t launch_ffn_prefill_mid(const moe_layer &L, const uint16_t *x, int T, int k,
+                                  const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
+                                  float *y_shared, void *ws, hipStream_t s);
+size_t ffn_prefill_mid_ws_bytes(int d, int f, int E, int T, int k);
+constexpr int kPfMidTMax = 2048;   // T above this: the large-chunk build
 
 hipError_t launch_combine(const float *y_pairs, const float *y_shared, const int32_t *pair_pos,
                           const float *w, int T, int k, int d, float *out, hipStream_t s);

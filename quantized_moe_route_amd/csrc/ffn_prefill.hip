@@ -39,11 +39,29 @@
 // dropped).  Max |err| / rms(out) stays near 1.1e-3 on these workloads.
 #include "common.h"
 
-namespace moe {
-
-#ifndef MOE_PF_ROWS
+// The file is built twice.  The default build serves large chunks: 192-row
+// work items, one GEMM workgroup per compute unit.  With MOE_PF_MID it serves
+// mid-size batches (up to a few thousand tokens, where the matrix work per
+// weight byte is small): 64-row items and two workgroups per compute unit,
+// so twice the weight loads are in flight.  Each build keeps its kernels in a
+// namespace of its own.
+#ifdef MOE_PF_MID
+#define MOE_PF_ROWS 64
+#define MOE_PF_OCC 2
+#define MOE_PF_NS pf_mid
+#define MOE_PF_LAUNCH launch_ffn_prefill_mid
+#define MOE_PF_WS ffn_prefill_mid_ws_bytes
+#else
 #define MOE_PF_ROWS 192
+#define MOE_PF_OCC 1
+#define MOE_PF_NS pf_big
+#define MOE_PF_LAUNCH launch_ffn_prefill
+#define MOE_PF_WS ffn_prefill_ws_bytes
 #endif
+
+namespace moe {
+namespace MOE_PF_NS {
+
 constexpr int PF_MT = MOE_PF_ROWS;                // rows per work item (multiple of 64, <= 192)
 constexpr int PF_KS = 128;                        // K per pipeline stage
 constexpr int PF_STAGE = PF_MT * PF_KS * 2;       // bytes of one A stage
@@ -679,7 +697,7 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
 // Persistent grouped GEMM: workgroups take (item, column tile) units by
 // ticket from their XCD's queue, then from the others.
 template <int FMT, int MODE, int NTW>
-__global__ __launch_bounds__(256, 1) void pf_gemm_kernel(PfGemmArgs a) {
+__global__ __launch_bounds__(256, MOE_PF_OCC) void pf_gemm_kernel(PfGemmArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t As[PF_NSTAGE * PF_STAGE];
     __shared__ int s_row[PF_MT];
     __shared__ int s_ticket;
@@ -776,7 +794,7 @@ static PfWs pf_carve(void *ws, int d, int f, int E, int T, int k) {
     return w;
 }
 
-size_t ffn_prefill_ws_bytes(int d, int f, int E, int T, int k) {
+static size_t ws_bytes(int d, int f, int E, int T, int k) {
     return 256 + align256(pf_max_items(E, T, k) * sizeof(PfItem)) + align256((size_t)T * d * 2) +
            align256(((size_t)T * k + T) * f * 2) + align256((size_t)T * f * 2);
 }
@@ -820,7 +838,7 @@ static void pf_launch_fmt(const moe_layer &L, const uint16_t *x, int T, int k, c
     a.d = d;
     a.f = f;
     using G = PfGeom<kPfNtw>;
-    const int grid = pf_grid(1);
+    const int grid = pf_grid(MOE_PF_OCC);
     // gate/up + SwiGLU
     a.w0 = QMatDev{L.gate.lo, L.gate.hi, L.gate.scale, L.gate.min};
     a.w1 = QMatDev{L.up.lo, L.up.hi, L.up.scale, L.up.min};
@@ -841,15 +859,25 @@ static void pf_launch_fmt(const moe_layer &L, const uint16_t *x, int T, int k, c
     hipLaunchKernelGGL((pf_gemm_kernel<FMT, 1, kPfNtw>), dim3(grid), dim3(256), 0, s, a);
 }
 
-hipError_t launch_ffn_prefill(const moe_layer &L, const uint16_t *x, int T, int k,
-                              const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
-                              float *y_shared, void *ws, hipStream_t s) {
+static hipError_t launch(const moe_layer &L, const uint16_t *x, int T, int k, const int32_t *offsets,
+                         const int32_t *sorted_pair, float *y_pairs, float *y_shared, void *ws,
+                         hipStream_t s) {
     const PfWs w = pf_carve(ws, L.d_model, L.d_ff, L.n_experts, T, k);
     if (L.format == MOE_FMT_Q2_B32)
         pf_launch_fmt<MOE_FMT_Q2_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, w, s);
     else
         pf_launch_fmt<MOE_FMT_Q3_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, w, s);
     return hipGetLastError();
+}
+
+}  // namespace MOE_PF_NS
+
+size_t MOE_PF_WS(int d, int f, int E, int T, int k) { return MOE_PF_NS::ws_bytes(d, f, E, T, k); }
+
+hipError_t MOE_PF_LAUNCH(const moe_layer &L, const uint16_t *x, int T, int k, const int32_t *offsets,
+                         const int32_t *sorted_pair, float *y_pairs, float *y_shared, void *ws,
+                         hipStream_t s) {
+    return MOE_PF_NS::launch(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, ws, s);
 }
 
 }  // namespace moe
