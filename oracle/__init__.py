@@ -119,6 +119,27 @@ def dispatch(ids, E):
     return offsets, sp, pp
 
 
+def dispatch_tail_skip(ids, E, tail_from):
+    """dispatch() without the pairs of experts that every token of the batch
+    picked only at rank >= tail_from (0-based); those pairs get pair_pos -1."""
+    ids = np.ascontiguousarray(ids, np.int32)
+    T, k = ids.shape
+    offsets = np.empty(E + 1, np.int32)
+    sp = np.empty(T * k, np.int32)
+    pp = np.empty(T * k, np.int32)
+    lib().oracle_dispatch_tail_skip(_p(ids), T, k, E, int(tail_from), _p(offsets), _p(sp), _p(pp))
+    return offsets, sp, pp
+
+
+def tail_keep(ids, E, tail_from):
+    """keep[e]: expert e is picked at some rank < tail_from in the batch."""
+    ids = np.ascontiguousarray(ids, np.int32)
+    T, k = ids.shape
+    keep = np.empty(E, np.int8)
+    lib().oracle_tail_keep(_p(ids), T, k, E, int(tail_from), _p(keep))
+    return keep.astype(bool)
+
+
 def _layer_structs(L):
     parts = [_qm(getattr(L, n)) for n in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")]
     return [C.byref(p[0]) for p in parts], parts
@@ -149,8 +170,9 @@ def combine(y_pairs, y_shared, pair_pos, w, T, k, d) -> np.ndarray:
     return out
 
 
-def layer(L, fmt, d, f, E, k, x_bits, wr=None, bias=None, logits=None):
-    """Whole layer; returns (ids, w, out).  Give `logits` to route on fixed logits."""
+def layer(L, fmt, d, f, E, k, x_bits, wr=None, bias=None, logits=None, tail_from=None):
+    """Whole layer; returns (ids, w, out).  Give `logits` to route on fixed logits;
+    `tail_from` < k skips the experts the batch picked only at ranks >= tail_from."""
     x_bits = np.ascontiguousarray(x_bits, np.uint16)
     T = x_bits.shape[0]
     ids = np.empty((T, k), np.int32)
@@ -160,6 +182,7 @@ def layer(L, fmt, d, f, E, k, x_bits, wr=None, bias=None, logits=None):
     b = None if bias is None else np.ascontiguousarray(bias, np.float32)
     lg = None if logits is None else np.ascontiguousarray(logits, np.float32)
     refs, keep = _layer_structs(L)
-    lib().oracle_layer(*refs, fmt, d, f, E, k, T, _p(x_bits), _p(wr), _p(b), _p(lg),
+    tf = k if tail_from is None else int(tail_from)
+    lib().oracle_layer(*refs, fmt, d, f, E, k, T, _p(x_bits), _p(wr), _p(b), _p(lg), tf,
                        _p(ids), _p(w), _p(out))
     return ids, w, out

@@ -203,6 +203,45 @@ void oracle_dispatch(const int32_t *ids, int T, int k, int E,
     offsets[E] = (int32_t)n;
 }
 
+/* Route tail-skip.  [forum] section "Strata의 동작 원리 / 그래픽카드, RAM, SSD에
+ * 나눠 담은 전문가": an expert that every token of the batch picked only at
+ * 7th place or lower of its top 10 is not computed (there, only for experts
+ * outside VRAM; the other routing weights are left as they are).  Here:
+ * expert e is kept iff some pair (t, j) with rank j < tail_from (0-based)
+ * selects it.  The pairs of the other experts are dropped: pair_pos = -1, and
+ * they appear in neither sorted_pair nor offsets.  Kept pairs are listed as
+ * oracle_dispatch lists them.  tail_from = k keeps every pair. */
+void oracle_tail_keep(const int32_t *ids, int T, int k, int E, int tail_from, char *keep)
+{
+    memset(keep, 0, (size_t)E);
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < k && j < tail_from; ++j) keep[ids[(long)t * k + j]] = 1;
+}
+
+void oracle_dispatch_tail_skip(const int32_t *ids, int T, int k, int E, int tail_from,
+                               int32_t *offsets, int32_t *sorted_pair, int32_t *pair_pos)
+{
+    long P = (long)T * k;
+    char *keep = malloc((size_t)E);
+    oracle_tail_keep(ids, T, k, E, tail_from, keep);
+    long n = 0;
+    for (int e = 0; e < E; ++e) {
+        offsets[e] = (int32_t)n;
+        for (long p = 0; p < P; ++p)
+            if (ids[p] == e) {
+                if (keep[e]) {
+                    sorted_pair[n] = (int32_t)p;
+                    pair_pos[p] = (int32_t)n;
+                    ++n;
+                } else {
+                    pair_pos[p] = -1;
+                }
+            }
+    }
+    offsets[E] = (int32_t)n;
+    free(keep);
+}
+
 /* ------------------------------------------------------------------- expert */
 
 /* One expert applied to one token row, with the expert's matrices given dense:
@@ -310,7 +349,8 @@ void oracle_expert_rows(const oracle_qmat *gate, const oracle_qmat *up, const or
 
 /* ------------------------------------------------------------------ combine */
 
-/* out[t] = y_shared[t] + sum_{j<k} w[t][j] * y_pairs[pair_pos[t*k+j]], in double. */
+/* out[t] = y_shared[t] + sum_{j<k} w[t][j] * y_pairs[pair_pos[t*k+j]], in double;
+ * a dropped pair (pair_pos < 0, route tail-skip) adds nothing. */
 void oracle_combine(const float *y_pairs, const float *y_shared, const int32_t *pair_pos,
                     const float *w, int T, int k, int d, float *out)
 {
@@ -318,9 +358,11 @@ void oracle_combine(const float *y_pairs, const float *y_shared, const int32_t *
     for (int t = 0; t < T; ++t)
         for (int o = 0; o < d; ++o) {
             double acc = y_shared[(long)t * d + o];
-            for (int j = 0; j < k; ++j)
-                acc += (double)w[(long)t * k + j] *
-                       (double)y_pairs[(long)pair_pos[(long)t * k + j] * d + o];
+            for (int j = 0; j < k; ++j) {
+                const int32_t pos = pair_pos[(long)t * k + j];
+                if (pos < 0) continue;
+                acc += (double)w[(long)t * k + j] * (double)y_pairs[(long)pos * d + o];
+            }
             out[(long)t * d + o] = (float)acc;
         }
 }
@@ -330,6 +372,9 @@ void oracle_combine(const float *y_pairs, const float *y_shared, const int32_t *
 /* The whole layer for T tokens:
  *   route (logits given, or computed from x, Wr, bias) -> top-k softmax
  *   weights -> k routed experts + the shared expert per token -> weighted sum.
+ * With tail_from < k the routed experts of the batch that only appear at
+ * ranks >= tail_from are skipped (route tail-skip, oracle_tail_keep); their
+ * terms are left out and the other weights are not changed.
  * The expert outputs stay in double up to the final sum, so this is the
  * closed-form value of the layer (the routing weights are the fp32 values
  * stored in w).  If logits_in is NULL the logits are computed with
@@ -337,7 +382,7 @@ void oracle_combine(const float *y_pairs, const float *y_shared, const int32_t *
 void oracle_layer(const oracle_qmat *gate, const oracle_qmat *up, const oracle_qmat *down,
                   const oracle_qmat *sh_gate, const oracle_qmat *sh_up, const oracle_qmat *sh_down,
                   int fmt, int d, int f, int E, int k, int T, const uint16_t *x,
-                  const float *wr, const float *bias, const float *logits_in,
+                  const float *wr, const float *bias, const float *logits_in, int tail_from,
                   int32_t *ids, float *w, float *out)
 {
     float *logits = NULL;
@@ -348,6 +393,8 @@ void oracle_layer(const oracle_qmat *gate, const oracle_qmat *up, const oracle_q
         lg = logits;
     }
     oracle_topk_softmax(lg, T, E, k, ids, w);
+    char *keep = malloc((size_t)E);
+    oracle_tail_keep(ids, T, k, E, tail_from, keep);
     /* row t*(k+1)+j: token t with its j-th expert; j == k is the shared expert */
     int n_rows = T * (k + 1);
     int32_t *re = malloc(sizeof(int32_t) * (size_t)n_rows);
@@ -364,9 +411,11 @@ void oracle_layer(const oracle_qmat *gate, const oracle_qmat *up, const oracle_q
         for (int o = 0; o < d; ++o) {
             double acc = yall[((long)t * (k + 1) + k) * d + o];
             for (int j = 0; j < k; ++j)
-                acc += (double)w[(long)t * k + j] * yall[((long)t * (k + 1) + j) * d + o];
+                if (keep[ids[(long)t * k + j]])
+                    acc += (double)w[(long)t * k + j] * yall[((long)t * (k + 1) + j) * d + o];
             out[(long)t * d + o] = (float)acc;
         }
+    free(keep);
     free(yall);
     free(rt);
     free(re);

@@ -395,3 +395,109 @@ def test_layer_equals_composition_of_steps():
     out2 = oracle.combine(y[:w.P], y[w.P:], pp, w2, w.T, w.k, w.d_model)
     assert np.array_equal(ids, ids2) and np.array_equal(wt, w2)
     assert np.max(np.abs(out - out2)) <= 1e-6 * np.sqrt(np.mean(out.astype(np.float64) ** 2))
+
+
+# ------------------------------------------------------------ route tail-skip
+def _read_fixture(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].split()
+            if line:
+                vals[line[0]] = [int(v) for v in line[1:]]
+    return vals
+
+
+def test_tail_skip_hand_example():
+    g = _read_fixture("tail_skip_example.txt")
+    T, k, E, tf = g["T"][0], g["k"][0], g["E"][0], g["tail_from"][0]
+    ids = np.array(g["ids"], np.int32).reshape(T, k)
+    assert np.array_equal(oracle.tail_keep(ids, E, tf), np.array(g["keep"], bool))
+    off, sp, pp = oracle.dispatch_tail_skip(ids, E, tf)
+    n = off[E]
+    assert np.array_equal(off, g["offsets"])
+    assert np.array_equal(sp[:n], g["sorted_pair"])
+    assert np.array_equal(pp, g["pair_pos"])
+
+
+def _tail_skip_brute(ids, E, tf):
+    """Loops straight from the rule: keep e iff some (t, j < tf) picks e."""
+    T, k = ids.shape
+    keep = [False] * E
+    for t in range(T):
+        for j in range(min(tf, k)):
+            keep[ids[t, j]] = True
+    offsets, sp, pp = [], [], [-1] * (T * k)
+    for e in range(E):
+        offsets.append(len(sp))
+        for p in range(T * k):
+            if ids[p // k, p % k] == e and keep[e]:
+                pp[p] = len(sp)
+                sp.append(p)
+    offsets.append(len(sp))
+    return np.array(keep), np.array(offsets), np.array(sp, np.int64), np.array(pp)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_tail_skip_vs_brute_force(seed):
+    rng = np.random.default_rng(900 + seed)
+    T, E = int(rng.integers(1, 20)), int(rng.integers(2, 13))
+    k = int(rng.integers(1, min(E, 6) + 1))
+    tf = int(rng.integers(0, k + 1))
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    keep, off_b, sp_b, pp_b = _tail_skip_brute(ids, E, tf)
+    off, sp, pp = oracle.dispatch_tail_skip(ids, E, tf)
+    assert np.array_equal(oracle.tail_keep(ids, E, tf), keep)
+    assert np.array_equal(off, off_b)
+    assert np.array_equal(sp[:off[E]], sp_b)
+    assert np.array_equal(pp, pp_b)
+
+
+def test_tail_skip_special_cases():
+    rng = np.random.default_rng(31)
+    E, k = 512, 10
+    # one token: exactly its first tail_from picks survive, in expert order
+    ids1 = rng.permutation(E)[:k].astype(np.int32)[None, :]
+    off, sp, pp = oracle.dispatch_tail_skip(ids1, E, 6)
+    assert off[E] == 6 and np.all(pp[6:] == -1)
+    assert np.array_equal(sp[:6], np.argsort(ids1[0, :6], kind="stable"))
+    # tail_from = k: the plain dispatch, bit for bit
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(40)]).astype(np.int32)
+    for a, b in zip(oracle.dispatch_tail_skip(ids, E, k), oracle.dispatch(ids, E)):
+        assert np.array_equal(a[:len(b)], b)
+    # tail_from = 0: nothing is computed
+    off, _, pp = oracle.dispatch_tail_skip(ids, E, 0)
+    assert np.all(off == 0) and np.all(pp == -1)
+
+
+def test_layer_tail_skip_equals_composition():
+    """oracle.layer(tail_from) == shared + the kept pairs' weighted rows; with
+    tail_from = k it is the plain layer; tail_from = 0 leaves the shared
+    expert alone."""
+    w = synth.custom(128, 128, 24, 6, 5, fmt=2, zipf_s=1.1, wid=930)
+    L = synth.gen_layer(w)
+    x = synth.gen_x(w)
+    d, f, E, k, T = w.d_model, w.d_ff, w.n_experts, w.k, w.T
+    lg = oracle.router_logits(x, L.router, L.bias)
+    ids, wt = oracle.topk_softmax(lg, k)
+    tf = 3
+    off, sp, pp = oracle.dispatch_tail_skip(ids, E, tf)
+    n = off[E]
+    assert 0 < n < T * k
+    flat = ids.ravel()
+    re = np.concatenate([flat[sp[:n]], -np.ones(T, np.int32)]).astype(np.int32)
+    rt = np.concatenate([sp[:n] // k, np.arange(T)]).astype(np.int32)
+    y = oracle.expert_rows(L, w.fmt, d, f, E, x, re, rt)
+    yp = np.zeros((T * k, d), np.float32)
+    yp[:n] = y[:n]
+    out_c = oracle.combine(yp, y[n:], pp, wt, T, k, d)
+    _, _, out = oracle.layer(L, w.fmt, d, f, E, k, x, logits=lg, tail_from=tf)
+    rms = np.sqrt(np.mean(out.astype(np.float64) ** 2))
+    assert np.max(np.abs(out - out_c)) <= 1e-6 * rms
+    _, _, plain = oracle.layer(L, w.fmt, d, f, E, k, x, logits=lg)
+    _, _, same = oracle.layer(L, w.fmt, d, f, E, k, x, logits=lg, tail_from=k)
+    assert np.array_equal(plain, same)
+    assert np.max(np.abs(out - plain)) > 0.0
+    _, _, sh = oracle.layer(L, w.fmt, d, f, E, k, x, logits=lg, tail_from=0)
+    ysh = oracle.expert_rows(L, w.fmt, d, f, E, x, -np.ones(T, np.int32), np.arange(T, dtype=np.int32))
+    assert np.max(np.abs(sh - ysh)) <= 1e-6 * np.sqrt(np.mean(ysh.astype(np.float64) ** 2))
