@@ -398,7 +398,7 @@ def test_layer_equals_composition_of_steps():
 
 
 # ------------------------------------------------------------ route tail-skip
-def _read_fixture(name):
+def _read_int_fixture(name):
     vals = {}
     with open(os.path.join(GOLDEN, name)) as fh:
         for line in fh:
@@ -409,7 +409,7 @@ def _read_fixture(name):
 
 
 def test_tail_skip_hand_example():
-    g = _read_fixture("tail_skip_example.txt")
+    g = _read_int_fixture("tail_skip_example.txt")
     T, k, E, tf = g["T"][0], g["k"][0], g["E"][0], g["tail_from"][0]
     ids = np.array(g["ids"], np.int32).reshape(T, k)
     assert np.array_equal(oracle.tail_keep(ids, E, tf), np.array(g["keep"], bool))
