@@ -156,6 +156,27 @@ moe_status moe_dispatch(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k
                         size_t ws_bytes, void *stream);
 
 /*
+ * moe_dispatch_tail_skip -- moe_dispatch with route tail-skip (opt-in, lossy).
+ * [forum] "Strata의 동작 원리 / 그래픽카드, RAM, SSD에 나눠 담은 전문가": an expert
+ * that every token of the batch picked only at 7th place or lower of its
+ * top 10 is not computed, and the other routing weights are left as they are
+ * (there the rule covers only experts outside VRAM; every expert is resident
+ * here, so it applies to all of them).
+ *
+ * tail_from in [0, k]: expert e is kept iff some token picks it at a rank
+ * j < tail_from (0-based; the page's rule is tail_from = 6 for k = 10).  The
+ * pairs of the other experts are dropped: pair_pos[p] = -1, and they appear in
+ * neither sorted_pair nor offsets (offsets[E] = number of kept pairs <= P).
+ * Kept pairs are listed exactly as moe_dispatch lists them.  tail_from = k
+ * gives moe_dispatch's result.  moe_expert_ffn computes only the listed rows;
+ * moe_combine leaves dropped pairs out.  Same preconditions, workspace and
+ * errors as moe_dispatch; tail_from outside [0, k] is MOE_ERR_INVALID_ARGUMENT.
+ */
+moe_status moe_dispatch_tail_skip(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k,
+                                  int32_t tail_from, int32_t *offsets, int32_t *sorted_pair,
+                                  int32_t *pair_pos, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * moe_expert_ffn -- the selected experts and the shared expert.
  * [forum] "Strata의 동작 원리" and [guide] "Strata, Qwen, GSQ-RCO…": 10 routed
  * experts plus one shared expert per token per layer; [video] "픽업": the
@@ -167,7 +188,9 @@ moe_status moe_dispatch(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k
  *   y = h . Wd_e^T
  * y_pairs  [T*k][d_model] fp32: row i = position i (expert-sorted order).
  * y_shared [T][d_model] fp32: the shared expert on each token.
- * offsets and sorted_pair as written by moe_dispatch for the same T, k, E.
+ * offsets and sorted_pair as written by moe_dispatch (or
+ * moe_dispatch_tail_skip) for the same T, k, E; rows past offsets[E] of
+ * y_pairs are not written.
  * Weights are dequantised exactly in fp32 when few rows share an expert
  * (decode); larger groups use fp16 matrix-core tiles with fp32 accumulation.
  */
@@ -180,7 +203,8 @@ moe_status moe_expert_ffn(const moe_layer *layer, const uint16_t *x_bf16, int32_
  * [forum] "Strata의 동작 원리": the GPU merges every expert's result, then the
  * next layer starts.
  *   out[t][:] = y_shared[t][:] + sum_{j<k} topk_w[t][j] * y_pairs[pair_pos[t*k+j]][:]
- * out [T][d_model] fp32, overwritten.  Needs no workspace.
+ * where a pair with pair_pos -1 (dropped by moe_dispatch_tail_skip) adds
+ * nothing.  out [T][d_model] fp32, overwritten.  Needs no workspace.
  */
 moe_status moe_combine(const float *y_pairs, const float *y_shared, const int32_t *pair_pos,
                        const float *topk_w, int32_t T, int32_t k, int32_t d_model, float *out,

@@ -105,10 +105,11 @@ moe_status moe_route(const uint16_t *x_bf16, const float *w_router, const float 
     return launched(launch_topk(logits, T, E, k, topk_ids, topk_w, s));
 }
 
-moe_status moe_dispatch(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k,
-                        int32_t *offsets, int32_t *sorted_pair, int32_t *pair_pos, void *ws,
-                        size_t ws_bytes, void *stream) {
+static moe_status dispatch_checked(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k,
+                                   int32_t tail_from, int32_t *offsets, int32_t *sorted_pair,
+                                   int32_t *pair_pos, void *ws, size_t ws_bytes, void *stream) {
     if (T < 0 || E < 1 || E > kMaxE || k < 1 || k > E) return MOE_ERR_INVALID_ARGUMENT;
+    if (tail_from < 0 || tail_from > k) return MOE_ERR_INVALID_ARGUMENT;
     if ((int64_t)T * k >= INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
     if (!topk_ids || !offsets || !sorted_pair || !pair_pos) return MOE_ERR_INVALID_ARGUMENT;
     if (!aligned16(topk_ids) || !aligned16(offsets) || !aligned16(sorted_pair) ||
@@ -116,8 +117,21 @@ moe_status moe_dispatch(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k
         return MOE_ERR_INVALID_ARGUMENT;
     if (!ws || !aligned256(ws) || ws_bytes < dispatch_need(E, T, k)) return MOE_ERR_WORKSPACE;
     if (T == 0) return MOE_OK;
-    return launched(launch_dispatch(topk_ids, T, E, k, offsets, sorted_pair, pair_pos, ws,
+    return launched(launch_dispatch(topk_ids, T, E, k, tail_from, offsets, sorted_pair, pair_pos, ws,
                                     as_stream(stream)));
+}
+
+moe_status moe_dispatch(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k,
+                        int32_t *offsets, int32_t *sorted_pair, int32_t *pair_pos, void *ws,
+                        size_t ws_bytes, void *stream) {
+    return dispatch_checked(topk_ids, T, E, k, k, offsets, sorted_pair, pair_pos, ws, ws_bytes, stream);
+}
+
+moe_status moe_dispatch_tail_skip(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k,
+                                  int32_t tail_from, int32_t *offsets, int32_t *sorted_pair,
+                                  int32_t *pair_pos, void *ws, size_t ws_bytes, void *stream) {
+    return dispatch_checked(topk_ids, T, E, k, tail_from, offsets, sorted_pair, pair_pos, ws, ws_bytes,
+                            stream);
 }
 
 moe_status moe_expert_ffn(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, int32_t k,

@@ -7,7 +7,9 @@
 // A pure streaming gather: one thread per 4 output columns, fp32, shared term
 // first then j = 0..k-1 (fixed order, deterministic).  The pair positions and
 // weights of a batch of 8 j are loaded first, then the batch's 8 rows all at
-// once, so each thread keeps 8 row loads in flight instead of one.
+// once, so each thread keeps 8 row loads in flight instead of one.  A pair
+// that route tail-skip dropped (pair_pos -1) adds nothing (its load reads
+// row 0, unused).
 #include "common.h"
 
 namespace moe {
@@ -37,10 +39,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
         float4 v[kCombineBatch];
 #pragma unroll
         for (int i = 0; i < kCombineBatch; ++i)
-            v[i] = *reinterpret_cast<const float4 *>(y_pairs + (size_t)p[i] * d + c);
+            v[i] = *reinterpret_cast<const float4 *>(y_pairs + (size_t)(p[i] >= 0 ? p[i] : 0) * d + c);
 #pragma unroll
         for (int i = 0; i < kCombineBatch; ++i) {
-            if (j0 + i < k) {
+            if (j0 + i < k && p[i] >= 0) {
                 acc.x += wj[i] * v[i].x;
                 acc.y += wj[i] * v[i].y;
                 acc.z += wj[i] * v[i].z;

@@ -268,7 +268,8 @@ hipError_t launch_topk(const float *logits, int T, int E, int k, int32_t *ids, f
                        hipStream_t s);
 size_t route_ws_bytes(int d, int E, int T);
 
-hipError_t launch_dispatch(const int32_t *ids, int T, int E, int k, int32_t *offsets,
+// tail_from >= k: every pair; tail_from < k: route tail-skip
+hipError_t launch_dispatch(const int32_t *ids, int T, int E, int k, int tail_from, int32_t *offsets,
                            int32_t *sorted_pair, int32_t *pair_pos, void *ws, hipStream_t s);
 size_t dispatch_ws_bytes(int E, int T, int k);
 

@@ -12,6 +12,13 @@
 // atomic OR.  The rank of a pair inside its expert segment is then
 //   (pairs of e in earlier chunks) + popcount(mask & lanes below this one),
 // which is exactly the position a stable sort by (expert, pair index) gives.
+//
+// Route tail-skip (opt-in; same page, same section: an expert that every token
+// of the batch picked only at 7th place or lower of its top 10 is not
+// computed).  With a rank threshold tail_from, expert e is kept iff some token
+// picks it at a rank j < tail_from; the pairs of the other experts are left
+// out of the listing (pair_pos = -1) and offsets count kept pairs only.  The
+// kernels take a keep flag per expert (nullptr: every pair is kept).
 #include "common.h"
 
 namespace moe {
@@ -20,14 +27,18 @@ __device__ __forceinline__ unsigned long long below_mask(int lane) {
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// one wave: OR each token's bit into masks[e] for its k experts
+// one wave: OR each token's bit into masks[e] for its k experts (kept ones)
 __device__ __forceinline__ void build_chunk_masks(const int32_t *__restrict__ ids, int T, int k,
-                                                  int chunk, unsigned long long *masks) {
+                                                  int chunk, unsigned long long *masks,
+                                                  const int32_t *keep) {
     const int lane = __lane_id();
     const int t = chunk * 64 + lane;
     if (t < T) {
         const unsigned long long bit = 1ull << lane;
-        for (int j = 0; j < k; ++j) atomicOr(&masks[ids[(size_t)t * k + j]], bit);
+        for (int j = 0; j < k; ++j) {
+            const int e = ids[(size_t)t * k + j];
+            if (!keep || keep[e]) atomicOr(&masks[e], bit);
+        }
     }
 }
 
@@ -35,17 +46,34 @@ __device__ __forceinline__ void write_chunk_positions(const int32_t *__restrict_
                                                       int chunk, const unsigned long long *masks,
                                                       const int32_t *base /* [E] for chunk */,
                                                       int32_t *__restrict__ sorted_pair,
-                                                      int32_t *__restrict__ pair_pos) {
+                                                      int32_t *__restrict__ pair_pos,
+                                                      const int32_t *keep) {
     const int lane = __lane_id();
     const int t = chunk * 64 + lane;
     if (t >= T) return;
     const unsigned long long lt = below_mask(lane);
     for (int j = 0; j < k; ++j) {
         const int e = ids[(size_t)t * k + j];
-        const int pos = base[e] + __popcll(masks[e] & lt);
         const int p = t * k + j;
+        if (keep && !keep[e]) {
+            pair_pos[p] = -1;
+            continue;
+        }
+        const int pos = base[e] + __popcll(masks[e] & lt);
         sorted_pair[pos] = p;
         pair_pos[p] = pos;
+    }
+}
+
+// keep[e] = 1 iff some token picks e at a rank below tail_from (keep zeroed
+// before); every writer stores the same value
+__device__ __forceinline__ void mark_kept(const int32_t *__restrict__ ids, int T, int k, int tail_from,
+                                          int32_t *keep, int i0, int stride) {
+    const int n = T * (tail_from < k ? tail_from : k);
+    const int kh = tail_from < k ? tail_from : k;
+    for (int i = i0; i < n; i += stride) {
+        const int t = i / kh, j = i - t * kh;
+        keep[ids[(size_t)t * k + j]] = 1;
     }
 }
 
@@ -70,8 +98,9 @@ __device__ void block_excl_scan_1024(int *v, int n, int *wsum /* LDS [16] */) {
 // ------------------------------------------------------------ fused, small P
 constexpr int kSmallMaskEntries = 4096;   // n_chunks * E
 
+template <bool TAIL>
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t *__restrict__ ids, int T,
-                                                              int E, int k,
+                                                              int E, int k, int tail_from,
                                                               int32_t *__restrict__ offsets,
                                                               int32_t *__restrict__ sorted_pair,
                                                               int32_t *__restrict__ pair_pos) {
@@ -79,16 +108,23 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t *__r
     __shared__ int32_t cbase[kSmallMaskEntries];
     __shared__ int32_t tot[1024];
     __shared__ int wsum[16];
+    __shared__ int32_t keep_s[TAIL ? 1024 : 1];
+    const int32_t *keep = TAIL ? keep_s : nullptr;
     const int tid = threadIdx.x;
     const int wv = tid >> 6;
     const int n_chunks = (T + 63) / 64;
     for (int i = tid; i < n_chunks * E; i += 1024) masks[i] = 0ull;
+    if constexpr (TAIL) {
+        for (int e = tid; e < E; e += 1024) keep_s[e] = 0;
+        __syncthreads();
+        mark_kept(ids, T, k, tail_from, keep_s, tid, 1024);
+    }
     __syncthreads();
-    for (int c = wv; c < n_chunks; c += 16) build_chunk_masks(ids, T, k, c, masks + (size_t)c * E);
+    for (int c = wv; c < n_chunks; c += 16) build_chunk_masks(ids, T, k, c, masks + (size_t)c * E, keep);
     __syncthreads();
     // per expert: prefix over chunks
+    int run = 0;
     if (tid < E) {
-        int run = 0;
         for (int c = 0; c < n_chunks; ++c) {
             cbase[c * E + tid] = run;
             run += __popcll(masks[c * E + tid]);
@@ -102,24 +138,30 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t *__r
         offsets[tid] = tot[tid];
         for (int c = 0; c < n_chunks; ++c) cbase[c * E + tid] += tot[tid];
     }
-    if (tid == 0) offsets[E] = T * k;
+    if (tid == E - 1) offsets[E] = tot[tid] + run;   // all (kept) pairs
     __syncthreads();
     for (int c = wv; c < n_chunks; c += 16)
         write_chunk_positions(ids, T, k, c, masks + (size_t)c * E, cbase + (size_t)c * E,
-                              sorted_pair, pair_pos);
+                              sorted_pair, pair_pos, keep);
+}
+
+// large batches, tail-skip: keep flags in the workspace (zeroed just before)
+__global__ __launch_bounds__(256) void dispatch_keep_kernel(const int32_t *__restrict__ ids, int T, int k,
+                                                            int tail_from, int32_t *__restrict__ keep) {
+    mark_kept(ids, T, k, tail_from, keep, blockIdx.x * 256 + threadIdx.x, gridDim.x * 256);
 }
 
 // ----------------------------------------------------------- three passes
 // 1. count: cnt[c][e] = pairs of expert e in chunk c (chunk-major, so a wave's
 //    64 lanes touch 64 consecutive experts).
 __global__ __launch_bounds__(64) void dispatch_count_kernel(const int32_t *__restrict__ ids, int T,
-                                                            int E, int k,
+                                                            int E, int k, const int32_t *keep,
                                                             int32_t *__restrict__ cnt) {
     __shared__ unsigned long long masks[1024];
     const int c = blockIdx.x;
     for (int i = threadIdx.x; i < E; i += 64) masks[i] = 0ull;
     __syncthreads();
-    build_chunk_masks(ids, T, k, c, masks);
+    build_chunk_masks(ids, T, k, c, masks, keep);
     __syncthreads();
     for (int i = threadIdx.x; i < E; i += 64) cnt[(size_t)c * E + i] = __popcll(masks[i]);
 }
@@ -183,7 +225,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t *__restrict
 //    lane sums a run of up to 16 experts, then a wave scan), written out by
 //    chunk 0; position = offsets[e] + cnt[c][e] + earlier lanes of the chunk.
 __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *__restrict__ ids, int T,
-                                                            int E, int k,
+                                                            int E, int k, const int32_t *keep,
                                                             const int32_t *__restrict__ cnt,
                                                             const int32_t *__restrict__ tot,
                                                             int32_t *__restrict__ offsets,
@@ -216,15 +258,19 @@ __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *__res
     }
     if (c == 0 && lane == 63) offsets[E] = run;
     __syncthreads();
-    build_chunk_masks(ids, T, k, c, masks);
+    build_chunk_masks(ids, T, k, c, masks, keep);
     __syncthreads();
     const int t = c * 64 + lane;
     if (t >= T) return;
     const unsigned long long lt = below_mask(lane);
     for (int j = 0; j < k; ++j) {
         const int e = ids[(size_t)t * k + j];
-        const int pos = off[e] + cnt[(size_t)c * E + e] + __popcll(masks[e] & lt);
         const int p = t * k + j;
+        if (keep && !keep[e]) {
+            pair_pos[p] = -1;
+            continue;
+        }
+        const int pos = off[e] + cnt[(size_t)c * E + e] + __popcll(masks[e] & lt);
         sorted_pair[pos] = p;
         pair_pos[p] = pos;
     }
@@ -234,27 +280,42 @@ static bool dispatch_fits_small(int E, int T) {
     return (size_t)((T + 63) / 64) * E <= (size_t)kSmallMaskEntries;
 }
 
-// cnt [n_chunks][E], then tot [E]
+// cnt [n_chunks][E], then tot [E], then the tail-skip keep flags [E]
 size_t dispatch_ws_bytes(int E, int T, int k) {
     (void)k;
     if (dispatch_fits_small(E, T)) return 0;
-    return ((size_t)((T + 63) / 64) * E + E) * sizeof(int32_t);
+    return ((size_t)((T + 63) / 64) * E + 2 * (size_t)E) * sizeof(int32_t);
 }
 
-hipError_t launch_dispatch(const int32_t *ids, int T, int E, int k, int32_t *offsets,
+hipError_t launch_dispatch(const int32_t *ids, int T, int E, int k, int tail_from, int32_t *offsets,
                            int32_t *sorted_pair, int32_t *pair_pos, void *ws, hipStream_t s) {
+    const bool tail = tail_from < k;
     if (dispatch_fits_small(E, T)) {
-        hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, s, ids, T, E, k, offsets,
-                           sorted_pair, pair_pos);
+        if (tail)
+            hipLaunchKernelGGL(dispatch_small_kernel<true>, dim3(1), dim3(1024), 0, s, ids, T, E, k,
+                               tail_from, offsets, sorted_pair, pair_pos);
+        else
+            hipLaunchKernelGGL(dispatch_small_kernel<false>, dim3(1), dim3(1024), 0, s, ids, T, E, k,
+                               tail_from, offsets, sorted_pair, pair_pos);
         return hipGetLastError();
     }
     const int n_chunks = (T + 63) / 64;
     int32_t *cnt = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + kWsHeader);
     int32_t *tot = cnt + (size_t)n_chunks * E;
-    hipLaunchKernelGGL(dispatch_count_kernel, dim3(n_chunks), dim3(64), 0, s, ids, T, E, k, cnt);
+    int32_t *keep = nullptr;
+    if (tail) {
+        keep = tot + E;
+        hipError_t e = launch_fill_zero(keep, (size_t)E * sizeof(int32_t), s);
+        if (e != hipSuccess) return e;
+        const int n = T * (tail_from > 0 ? tail_from : 1);
+        int blocks = (n + 255) / 256;
+        blocks = blocks < 1024 ? blocks : 1024;
+        hipLaunchKernelGGL(dispatch_keep_kernel, dim3(blocks), dim3(256), 0, s, ids, T, k, tail_from, keep);
+    }
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(n_chunks), dim3(64), 0, s, ids, T, E, k, keep, cnt);
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3((E + 63) / 64), dim3(1024), 0, s, cnt, n_chunks, E,
                        tot);
-    hipLaunchKernelGGL(dispatch_place_kernel, dim3(n_chunks), dim3(64), 0, s, ids, T, E, k, cnt, tot,
+    hipLaunchKernelGGL(dispatch_place_kernel, dim3(n_chunks), dim3(64), 0, s, ids, T, E, k, keep, cnt, tot,
                        offsets, sorted_pair, pair_pos);
     return hipGetLastError();
 }

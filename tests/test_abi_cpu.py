@@ -64,6 +64,12 @@ def test_dispatch_and_combine_validation(q):
     assert d(A, 4, 16, 0, A, A, A, A, 1 << 20) == q.MOE_ERR_INVALID_ARGUMENT
     assert d(A, 4, 16, 2, A, A, A, None, 0) == q.MOE_ERR_WORKSPACE
     assert d(A, 0, 16, 2, A, A, A, A, 1 << 20) == q.MOE_OK
+    ts = lambda *a: q.moe_dispatch_tail_skip(*a, check=False)
+    assert ts(A, 4, 16, 2, -1, A, A, A, A, 1 << 20) == q.MOE_ERR_INVALID_ARGUMENT   # tail_from < 0
+    assert ts(A, 4, 16, 2, 3, A, A, A, A, 1 << 20) == q.MOE_ERR_INVALID_ARGUMENT    # tail_from > k
+    assert ts(None, 4, 16, 2, 1, A, A, A, A, 1 << 20) == q.MOE_ERR_INVALID_ARGUMENT
+    assert ts(A, 4, 16, 2, 1, A, A, A, None, 0) == q.MOE_ERR_WORKSPACE
+    assert ts(A, 0, 16, 2, 2, A, A, A, A, 1 << 20) == q.MOE_OK
     c = lambda *a: q.moe_combine(*a, check=False)
     assert c(A, A, A, A, 3, 2, 2048, None) == q.MOE_ERR_INVALID_ARGUMENT
     assert c(A, A, A, A, 3, 2, 100, A) == q.MOE_ERR_UNSUPPORTED
