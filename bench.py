@@ -19,6 +19,10 @@ Workloads (default 1):
                                                Zipf(1.3) router bias
   5, 6  the "coder" variant (E=256 routed experts): decode T=1 as 1, prefill
         T=8192 as 3
+--tail-skip RANK times the lossy route tail-skip variant (moe_dispatch_tail_skip)
+and reports the pairs kept and the output's deviation from the full layer;
+--tokens T overrides the workload's batch size.
+
 Decode workloads report the expert FFN call against HBM bandwidth (bytes of
 the distinct experts selected + activations); prefill workloads against the
 dense fp16/bf16 matrix-core peak (2*M*N*K of the expert GEMMs).
@@ -107,6 +111,9 @@ def main():
     ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--tokens", type=int, default=None,
                     help="override the workload's T (tokens per layer), e.g. the mid-size batches")
+    ap.add_argument("--tail-skip", type=int, default=None, metavar="RANK",
+                    help="route tail-skip: experts the batch picked only at 0-based ranks >= RANK "
+                         "are not computed (the pages' rule: 6 for a top-10); lossy, opt-in")
     ap.add_argument("--copies", type=int, default=None,
                     help="layer copies cycled, single-layer workloads (default 16 decode, 1 prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -195,24 +202,63 @@ def main():
     # evaluates them one by one from the GPU's logits).  ids and the
     # permutation are checked in full either way.
     import oracle
-    run_layer(layer_of(0, 0), xs[0][0], buf, stream=sh)
+    tf = args.tail_skip
+    if tf is not None and not 0 <= tf <= w.k:
+        log(f"--tail-skip must lie in [0, {w.k}]")
+        sys.exit(2)
+    run_layer(layer_of(0, 0), xs[0][0], buf, stream=sh, tail_from=tf)
     hip.stream_synchronize(sh)
     x0 = xs[0][0].cpu().numpy().view(np.uint16)
     lg = buf.logits[:w.T].cpu().numpy()
     ids_ref, _ = oracle.topk_softmax(lg, w.k)
-    off_ref, sp_ref, _ = oracle.dispatch(ids_ref, w.n_experts)
+    if tf is None:
+        off_ref, sp_ref, _ = oracle.dispatch(ids_ref, w.n_experts)
+    else:
+        off_ref, sp_ref, _ = oracle.dispatch_tail_skip(ids_ref, w.n_experts, tf)
+    n_kept = int(off_ref[w.n_experts])
     ids_ok = bool(np.array_equal(buf.ids[:w.T].cpu().numpy(), ids_ref)
                   and np.array_equal(buf.offsets.cpu().numpy(), off_ref)
-                  and np.array_equal(buf.sorted_pair[:w.T * w.k].cpu().numpy(), sp_ref))
+                  and np.array_equal(buf.sorted_pair[:n_kept].cpu().numpy(), sp_ref[:n_kept]))
     rows = (np.sort(np.random.default_rng(7).choice(w.T, size=16, replace=False))
             if prefill else np.arange(w.T))
-    _, _, out_ref = oracle.layer(host_layer, w.fmt, w.d_model, w.d_ff, w.n_experts, w.k,
-                                 x0[rows], logits=lg[rows])
+    if tf is None:
+        _, _, out_ref = oracle.layer(host_layer, w.fmt, w.d_model, w.d_ff, w.n_experts, w.k,
+                                     x0[rows], logits=lg[rows])
+    else:
+        # the kept set belongs to the whole batch: the sampled tokens' output
+        # from their kept rows
+        keep = oracle.tail_keep(ids_ref, w.n_experts, tf)
+        idr = ids_ref[rows]
+        re = np.concatenate([idr.ravel(), -np.ones(len(rows), np.int32)]).astype(np.int32)
+        rt = np.concatenate([np.repeat(rows, w.k), rows]).astype(np.int32)
+        yr = oracle.expert_rows(host_layer, w.fmt, w.d_model, w.d_ff, w.n_experts, x0, re, rt, f64=True)
+        wk = buf.w[:w.T].cpu().numpy()[rows].astype(np.float64) * keep[idr]
+        out_ref = yr[len(rows) * w.k:] + np.einsum(
+            "tj,tjd->td", wk, yr[:len(rows) * w.k].reshape(len(rows), w.k, w.d_model))
     rms = float(np.sqrt(np.mean(out_ref.astype(np.float64) ** 2)))
     err = float(np.max(np.abs(buf.out[:w.T].cpu().numpy()[rows].astype(np.float64) - out_ref))
                 / rms)
     log(f"parity step 0 ({len(rows)} tokens): ids/permutation exact={ids_ok} "
         f"max|err|/rms={err:.3e}")
+
+    # deviation of the lossy tail-skip layer from the full layer (same input)
+    tail_info = None
+    if tf is not None:
+        out_skip = buf.out[:w.T].clone()
+        run_layer(layer_of(0, 0), xs[0][0], buf, stream=sh)
+        hip.stream_synchronize(sh)
+        full = buf.out[:w.T].double()
+        dev = float((out_skip.double() - full).abs().max() / full.pow(2).mean().sqrt())
+        tail_info = {"tail_from": tf, "pairs": w.T * w.k, "kept_pairs_step0": n_kept,
+                     "max_dev_from_full_layer_over_rms": dev}
+
+    def dispatch():
+        if tf is None:
+            q.moe_dispatch(buf.ids, w.T, w.n_experts, w.k, buf.offsets, buf.sorted_pair,
+                           buf.pair_pos, buf.ws, buf.ws_bytes, sh)
+        else:
+            q.moe_dispatch_tail_skip(buf.ids, w.T, w.n_experts, w.k, tf, buf.offsets,
+                                     buf.sorted_pair, buf.pair_pos, buf.ws, buf.ws_bytes, sh)
 
     # ------------------------------------------------------------ capture
     ev_start, ev_end = hip.Event(), hip.Event()
@@ -224,8 +270,7 @@ def main():
             q.moe_route(x, L.router, L.bias, buf.logits, w.T, w.d_model, w.n_experts, w.k,
                         buf.ids, buf.w, buf.ws, buf.ws_bytes, sh)
         elif c == "dispatch":
-            q.moe_dispatch(buf.ids, w.T, w.n_experts, w.k, buf.offsets, buf.sorted_pair,
-                           buf.pair_pos, buf.ws, buf.ws_bytes, sh)
+            dispatch()
         elif c == "expert_ffn":
             q.moe_expert_ffn(L.struct, x, w.T, w.k, buf.offsets, buf.sorted_pair, buf.y_pairs,
                              buf.y_shared, buf.ws, buf.ws_bytes, sh)
@@ -302,8 +347,7 @@ def main():
             L = layer_of(s, li)
             q.moe_route(xs[s][li], L.router, L.bias, buf.logits, w.T, w.d_model, w.n_experts,
                         w.k, buf.ids, buf.w, buf.ws, buf.ws_bytes, sh)
-            q.moe_dispatch(buf.ids, w.T, w.n_experts, w.k, buf.offsets, buf.sorted_pair,
-                           buf.pair_pos, buf.ws, buf.ws_bytes, sh)
+            dispatch()
             hip.stream_synchronize(sh)
             off = buf.offsets.cpu().numpy()
             groups.append(int(np.count_nonzero(np.diff(off))) + 1)
@@ -368,7 +412,8 @@ def main():
                    "n_experts": w.n_experts, "top_k": w.k, "shared_experts": 1, "T": w.T,
                    "layers": n_lay, "format": "Q2_B32" if w.fmt == 1 else "Q3_B32",
                    "layer_copies": len(layers) if n_lay == 1 else 1,
-                   "mode": "eager" if args.eager else "hip-graph"},
+                   "mode": "eager" if args.eager else "hip-graph",
+                   **({} if tf is None else {"route_tail_skip_from": tf})},
         "roofline": roof,
         "cpu_baseline": cpu,
         "gpu_ms_per_step": gpu_ms / K,
@@ -378,6 +423,7 @@ def main():
             (layer_bytes * n_lay / (gpu_ms / K * 1e-3) / 1e9 / HBM_PEAK_GBS),
         "parity": {"ids_exact": ids_ok, "max_err_over_rms": err, "tokens_checked": int(len(rows)),
                    "graph_replay_bitwise": replay_ok},
+        **({} if tail_info is None else {"tail_skip": tail_info}),
     }
     print(json.dumps(res))
     if not (ids_ok and err <= 2e-3 and replay_ok):

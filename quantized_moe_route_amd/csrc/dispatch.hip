@@ -27,10 +27,13 @@ __device__ __forceinline__ unsigned long long below_mask(int lane) {
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// one wave: OR each token's bit into masks[e] for its k experts (kept ones)
+// one wave: OR each token's bit into masks[e] for its k experts (kept ones,
+// if keep is given); with mark given, also flag mark[e] for the experts
+// picked at a rank below tail_from
 __device__ __forceinline__ void build_chunk_masks(const int32_t *__restrict__ ids, int T, int k,
                                                   int chunk, unsigned long long *masks,
-                                                  const int32_t *keep) {
+                                                  const int32_t *keep, int32_t *mark = nullptr,
+                                                  int tail_from = 0) {
     const int lane = __lane_id();
     const int t = chunk * 64 + lane;
     if (t < T) {
@@ -38,6 +41,7 @@ __device__ __forceinline__ void build_chunk_masks(const int32_t *__restrict__ id
         for (int j = 0; j < k; ++j) {
             const int e = ids[(size_t)t * k + j];
             if (!keep || keep[e]) atomicOr(&masks[e], bit);
+            if (mark && j < tail_from) mark[e] = 1;
         }
     }
 }
@@ -114,20 +118,20 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t *__r
     const int wv = tid >> 6;
     const int n_chunks = (T + 63) / 64;
     for (int i = tid; i < n_chunks * E; i += 1024) masks[i] = 0ull;
-    if constexpr (TAIL) {
+    if constexpr (TAIL)
         for (int e = tid; e < E; e += 1024) keep_s[e] = 0;
-        __syncthreads();
-        mark_kept(ids, T, k, tail_from, keep_s, tid, 1024);
-    }
     __syncthreads();
-    for (int c = wv; c < n_chunks; c += 16) build_chunk_masks(ids, T, k, c, masks + (size_t)c * E, keep);
+    // masks of every pair; with tail-skip the same pass flags the kept experts
+    for (int c = wv; c < n_chunks; c += 16)
+        build_chunk_masks(ids, T, k, c, masks + (size_t)c * E, nullptr, TAIL ? keep_s : nullptr, tail_from);
     __syncthreads();
-    // per expert: prefix over chunks
+    // per expert: prefix over chunks (a dropped expert counts no pairs)
     int run = 0;
     if (tid < E) {
+        const bool kept = !TAIL || keep_s[tid];
         for (int c = 0; c < n_chunks; ++c) {
             cbase[c * E + tid] = run;
-            run += __popcll(masks[c * E + tid]);
+            run += kept ? __popcll(masks[c * E + tid]) : 0;
         }
         tot[tid] = run;
     }
