@@ -2,8 +2,10 @@
 """MoE-layer throughput on one MI355X: routed, block-quantized experts.
 
 A step is one pass of the whole layer path over one batch of synthetic input:
-moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine (for the 48-layer
-workloads: all 48 layers in sequence).  Inputs are resident in HBM before the
+moe_route_dispatch (moe_route + moe_dispatch; one launch for batches of up to
+8 tokens) -> moe_expert_ffn -> moe_combine, or with --separate-calls the four
+calls moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine (for the
+48-layer workloads: all 48 layers in sequence).  Inputs are resident in HBM before the
 timed region.  The K timed steps (and the W warm-up steps) are captured into
 one HIP graph each and replayed once, bracketed by stream synchronisation and
 HIP events on the launch stream.  Per-call GPU durations come from one more
@@ -114,6 +116,8 @@ def main():
     ap.add_argument("--tail-skip", type=int, default=None, metavar="RANK",
                     help="route tail-skip: experts the batch picked only at 0-based ranks >= RANK "
                          "are not computed (the pages' rule: 6 for a top-10); lossy, opt-in")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="time moe_route and moe_dispatch as two calls (default: moe_route_dispatch)")
     ap.add_argument("--copies", type=int, default=None,
                     help="layer copies cycled, single-layer workloads (default 16 decode, 1 prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -206,7 +210,8 @@ def main():
     if tf is not None and not 0 <= tf <= w.k:
         log(f"--tail-skip must lie in [0, {w.k}]")
         sys.exit(2)
-    run_layer(layer_of(0, 0), xs[0][0], buf, stream=sh, tail_from=tf)
+    fused = not args.separate_calls and tf is None
+    run_layer(layer_of(0, 0), xs[0][0], buf, stream=sh, tail_from=tf, fused=fused)
     hip.stream_synchronize(sh)
     x0 = xs[0][0].cpu().numpy().view(np.uint16)
     lg = buf.logits[:w.T].cpu().numpy()
@@ -266,7 +271,11 @@ def main():
     def call(c, s, li):
         L = layer_of(s, li)
         x = xs[s][li]
-        if c == "route":
+        if c == "route_dispatch":
+            q.moe_route_dispatch(x, L.router, L.bias, buf.logits, w.T, w.d_model, w.n_experts, w.k,
+                                 buf.ids, buf.w, buf.offsets, buf.sorted_pair, buf.pair_pos, buf.ws,
+                                 buf.ws_bytes, sh)
+        elif c == "route":
             q.moe_route(x, L.router, L.bias, buf.logits, w.T, w.d_model, w.n_experts, w.k,
                         buf.ids, buf.w, buf.ws, buf.ws_bytes, sh)
         elif c == "dispatch":
@@ -278,7 +287,7 @@ def main():
             q.moe_combine(buf.y_pairs, buf.y_shared, buf.pair_pos, buf.w, w.T, w.k, w.d_model,
                           buf.out, sh)
 
-    calls = ["route", "dispatch", "expert_ffn", "combine"]
+    calls = (["route_dispatch"] if fused else ["route", "dispatch"]) + ["expert_ffn", "combine"]
 
     def enqueue(step0, nsteps):
         for s in range(step0, step0 + nsteps):
@@ -413,6 +422,7 @@ def main():
                    "layers": n_lay, "format": "Q2_B32" if w.fmt == 1 else "Q3_B32",
                    "layer_copies": len(layers) if n_lay == 1 else 1,
                    "mode": "eager" if args.eager else "hip-graph",
+                   "calls": calls,
                    **({} if tf is None else {"route_tail_skip_from": tf})},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -177,6 +177,24 @@ moe_status moe_dispatch_tail_skip(const int32_t *topk_ids, int32_t T, int32_t E,
                                   int32_t *pair_pos, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_route_dispatch -- moe_route followed by moe_dispatch, in one launch
+ * where the batch allows it.  [forum] "Strata의 동작 원리": per layer the
+ * router's picks go straight on to the split among executors; a decode layer
+ * is a chain of small steps, so each launch saved is time saved per layer.
+ *
+ * Writes exactly what moe_route then moe_dispatch (same arguments) write:
+ * logits, topk_ids, topk_w, offsets, sorted_pair, pair_pos.  w_router and
+ * x_bf16 must be given (no logits input).  With T <= 8 and k <= 64 one kernel
+ * does both; otherwise the two calls are enqueued in turn.  ws must suffice
+ * for both (moe_workspace_size does).  Errors: those of the two calls,
+ * checked before anything is enqueued.
+ */
+moe_status moe_route_dispatch(const uint16_t *x_bf16, const float *w_router, const float *bias,
+                              float *logits, int32_t T, int32_t d_model, int32_t E, int32_t k,
+                              int32_t *topk_ids, float *topk_w, int32_t *offsets, int32_t *sorted_pair,
+                              int32_t *pair_pos, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * moe_expert_ffn -- the selected experts and the shared expert.
  * [forum] "Strata의 동작 원리" and [guide] "Strata, Qwen, GSQ-RCO…": 10 routed
  * experts plus one shared expert per token per layer; [video] "픽업": the

@@ -256,13 +256,17 @@ __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + _
 
 // ---------------------------------------------------------------- launchers
 // (defined in the .hip files; return hipError_t of the launch)
+// offsets, sorted_pair, pair_pos (all or none): also list the pairs by expert
+// (T <= kRouteTile and k <= 64 only)
 hipError_t launch_route_small(const uint16_t *x, const float *wr, const float *bias, float *logits,
                               int T, int d, int E, int k, int32_t *ids, float *w, void *ws,
-                              hipStream_t s);
+                              hipStream_t s, int32_t *offsets = nullptr, int32_t *sorted_pair = nullptr,
+                              int32_t *pair_pos = nullptr);
 hipError_t launch_router_gemm(const uint16_t *x, const float *wr, const float *bias, float *logits,
                               int T, int d, int E, void *ws, hipStream_t s);
 size_t router_gemm_ws_bytes(int d, int E);
 constexpr int kRouteSmallTMax = 128;   // T above this: router GEMM + top-k kernel
+constexpr int kWaveTopkMaxK = 64;      // register top-k (one wave per token) up to this k
 static_assert(kRouteSmallTMax / kRouteTile * kCntLine * 4 <= (int)kWsHeader, "tile counters exceed the header");
 hipError_t launch_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w,
                        hipStream_t s);

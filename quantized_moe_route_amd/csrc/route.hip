@@ -228,7 +228,7 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 
 template <int PER>
 __device__ void wave_topk_ord(const float *__restrict__ lg, int E, int k, int32_t *__restrict__ ids,
-                              float *__restrict__ w) {
+                              float *__restrict__ w, int32_t *ids_lds = nullptr) {
     const int l = __lane_id();
     uint32_t key[PER];
 #pragma unroll
@@ -287,22 +287,23 @@ __device__ void wave_topk_ord(const float *__restrict__ lg, int E, int k, int32_
     if (l < k) {
         w[l] = ev * inv;
         ids[l] = my_id;
+        if (ids_lds) ids_lds[l] = my_id;
     }
 }
 
-constexpr int kWaveTopkMaxK = 64;   // register top-k up to this k
 
-__device__ __forceinline__ void wave_topk_ord_any(const float *lg, int E, int k, int32_t *ids, float *w) {
+__device__ __forceinline__ void wave_topk_ord_any(const float *lg, int E, int k, int32_t *ids, float *w,
+                                                  int32_t *ids_lds = nullptr) {
     if (E <= 64)
-        wave_topk_ord<1>(lg, E, k, ids, w);
+        wave_topk_ord<1>(lg, E, k, ids, w, ids_lds);
     else if (E <= 128)
-        wave_topk_ord<2>(lg, E, k, ids, w);
+        wave_topk_ord<2>(lg, E, k, ids, w, ids_lds);
     else if (E <= 256)
-        wave_topk_ord<4>(lg, E, k, ids, w);
+        wave_topk_ord<4>(lg, E, k, ids, w, ids_lds);
     else if (E <= 512)
-        wave_topk_ord<8>(lg, E, k, ids, w);
+        wave_topk_ord<8>(lg, E, k, ids, w, ids_lds);
     else
-        wave_topk_ord<16>(lg, E, k, ids, w);
+        wave_topk_ord<16>(lg, E, k, ids, w, ids_lds);
 }
 
 // ------------------------------------------------------- small T: one launch
@@ -314,11 +315,16 @@ __device__ __forceinline__ void wave_topk_ord_any(const float *lg, int E, int k,
 // runs the top-k from LDS.  Tiles are independent (a counter line each).
 constexpr int kMaxSmallT = kRouteTile;
 
+// With offsets given (a batch of one tile, k <= 64), the last workgroup also
+// lists the pairs by expert, as moe_dispatch does, from the ids it has just
+// picked: one launch instead of two.
 __global__ __launch_bounds__(512) void route_small_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
     float *__restrict__ logits, int T, int d, int E, int k, int32_t *__restrict__ ids,
-    float *__restrict__ w, int32_t *__restrict__ counters, float *__restrict__ partial) {
+    float *__restrict__ w, int32_t *__restrict__ counters, float *__restrict__ partial,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pair_pos) {
     __shared__ float red[8][kMaxSmallT][64];
+    __shared__ int32_t sel_ids[kMaxSmallT * kWaveTopkMaxK];   // the batch's picks, for the listing
     // one LDS pool: the logits [T][E] for the register top-k (k <= 64), or
     // the serial top-k's per-wave scratch (k > 64)
     constexpr int kPoolBytes = 2 * 8 * 1024 * 4;
@@ -423,7 +429,29 @@ __global__ __launch_bounds__(512) void route_small_kernel(
     __syncthreads();
     // one wave per token
     if (k <= kWaveTopkMaxK) {
-        for (int t = wv; t < T; t += 8) wave_topk_ord_any(lgs + t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+        for (int t = wv; t < T; t += 8)
+            wave_topk_ord_any(lgs + t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k,
+                              offsets ? sel_ids + t * k : nullptr);
+        if (!offsets) return;
+        // pair p = t k + j goes to position (pairs with a lower expert) +
+        // (earlier pairs with the same expert): a stable sort by expert
+        __syncthreads();
+        const int P = T * k;
+        for (int e = tid; e <= E; e += 512) {
+            int c = 0;
+            for (int q = 0; q < P; ++q) c += sel_ids[q] < e;
+            offsets[e] = c;
+        }
+        if (tid < P) {
+            const int e = sel_ids[tid];
+            int pos = 0;
+            for (int q = 0; q < P; ++q) {
+                const int eq = sel_ids[q];
+                pos += (eq < e) | ((eq == e) & (q < tid));
+            }
+            sorted_pair[pos] = tid;
+            pair_pos[tid] = pos;
+        }
         return;
     }
     // large k: serial selection per token from the logits just written
@@ -440,12 +468,12 @@ size_t route_ws_bytes(int d, int E, int T) {
 
 hipError_t launch_route_small(const uint16_t *x, const float *wr, const float *bias, float *logits,
                               int T, int d, int E, int k, int32_t *ids, float *w, void *ws,
-                              hipStream_t s) {
+                              hipStream_t s, int32_t *offsets, int32_t *sorted_pair, int32_t *pair_pos) {
     int32_t *counters = reinterpret_cast<int32_t *>(ws);
     float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + kWsHeader);
     dim3 grid((E + 63) / 64, d / 128, (T + kRouteTile - 1) / kRouteTile);
     hipLaunchKernelGGL(route_small_kernel, grid, dim3(512), 0, s, x, wr, bias, logits, T, d, E, k,
-                       ids, w, counters, partial);
+                       ids, w, counters, partial, offsets, sorted_pair, pair_pos);
     return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@ import dataclasses
 import torch
 
 from . import (MOE_FMT_Q2_B32, make_layer, moe_combine, moe_dispatch, moe_dispatch_tail_skip,
-               moe_expert_ffn, moe_route, moe_workspace_init, moe_workspace_size)
+               moe_expert_ffn, moe_route, moe_route_dispatch, moe_workspace_init, moe_workspace_size)
 
 MATS = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
 
@@ -87,18 +87,26 @@ def alloc_buffers(layer: DeviceLayer, T: int, k: int, device="cuda", stream=None
     return b
 
 
-def run_layer(layer: DeviceLayer, x, b: Buffers, stream=None, logits_in=False, tail_from=None):
+def run_layer(layer: DeviceLayer, x, b: Buffers, stream=None, logits_in=False, tail_from=None,
+              fused=False):
     """x: [T][d] bf16 (or int16 bits) device tensor.  Runs route -> dispatch ->
     expert FFN -> combine; returns b.out.  tail_from (< k) switches on route
-    tail-skip in the dispatch step."""
+    tail-skip in the dispatch step; fused uses moe_route_dispatch for the
+    first two steps."""
     T, k = b.T, b.k
     d, E = layer.d_model, layer.n_experts
-    if logits_in:
+    if fused:
+        assert not logits_in and tail_from is None
+        moe_route_dispatch(x, layer.router, layer.bias, b.logits, T, d, E, k, b.ids, b.w, b.offsets,
+                           b.sorted_pair, b.pair_pos, b.ws, b.ws_bytes, stream)
+    elif logits_in:
         moe_route(None, None, None, b.logits, T, d, E, k, b.ids, b.w, b.ws, b.ws_bytes, stream)
     else:
         moe_route(x, layer.router, layer.bias, b.logits, T, d, E, k, b.ids, b.w, b.ws, b.ws_bytes,
                   stream)
-    if tail_from is None:
+    if fused:
+        pass
+    elif tail_from is None:
         moe_dispatch(b.ids, T, E, k, b.offsets, b.sorted_pair, b.pair_pos, b.ws, b.ws_bytes, stream)
     else:
         moe_dispatch_tail_skip(b.ids, T, E, k, tail_from, b.offsets, b.sorted_pair, b.pair_pos, b.ws,

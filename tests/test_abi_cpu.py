@@ -70,6 +70,12 @@ def test_dispatch_and_combine_validation(q):
     assert ts(None, 4, 16, 2, 1, A, A, A, A, 1 << 20) == q.MOE_ERR_INVALID_ARGUMENT
     assert ts(A, 4, 16, 2, 1, A, A, A, None, 0) == q.MOE_ERR_WORKSPACE
     assert ts(A, 0, 16, 2, 2, A, A, A, A, 1 << 20) == q.MOE_OK
+    rd = lambda *a: q.moe_route_dispatch(*a, check=False)
+    assert rd(A, None, None, A, 1, 2048, 16, 2, A, A, A, A, A, A, 1 << 24) == q.MOE_ERR_INVALID_ARGUMENT
+    assert rd(A, A, None, A, 1, 2048, 16, 2, A, A, None, A, A, A, 1 << 24) == q.MOE_ERR_INVALID_ARGUMENT
+    assert rd(A, A, None, A, 1, 100, 16, 2, A, A, A, A, A, A, 1 << 24) == q.MOE_ERR_UNSUPPORTED
+    assert rd(A, A, None, A, 1, 2048, 16, 2, A, A, A, A, A, A, 4096) == q.MOE_ERR_WORKSPACE
+    assert rd(A, A, None, A, 0, 2048, 16, 2, A, A, A, A, A, A, 1 << 24) == q.MOE_OK
     c = lambda *a: q.moe_combine(*a, check=False)
     assert c(A, A, A, A, 3, 2, 2048, None) == q.MOE_ERR_INVALID_ARGUMENT
     assert c(A, A, A, A, 3, 2, 100, A) == q.MOE_ERR_UNSUPPORTED

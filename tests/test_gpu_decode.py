@@ -349,3 +349,53 @@ def test_graph_replay_matches_eager(q):
         g.launch()
         hip.stream_synchronize(stream.cuda_stream)
         assert torch.equal(b.out, be.out) and torch.equal(b.ids, be.ids), rep
+
+
+@pytest.mark.parametrize("T,E,k,d", [(1, 512, 10, 2048), (4, 512, 10, 2048), (8, 1024, 64, 256),
+                                     (3, 16, 2, 128), (9, 512, 10, 256), (5, 300, 70, 128)])
+def test_route_dispatch_equals_separate_calls(q, T, E, k, d):
+    """moe_route_dispatch writes what moe_route then moe_dispatch write, bit
+    for bit: one launch for one tile (T <= 8, k <= 64), the two calls
+    otherwise (T = 9; k = 70)."""
+    rng = np.random.default_rng(T * 11 + E + k)
+    x = torch.from_numpy(synth._f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+                         .view(np.int16)).cuda()
+    wr = torch.from_numpy((rng.standard_normal((d, E)) / np.sqrt(d)).astype(np.float32)).cuda()
+    bias = torch.from_numpy(rng.standard_normal(E).astype(np.float32)).cuda()
+    ws_bytes = q.moe_workspace_size(d, 128, E, T, k)
+    outs = []
+    for fused in (False, True):
+        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+        lg = torch.full((T, E), -5.0, device="cuda")
+        ids = torch.full((T, k), -5, dtype=torch.int32, device="cuda")
+        wt = torch.full((T, k), -5.0, device="cuda")
+        off = torch.full((E + 1,), -5, dtype=torch.int32, device="cuda")
+        sp = torch.full((T * k,), -5, dtype=torch.int32, device="cuda")
+        pp = torch.full((T * k,), -5, dtype=torch.int32, device="cuda")
+        for rep in range(2):   # the second call checks the arrival counter is back at zero
+            if fused:
+                q.moe_route_dispatch(x, wr, bias, lg, T, d, E, k, ids, wt, off, sp, pp, ws, ws_bytes)
+            else:
+                q.moe_route(x, wr, bias, lg, T, d, E, k, ids, wt, ws, ws_bytes)
+                q.moe_dispatch(ids, T, E, k, off, sp, pp, ws, ws_bytes)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws[:4096])) == 0
+        outs.append([t.cpu().numpy() for t in (lg, ids, wt, off, sp, pp)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    off_ref, sp_ref, pp_ref = oracle.dispatch(outs[1][1], E)
+    assert np.array_equal(outs[1][3], off_ref) and np.array_equal(outs[1][4], sp_ref)
+    assert np.array_equal(outs[1][5], pp_ref)
+
+
+@pytest.mark.parametrize("wid", [1, 2])
+def test_workload_layer_parity_fused_route_dispatch(q, wid):
+    w = synth.WORKLOADS[wid]
+    L = synth.gen_layer(w, layer=0)
+    x = synth.gen_x(w, layer=0)
+    from quantized_moe_route_amd.layer import alloc_buffers, run_layer
+    dl = _upload(L, w)
+    b = alloc_buffers(dl, w.T, w.k)
+    run_layer(dl, _x_dev(x), b, fused=True)
+    torch.cuda.synchronize()
+    _check_layer(q, w, L, x, b)
