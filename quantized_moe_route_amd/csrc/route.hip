@@ -325,6 +325,9 @@ __global__ __launch_bounds__(512) void route_small_kernel(
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pair_pos) {
     __shared__ float red[8][kMaxSmallT][64];
     __shared__ int32_t sel_ids[kMaxSmallT * kWaveTopkMaxK];   // the batch's picks, for the listing
+    __shared__ uint32_t emask[1024];                          // listing: tokens (bits) per expert
+    __shared__ int32_t eoff[1024];                            // listing: first position per expert
+    __shared__ int32_t wtot[8];
     // one LDS pool: the logits [T][E] for the register top-k (k <= 64), or
     // the serial top-k's per-wave scratch (k > 64)
     constexpr int kPoolBytes = 2 * 8 * 1024 * 4;
@@ -433,22 +436,33 @@ __global__ __launch_bounds__(512) void route_small_kernel(
             wave_topk_ord_any(lgs + t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k,
                               offsets ? sel_ids + t * k : nullptr);
         if (!offsets) return;
-        // pair p = t k + j goes to position (pairs with a lower expert) +
-        // (earlier pairs with the same expert): a stable sort by expert
+        // The listing: a token picks an expert at most once, so the pairs of
+        // expert e are the tokens in emask[e]; pair p = t k + j goes to
+        // (pairs of lower experts) + (tokens before t in emask[e]), the
+        // position a stable sort by expert gives.
+        for (int e = tid; e < 1024; e += 512) emask[e] = 0u;
         __syncthreads();
         const int P = T * k;
-        for (int e = tid; e <= E; e += 512) {
-            int c = 0;
-            for (int q = 0; q < P; ++q) c += sel_ids[q] < e;
-            offsets[e] = c;
-        }
+        if (tid < P) atomicOr(&emask[sel_ids[tid]], 1u << (tid / k));
+        __syncthreads();
+        // exclusive scan of the per-expert counts, two experts per thread
+        const int e0 = 2 * tid;
+        const int c0 = __popc(emask[e0]), c1 = __popc(emask[e0 + 1]);
+        const int incl = wave_incl_scan(c0 + c1);
+        if (__lane_id() == 63) wtot[wv] = incl;
+        __syncthreads();
+        int base = 0;
+        for (int w2 = 0; w2 < wv; ++w2) base += wtot[w2];
+        const int ex = base + incl - (c0 + c1);
+        eoff[e0] = ex;
+        eoff[e0 + 1] = ex + c0;
+        if (e0 < E) offsets[e0] = ex;
+        if (e0 + 1 < E) offsets[e0 + 1] = ex + c0;
+        if (tid == 511) offsets[E] = base + incl;   // all pairs (slots past E count none)
+        __syncthreads();
         if (tid < P) {
-            const int e = sel_ids[tid];
-            int pos = 0;
-            for (int q = 0; q < P; ++q) {
-                const int eq = sel_ids[q];
-                pos += (eq < e) | ((eq == e) & (q < tid));
-            }
+            const int e = sel_ids[tid], t = tid / k;
+            const int pos = eoff[e] + __popc(emask[e] & ((1u << t) - 1u));
             sorted_pair[pos] = tid;
             pair_pos[tid] = pos;
         }
