@@ -21,8 +21,9 @@
 //     X = sum of the block's activations (a matrix-core step against ones).
 //   Weights are therefore used exactly (no rounding of d*q + m), and all sums
 //   are fp32.
-//   - gate/up: A = x rows of the group (bf16, exact); h = silu(g)*u in fp32 is
-//     written as fp16 hi + fp16 lo (22 significant bits).
+//   - gate/up: A = the batch's x rows (bf16, exact; each group row then takes
+//     its token's sums); h = silu(g)*u in fp32 is written as fp16 hi + fp16
+//     lo (22 significant bits).
 //   - down: A stacks the group's h_hi rows over its h_lo rows in one 16-row
 //     tile, so one fp16 matrix-core step covers both halves.
 //   - four waves of a workgroup split K; partial sums meet in LDS in a fixed
@@ -132,18 +133,18 @@ constexpr int kBatch = MOE_DECODE_BATCH;   // units prefetched per wave per batc
 // of the group's rows.  The NW waves of the workgroup split K and meet in LDS
 // (red); wave 0 applies SwiGLU and writes h as fp16 hi + lo.
 //
-// TOKROWS (batches of at most 16 tokens): the 16 matrix rows are the batch's
-// tokens themselves, not the group's rows, so the activation loads depend on
-// nothing and go out with the weights; a group row's token (its pair's entry
-// in sorted_pair) is needed only when wave 0 picks its row out of the sums.
-// Each output row is the same dot product either way.
-template <int FMT, int MT, int IMAX, int NW, bool TOKROWS>
+// The 16 matrix rows are the batch's tokens themselves (T <= 16), not the
+// group's rows, so the activation loads depend on nothing and go out with
+// the weights; a group row's token (its pair's entry in sorted_pair) is
+// needed only when wave 0 picks its row out of the sums.  Each output row is
+// the same dot product either way.
+template <int FMT, int IMAX, int NW>
 __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &up, const QMatDev &sgate,
                                             const QMatDev &sup, const uint16_t *__restrict__ x, int T, int k, int d,
                                             int f, const int32_t *__restrict__ sorted_pair, const Group &grp,
-                                            int nt, float (*red)[MT][2][IMAX][64], uint16_t *__restrict__ h_hi,
+                                            int nt, float (*red)[2][IMAX][64], uint16_t *__restrict__ h_hi,
                                             uint16_t *__restrict__ h_lo) {
-    static_assert(!TOKROWS || (MT == 1 && NW > 1), "token rows: one 16-row tile, K split over waves");
+    static_assert(NW > 1, "token rows: K split over waves");
     const int lane = __lane_id();
     const int wv = wave_uniform(threadIdx.x >> 6);
     const int gq = lane >> 4, rr = lane & 15;
@@ -155,49 +156,28 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
     const size_t ubase = ((size_t)e * (f / 16) + nt) * KC;
     const int nrows = grp.nrows;
 
-    // Token of the lane's A-operand row rr in each M tile.  Lanes past the
-    // group's last row use its last row (their D rows are never stored); the
-    // loads are unconditional so they are in flight together.  The
-    // sorted_pair loads go out first, then the first batch of weights; only
-    // the activation loads wait for the token ids.
-    int tok[MT];
-    int otok[IMAX];   // TOKROWS: token of output row 4 gq + i
-    if constexpr (TOKROWS) {
+    // token of output row 4 gq + i; lanes past the group's last row use its
+    // last row (never stored), so the loads are unconditional and go out
+    // together, before the weights
+    int otok[IMAX];
 #pragma unroll
-        for (int i = 0; i < IMAX; ++i) {
-            int r = 4 * gq + i;
-            r = r < nrows ? r : nrows - 1;
-            otok[i] = shared ? r : sorted_pair[grp.row0 + r];
-        }
-    } else {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            int r = mt * 16 + rr;
-            r = r < nrows ? r : nrows - 1;
-            tok[mt] = shared ? r : sorted_pair[grp.row0 + r];
-        }
+    for (int i = 0; i < IMAX; ++i) {
+        int r = 4 * gq + i;
+        r = r < nrows ? r : nrows - 1;
+        otok[i] = shared ? r : sorted_pair[grp.row0 + r];
     }
-    f32x4 ag[MT], au[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        ag[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        au[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    const uint16_t *xrow[MT];
+    f32x4 ag[1], au[1];
+    ag[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    au[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t *xrow[1] = {x + (size_t)(rr < T ? rr : T - 1) * d};
     for (int u0 = wv; u0 < KC; u0 += NW * kBatch) {
-        GateUpUnit<FMT, MT> U[kBatch];
+        GateUpUnit<FMT, 1> U[kBatch];
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
             const int u = u0 + NW * b;
             if (u < KC) gateup_load_w(U[b], Wg, Wu, ubase + u, lane, rr);
         }
         __asm__ volatile("" ::: "memory");
-        if constexpr (TOKROWS) {
-            xrow[0] = x + (size_t)(rr < T ? rr : T - 1) * d;
-        } else {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) xrow[mt] = x + (size_t)(shared ? tok[mt] : tok[mt] / k) * d;
-        }
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
             const int u = u0 + NW * b;
@@ -206,84 +186,40 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
             if (u0 + NW * b < KC) {
-                gateup_block<FMT, MT, IMAX, 0>(U[b], ag, au);
-                gateup_block<FMT, MT, IMAX, 1>(U[b], ag, au);
-                gateup_block<FMT, MT, IMAX, 2>(U[b], ag, au);
-                gateup_block<FMT, MT, IMAX, 3>(U[b], ag, au);
+                gateup_block<FMT, 1, IMAX, 0>(U[b], ag, au);
+                gateup_block<FMT, 1, IMAX, 1>(U[b], ag, au);
+                gateup_block<FMT, 1, IMAX, 2>(U[b], ag, au);
+                gateup_block<FMT, 1, IMAX, 3>(U[b], ag, au);
             }
         }
     }
-    if constexpr (TOKROWS) {
 #pragma unroll
-        for (int i = 0; i < IMAX; ++i) {
-            red[wv][0][0][i][lane] = ag[0][i];
-            red[wv][0][1][i][lane] = au[0][i];
-        }
-        __syncthreads();
-        if (wv != 0) return;
-        // output row r = 4 gq + i takes the sums of its token's matrix row
-        const int n = nt * 16 + rr;
-#pragma unroll
-        for (int i = 0; i < IMAX; ++i) {
-            const int r = 4 * gq + i;
-            if (r >= nrows) continue;
-            const int t = shared ? otok[i] : otok[i] / k;
-            const int sl = (t >> 2) * 16 + rr, si = t & 3;
-            float gs = red[0][0][0][si][sl], us = red[0][0][1][si][sl];
-#pragma unroll
-            for (int w2 = 1; w2 < NW; ++w2) {
-                gs += red[w2][0][0][si][sl];
-                us += red[w2][0][1][si][sl];
-            }
-            const float h = swiglu(gs, us);
-            const _Float16 hh = static_cast<_Float16>(h);
-            const float rem = h - static_cast<float>(hh);
-            const size_t off = (size_t)(grp.hrow0 + r) * f + n;
-            h_hi[off] = __builtin_bit_cast(uint16_t, hh);
-            h_lo[off] = f32_to_f16_bits(rem);
-        }
-        return;
+    for (int i = 0; i < IMAX; ++i) {
+        red[wv][0][i][lane] = ag[0][i];
+        red[wv][1][i][lane] = au[0][i];
     }
-    if constexpr (NW > 1) {
+    __syncthreads();
+    if (wv != 0) return;
+    // output row r = 4 gq + i takes the sums of its token's matrix row
+    const int n = nt * 16 + rr;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+    for (int i = 0; i < IMAX; ++i) {
+        const int r = 4 * gq + i;
+        if (r >= nrows) continue;
+        const int t = shared ? otok[i] : otok[i] / k;
+        const int sl = (t >> 2) * 16 + rr, si = t & 3;
+        float gs = red[0][0][si][sl], us = red[0][1][si][sl];
 #pragma unroll
-            for (int i = 0; i < IMAX; ++i) {
-                red[wv][mt][0][i][lane] = ag[mt][i];
-                red[wv][mt][1][i][lane] = au[mt][i];
-            }
-        __syncthreads();
-        if (wv == 0) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int i = 0; i < IMAX; ++i) {
-                    float gs = red[0][mt][0][i][lane], us = red[0][mt][1][i][lane];
-#pragma unroll
-                    for (int w2 = 1; w2 < NW; ++w2) {
-                        gs += red[w2][mt][0][i][lane];
-                        us += red[w2][mt][1][i][lane];
-                    }
-                    ag[mt][i] = gs;
-                    au[mt][i] = us;
-                }
+        for (int w2 = 1; w2 < NW; ++w2) {
+            gs += red[w2][0][si][sl];
+            us += red[w2][1][si][sl];
         }
-    }
-    if (wv == 0) {
-        const int n = nt * 16 + rr;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < IMAX; ++i) {
-                const int r = mt * 16 + gq * 4 + i;
-                if (r >= nrows) continue;
-                const float h = swiglu(ag[mt][i], au[mt][i]);
-                const _Float16 hh = static_cast<_Float16>(h);
-                const float rem = h - static_cast<float>(hh);
-                const size_t off = (size_t)(grp.hrow0 + r) * f + n;
-                h_hi[off] = __builtin_bit_cast(uint16_t, hh);
-                h_lo[off] = f32_to_f16_bits(rem);
-            }
+        const float h = swiglu(gs, us);
+        const _Float16 hh = static_cast<_Float16>(h);
+        const float rem = h - static_cast<float>(hh);
+        const size_t off = (size_t)(grp.hrow0 + r) * f + n;
+        h_hi[off] = __builtin_bit_cast(uint16_t, hh);
+        h_lo[off] = f32_to_f16_bits(rem);
     }
 }
 
@@ -438,17 +374,17 @@ __device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev 
 
 // ---------------------------------------------------------------- kernels
 // grid: (d_ff/16 row tiles, 1 + min(E, P) group slots); NW waves split K.
-template <int FMT, int MT, int IMAX, int NW>
+template <int FMT, int IMAX, int NW>
 __global__ __launch_bounds__(64 * NW) void gateup_small_kernel(
     QMatDev gate, QMatDev up, QMatDev sgate, QMatDev sup, const uint16_t *__restrict__ x, int T,
     int k, int d, int f, int E, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ sorted_pair, uint16_t *__restrict__ h_hi,
     uint16_t *__restrict__ h_lo) {
-    __shared__ float red[NW][MT][2][IMAX][64];
+    __shared__ float red[NW][2][IMAX][64];
     Group grp;
     if (!find_group(offsets, E, T, T * k, blockIdx.y, grp)) return;
-    gateup_task<FMT, MT, IMAX, NW, MT == 1>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp,
-                                            blockIdx.x, red, h_hi, h_lo);
+    gateup_task<FMT, IMAX, NW>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp, blockIdx.x, red, h_hi,
+                               h_lo);
 }
 
 // grid: (d_model/16 row tiles, group slots); NW waves split K = d_ff.
@@ -476,7 +412,7 @@ size_t ffn_small_ws_bytes(int d, int f, int E, int T, int k) {
     return 2 * rows * f * sizeof(uint16_t) + 256;
 }
 
-template <int FMT, int MTG, int MTD, int IMAX>
+template <int FMT, int MTD, int IMAX>
 static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k,
                              const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
                              float *y_shared, uint16_t *h_hi, uint16_t *h_lo, hipStream_t s) {
@@ -490,7 +426,7 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
 #define MOE_DN_WAVES 2
 #endif
     constexpr int NWG = MOE_GU_WAVES, NWD = MOE_DN_WAVES;   // waves per workgroup (split K)
-    hipLaunchKernelGGL((gateup_small_kernel<FMT, MTG, IMAX, NWG>), dim3(f / 16, slots),
+    hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG>), dim3(f / 16, slots),
                        dim3(64 * NWG), 0, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up), x,
                        T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo);
     hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD>), dim3(d / 16, slots),
@@ -502,15 +438,15 @@ template <int FMT>
 static void launch_small_t(const moe_layer &L, const uint16_t *x, int T, int k,
                            const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
                            float *y_shared, uint16_t *h_hi, uint16_t *h_lo, hipStream_t s) {
-    // M tiles: gate/up 16 rows per tile, down 8 rows (hi over lo) per tile
+    // down M tiles: 8 rows (hi over lo) per tile; gate/up: one 16-token tile
     if (T == 1)
-        launch_small_fmt<FMT, 1, 1, 1>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
+        launch_small_fmt<FMT, 1, 1>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
     else if (T == 2)
-        launch_small_fmt<FMT, 1, 1, 2>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
+        launch_small_fmt<FMT, 1, 2>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
     else if (T <= 8)
-        launch_small_fmt<FMT, 1, 1, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
+        launch_small_fmt<FMT, 1, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
     else   // T <= 16
-        launch_small_fmt<FMT, 1, 2, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
+        launch_small_fmt<FMT, 2, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
 }
 
 hipError_t launch_ffn_small(const moe_layer &L, const uint16_t *x, int T, int k,
