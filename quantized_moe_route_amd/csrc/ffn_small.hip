@@ -374,15 +374,22 @@ __device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev 
 
 // ---------------------------------------------------------------- kernels
 // grid: (d_ff/16 row tiles, 1 + min(E, P) group slots); NW waves split K.
+// The first tile of each slot also records the slot's group (nrows 0: none)
+// in `table`, so the down kernel reads it with one load.
 template <int FMT, int IMAX, int NW>
 __global__ __launch_bounds__(64 * NW) void gateup_small_kernel(
     QMatDev gate, QMatDev up, QMatDev sgate, QMatDev sup, const uint16_t *__restrict__ x, int T,
     int k, int d, int f, int E, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ sorted_pair, uint16_t *__restrict__ h_hi,
-    uint16_t *__restrict__ h_lo) {
+    uint16_t *__restrict__ h_lo, Group *__restrict__ table) {
     __shared__ float red[NW][2][IMAX][64];
     Group grp;
-    if (!find_group(offsets, E, T, T * k, blockIdx.y, grp)) return;
+    const bool found = find_group(offsets, E, T, T * k, blockIdx.y, grp);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        const Group none{0, 0, 0, 0};
+        *reinterpret_cast<u32x4 *>(&table[blockIdx.y]) = __builtin_bit_cast(u32x4, found ? grp : none);
+    }
+    if (!found) return;
     gateup_task<FMT, IMAX, NW>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp, blockIdx.x, red, h_hi,
                                h_lo);
 }
@@ -391,11 +398,11 @@ __global__ __launch_bounds__(64 * NW) void gateup_small_kernel(
 template <int FMT, int MT, int IMAX, int NW>
 __global__ __launch_bounds__(64 * NW) void down_small_kernel(
     QMatDev down, QMatDev sdown, const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
-    int T, int k, int d, int f, int E, const int32_t *__restrict__ offsets,
-    float *__restrict__ y_pairs, float *__restrict__ y_shared) {
+    int d, int f, const Group *__restrict__ table, float *__restrict__ y_pairs,
+    float *__restrict__ y_shared) {
     __shared__ float red[NW][MT][IMAX][64];
-    Group grp;
-    if (!find_group(offsets, E, T, T * k, blockIdx.y, grp)) return;
+    const Group grp = table[blockIdx.y];   // written by the gate/up kernel
+    if (grp.nrows == 0) return;
     const int wq = wave_uniform(threadIdx.x >> 6);
     DownW<FMT, MT, NW> Wt;
     down_load_w<FMT, MT, NW>(Wt, down, sdown, d, f, grp, blockIdx.x, wq);
@@ -405,17 +412,19 @@ __global__ __launch_bounds__(64 * NW) void down_small_kernel(
 
 static QMatDev qm(const moe_qmat &m) { return QMatDev{m.lo, m.hi, m.scale, m.min}; }
 
+// h_hi, h_lo [rows][f] (each padded to 128 elements), then the group table
 size_t ffn_small_ws_bytes(int d, int f, int E, int T, int k) {
     (void)d;
-    (void)E;
     const size_t rows = (size_t)T * k + T;
-    return 2 * rows * f * sizeof(uint16_t) + 256;
+    const size_t P = (size_t)T * k;
+    const size_t slots = 1 + ((size_t)E < P ? (size_t)E : P);
+    return 2 * (((rows * f + 127) / 128) * 128) * sizeof(uint16_t) + slots * sizeof(Group) + 256;
 }
 
 template <int FMT, int MTD, int IMAX>
 static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k,
                              const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
-                             float *y_shared, uint16_t *h_hi, uint16_t *h_lo, hipStream_t s) {
+                             float *y_shared, uint16_t *h_hi, uint16_t *h_lo, Group *table, hipStream_t s) {
     const int d = L.d_model, f = L.d_ff, E = L.n_experts;
     const int P = T * k;
     const int slots = 1 + (E < P ? E : P);
@@ -428,25 +437,25 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
     constexpr int NWG = MOE_GU_WAVES, NWD = MOE_DN_WAVES;   // waves per workgroup (split K)
     hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG>), dim3(f / 16, slots),
                        dim3(64 * NWG), 0, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up), x,
-                       T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo);
+                       T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, table);
     hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD>), dim3(d / 16, slots),
-                       dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, T, k, d, f, E,
-                       offsets, y_pairs, y_shared);
+                       dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, d, f, table,
+                       y_pairs, y_shared);
 }
 
 template <int FMT>
 static void launch_small_t(const moe_layer &L, const uint16_t *x, int T, int k,
                            const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
-                           float *y_shared, uint16_t *h_hi, uint16_t *h_lo, hipStream_t s) {
+                           float *y_shared, uint16_t *h_hi, uint16_t *h_lo, Group *table, hipStream_t s) {
     // down M tiles: 8 rows (hi over lo) per tile; gate/up: one 16-token tile
     if (T == 1)
-        launch_small_fmt<FMT, 1, 1>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
+        launch_small_fmt<FMT, 1, 1>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, s);
     else if (T == 2)
-        launch_small_fmt<FMT, 1, 2>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
+        launch_small_fmt<FMT, 1, 2>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, s);
     else if (T <= 8)
-        launch_small_fmt<FMT, 1, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
+        launch_small_fmt<FMT, 1, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, s);
     else   // T <= 16
-        launch_small_fmt<FMT, 2, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
+        launch_small_fmt<FMT, 2, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, s);
 }
 
 hipError_t launch_ffn_small(const moe_layer &L, const uint16_t *x, int T, int k,
@@ -455,10 +464,11 @@ hipError_t launch_ffn_small(const moe_layer &L, const uint16_t *x, int T, int k,
     const size_t rows = (size_t)T * k + T;
     uint16_t *h_hi = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + kWsHeader);
     uint16_t *h_lo = h_hi + ((rows * L.d_ff + 127) / 128) * 128;
+    Group *table = reinterpret_cast<Group *>(h_lo + ((rows * L.d_ff + 127) / 128) * 128);
     if (L.format == MOE_FMT_Q2_B32)
-        launch_small_t<MOE_FMT_Q2_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
+        launch_small_t<MOE_FMT_Q2_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, s);
     else
-        launch_small_t<MOE_FMT_Q3_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, s);
+        launch_small_t<MOE_FMT_Q3_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, s);
     return hipGetLastError();
 }
 
