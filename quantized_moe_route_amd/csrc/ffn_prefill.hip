@@ -92,10 +92,8 @@ static_assert(sizeof(PfItem) == 16, "items are read as one 16-byte vector");
 // 1 + e the routed expert e.  Sort key: (work desc, group asc), work = rows
 // (x2 for the shared expert); bitonic sort in LDS over the next power of two
 // >= E + 1 slots (at most PF_SORT).
-__global__ __launch_bounds__(1024) void pf_build_items_kernel(const int32_t *__restrict__ offsets,
-                                                              int E, int T, int P,
-                                                              PfItem *__restrict__ items,
-                                                              PfSched *__restrict__ sched) {
+__device__ __forceinline__ void build_items_block(const int32_t *__restrict__ offsets, int E, int T, int P,
+                                                  PfItem *__restrict__ items, PfSched *__restrict__ sched) {
     __shared__ unsigned long long key[PF_SORT];
     __shared__ int start[PF_SORT / PF_NXCD * PF_NXCD];
     __shared__ int xcount[PF_NXCD];
@@ -195,10 +193,19 @@ __global__ __launch_bounds__(1024) void pf_build_items_kernel(const int32_t *__r
     }
 }
 
-__global__ __launch_bounds__(256) void pf_x_to_f16_kernel(const uint16_t *__restrict__ x,
-                                                          uint16_t *__restrict__ x16, size_t n8) {
-    const size_t stride = (size_t)gridDim.x * 256;
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+// The two prepasses in one launch: block 0 builds the work items, the other
+// blocks convert x to fp16 (exact for bf16 values in fp16 range).
+__global__ __launch_bounds__(1024) void pf_prep_kernel(const int32_t *__restrict__ offsets, int E, int T,
+                                                       int P, PfItem *__restrict__ items,
+                                                       PfSched *__restrict__ sched,
+                                                       const uint16_t *__restrict__ x,
+                                                       uint16_t *__restrict__ x16, size_t n8) {
+    if (blockIdx.x == 0) {
+        build_items_block(offsets, E, T, P, items, sched);
+        return;
+    }
+    const size_t stride = (size_t)(gridDim.x - 1) * 1024;
+    for (size_t i = (size_t)(blockIdx.x - 1) * 1024 + threadIdx.x; i < n8; i += stride) {
         const u32x4 v = reinterpret_cast<const u32x4 *>(x)[i];
         u32x4 o;
 #pragma unroll
@@ -820,12 +827,11 @@ static void pf_launch_fmt(const moe_layer &L, const uint16_t *x, int T, int k, c
                           hipStream_t s) {
     const int d = L.d_model, f = L.d_ff, E = L.n_experts;
     const int P = T * k;
-    hipLaunchKernelGGL(pf_build_items_kernel, dim3(1), dim3(1024), 0, s, offsets, E, T, P, w.items,
-                       w.sched);
     const size_t n8 = (size_t)T * d / 8;
-    size_t blocks = (n8 + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(pf_x_to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, w.x16, n8);
+    size_t blocks = (n8 + 1023) / 1024;
+    if (blocks > 2048) blocks = 2048;
+    hipLaunchKernelGGL(pf_prep_kernel, dim3((unsigned)(1 + blocks)), dim3(1024), 0, s, offsets, E, T, P,
+                       w.items, w.sched, x, w.x16, n8);
     PfGemmArgs a{};
     a.items = w.items;
     a.sched = w.sched;
