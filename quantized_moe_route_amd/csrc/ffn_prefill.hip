@@ -422,48 +422,6 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
     const int nrows = item.nrows;
     const int e = SH ? 0 : item.expert;
 
-    // source row (token, or h row) of each tile row; rows past the item's
-    // end repeat its last row and are never stored
-    if (tid < PF_MT) {
-        const int r = tid < nrows ? tid : nrows - 1;
-        int src;
-        if constexpr (MODE == 0)
-            src = SH ? item.row0 + r : a.sorted_pair[item.row0 + r] / a.k;
-        else
-            src = item.hrow0 + r;
-        s_row[tid] = src;
-    }
-    // LDS only: the previous unit's output stores may still be in flight
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    wg_barrier();
-
-    // A copy slots of this lane: instruction i covers tile rows 4 (NI wv + i)
-    // .. +4; lane l takes row R = 4 (NI wv + i) + l / 16 and stores physical
-    // chunk l % 16, which holds logical chunk (l % 16) ^ (R % 16)
-    int arow_i[PF_NI];
-    const char *abase = reinterpret_cast<const char *>(a.a_hi);
-#pragma unroll
-    for (int i = 0; i < PF_NI; ++i) arow_i[i] = s_row[4 * (PF_NI * wv + i) + (l >> 4)];
-    auto switch_to_lo = [&]() {
-        abase = reinterpret_cast<const char *>(a.a_lo);
-#pragma unroll
-        for (int i = 0; i < PF_NI; ++i) {
-            const int R = 4 * (PF_NI * wv + i) + (l >> 4);
-            arow_i[i] = item.row0 + (R < nrows ? R : nrows - 1);
-        }
-    };
-    auto issue_a_part = [&](int kc, int i) {
-        const int kk = kc < KC ? kc : kc - KC;
-        uint8_t *dst = As + (kc % PF_NSTAGE) * PF_STAGE + wv * PF_NI * 1024;
-        const int R = 4 * (PF_NI * wv + i) + (l >> 4);
-        const int c = (l & 15) ^ (R & 15);
-        copy_to_lds16(abase + (size_t)arow_i[i] * (K * 2) + (kk * (PF_KS * 2) + c * 16), dst + i * 1024);
-    };
-    auto issue_a = [&](int kc) {
-#pragma unroll
-        for (int i = 0; i < PF_NI; ++i) issue_a_part(kc, i);
-    };
-
     // B: storage-unit index (at kc = 0) of this lane's unit in n-tile n
     const QMatDev W0 = SH ? a.s0 : a.w0;
     const QMatDev W1 = SH ? a.s1 : a.w1;
@@ -512,6 +470,53 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
         }
     };
 
+    BRaw<FMT> bcur[NTW][2], bnext[NTW][2];
+    // source row (token, or h row) of each tile row; rows past the item's
+    // end repeat its last row and are never stored.  The first step's
+    // weights are loaded right after the pair lookup and before its use, so
+    // their latency runs under the lookup, the barrier and the A copies.
+    int src = 0;
+    if (tid < PF_MT) {
+        const int r = tid < nrows ? tid : nrows - 1;
+        if constexpr (MODE == 0)
+            src = SH ? item.row0 + r : a.sorted_pair[item.row0 + r];
+        else
+            src = item.hrow0 + r;
+    }
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) load_b_tile(bcur, 0, n);
+    if (tid < PF_MT) s_row[tid] = (MODE == 0 && !SH) ? src / a.k : src;
+    // LDS only: the previous unit's output stores may still be in flight
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    wg_barrier();
+
+    // A copy slots of this lane: instruction i covers tile rows 4 (NI wv + i)
+    // .. +4; lane l takes row R = 4 (NI wv + i) + l / 16 and stores physical
+    // chunk l % 16, which holds logical chunk (l % 16) ^ (R % 16)
+    int arow_i[PF_NI];
+    const char *abase = reinterpret_cast<const char *>(a.a_hi);
+#pragma unroll
+    for (int i = 0; i < PF_NI; ++i) arow_i[i] = s_row[4 * (PF_NI * wv + i) + (l >> 4)];
+    auto switch_to_lo = [&]() {
+        abase = reinterpret_cast<const char *>(a.a_lo);
+#pragma unroll
+        for (int i = 0; i < PF_NI; ++i) {
+            const int R = 4 * (PF_NI * wv + i) + (l >> 4);
+            arow_i[i] = item.row0 + (R < nrows ? R : nrows - 1);
+        }
+    };
+    auto issue_a_part = [&](int kc, int i) {
+        const int kk = kc < KC ? kc : kc - KC;
+        uint8_t *dst = As + (kc % PF_NSTAGE) * PF_STAGE + wv * PF_NI * 1024;
+        const int R = 4 * (PF_NI * wv + i) + (l >> 4);
+        const int c = (l & 15) ^ (R & 15);
+        copy_to_lds16(abase + (size_t)arow_i[i] * (K * 2) + (kk * (PF_KS * 2) + c * 16), dst + i * 1024);
+    };
+    auto issue_a = [&](int kc) {
+#pragma unroll
+        for (int i = 0; i < PF_NI; ++i) issue_a_part(kc, i);
+    };
+
     f32x16 acc[MT][NTW];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -530,10 +535,7 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
 
     // Loads return in issue order, so one vmcnt wait and one barrier per step
     // cover them (see issue_part).
-    BRaw<FMT> bcur[NTW][2], bnext[NTW][2];
     issue_a(0);
-#pragma unroll
-    for (int n = 0; n < NTW; ++n) load_b_tile(bcur, 0, n);
     if (NSTEP > 1) {
         if (MODE == 1 && SH && KC == 1) switch_to_lo();
         issue_a(1);
