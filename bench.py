@@ -23,7 +23,10 @@ Workloads (default 1):
         T=8192 as 3
 --tail-skip RANK times the lossy route tail-skip variant (moe_dispatch_tail_skip)
 and reports the pairs kept and the output's deviation from the full layer;
---tokens T overrides the workload's batch size.
+--overlap-shared runs the shared expert (moe_shared_ffn) on a second stream
+beside moe_route_dispatch, then moe_routed_ffn, joining before moe_combine
+(the fork and join are captured in the graph); --tokens T overrides the
+workload's batch size.
 
 Decode workloads report the expert FFN call against HBM bandwidth (bytes of
 the distinct experts selected + activations); prefill workloads against the
@@ -118,6 +121,9 @@ def main():
                          "are not computed (the pages' rule: 6 for a top-10); lossy, opt-in")
     ap.add_argument("--separate-calls", action="store_true",
                     help="time moe_route and moe_dispatch as two calls (default: moe_route_dispatch)")
+    ap.add_argument("--overlap-shared", action="store_true",
+                    help="shared expert on a second stream beside routing (moe_shared_ffn), "
+                         "routed experts after it (moe_routed_ffn)")
     ap.add_argument("--copies", type=int, default=None,
                     help="layer copies cycled, single-layer workloads (default 16 decode, 1 prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -150,7 +156,7 @@ def main():
     import synth.device as sdev
     import quantized_moe_route_amd as q
     from quantized_moe_route_amd import hip
-    from quantized_moe_route_amd.layer import DeviceLayer, alloc_buffers, run_layer
+    from quantized_moe_route_amd.layer import DeviceLayer, SideStream, alloc_buffers, run_layer
 
     w = synth.WORKLOADS[args.workload]
     if args.tokens is not None:
@@ -211,7 +217,12 @@ def main():
         log(f"--tail-skip must lie in [0, {w.k}]")
         sys.exit(2)
     fused = not args.separate_calls and tf is None
-    run_layer(layer_of(0, 0), xs[0][0], buf, stream=sh, tail_from=tf, fused=fused)
+    ov = args.overlap_shared
+    if ov and not fused:
+        log("--overlap-shared goes with the default calls (no --separate-calls / --tail-skip)")
+        sys.exit(2)
+    side = SideStream(device=dev) if ov else None
+    run_layer(layer_of(0, 0), xs[0][0], buf, stream=sh, tail_from=tf, fused=fused, side=side)
     hip.stream_synchronize(sh)
     x0 = xs[0][0].cpu().numpy().view(np.uint16)
     lg = buf.logits[:w.T].cpu().numpy()
@@ -271,7 +282,13 @@ def main():
     def call(c, s, li):
         L = layer_of(s, li)
         x = xs[s][li]
-        if c == "route_dispatch":
+        if c == "shared_ffn":
+            q.moe_shared_ffn(L.struct, x, w.T, buf.y_shared, buf.ws_sh, buf.ws_sh_bytes,
+                             side.handle if side is not None else sh)
+        elif c == "routed_ffn":
+            q.moe_routed_ffn(L.struct, x, w.T, w.k, buf.offsets, buf.sorted_pair, buf.y_pairs,
+                             buf.ws, buf.ws_bytes, sh)
+        elif c == "route_dispatch":
             q.moe_route_dispatch(x, L.router, L.bias, buf.logits, w.T, w.d_model, w.n_experts, w.k,
                                  buf.ids, buf.w, buf.offsets, buf.sorted_pair, buf.pair_pos, buf.ws,
                                  buf.ws_bytes, sh)
@@ -287,13 +304,27 @@ def main():
             q.moe_combine(buf.y_pairs, buf.y_shared, buf.pair_pos, buf.w, w.T, w.k, w.d_model,
                           buf.out, sh)
 
-    calls = (["route_dispatch"] if fused else ["route", "dispatch"]) + ["expert_ffn", "combine"]
+    if ov:
+        calls = ["shared_ffn", "route_dispatch", "routed_ffn", "combine"]
+    else:
+        calls = (["route_dispatch"] if fused else ["route", "dispatch"]) + ["expert_ffn", "combine"]
 
     def enqueue(step0, nsteps):
         for s in range(step0, step0 + nsteps):
             for li in range(n_lay):
-                for c in calls:
-                    call(c, s, li)
+                if ov:
+                    # fork: the shared expert beside routing; join before the combine
+                    side.fork.record(sh)
+                    hip.stream_wait_event(side.handle, side.fork)
+                    call("shared_ffn", s, li)
+                    side.join.record(side.handle)
+                    call("route_dispatch", s, li)
+                    call("routed_ffn", s, li)
+                    hip.stream_wait_event(sh, side.join)
+                    call("combine", s, li)
+                else:
+                    for c in calls:
+                        call(c, s, li)
 
     if args.eager:
         enqueue(K, W)
@@ -334,7 +365,8 @@ def main():
     # (inputs of consecutive steps / layer copies), events around the graph
     G = min(K, 8 if prefill else 64)
     avg_us = {}
-    for c in calls:
+    side_saved, side = side, None   # per-call timing: every call on the main stream
+    for c in calls + (["expert_ffn"] if ov else []):
         with hip.Graph(sh) as gc:
             for s in range(G):
                 call(c, s, s % n_lay if n_lay > 1 else 0)
@@ -345,6 +377,7 @@ def main():
         e1.record(sh)
         hip.stream_synchronize(sh)
         avg_us[c] = 1e3 * e0.elapsed_ms(e1) / G
+    side = side_saved
 
     # algorithmic work of one moe_expert_ffn launch.
     #   decode: bytes = distinct experts used + shared, x rows in, y rows out
@@ -423,6 +456,7 @@ def main():
                    "layer_copies": len(layers) if n_lay == 1 else 1,
                    "mode": "eager" if args.eager else "hip-graph",
                    "calls": calls,
+                   **({"shared_expert": "second stream, beside routing"} if ov else {}),
                    **({} if tf is None else {"route_tail_skip_from": tf})},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -217,6 +217,29 @@ moe_status moe_expert_ffn(const moe_layer *layer, const uint16_t *x_bf16, int32_
                           float *y_shared, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_routed_ffn, moe_shared_ffn -- the two halves of moe_expert_ffn.
+ * [forum] "Strata의 동작 원리": the shared expert is always resident and
+ * needs no routing decision; [local] localai.co.kr guide, section "0.1.43의
+ * GPU별 측정 결과를 살펴봐요": copies are overlapped with the decode work they
+ * do not depend on.  moe_shared_ffn needs only x, so a caller can run it on a
+ * second stream while moe_route / moe_dispatch run, then moe_routed_ffn, and
+ * join the streams before moe_combine.
+ *
+ * moe_routed_ffn writes exactly the y_pairs of moe_expert_ffn (same
+ * arguments); moe_shared_ffn exactly its y_shared [T][d_model].  Each reads
+ * only its own expert matrices (the shared ones may be null for
+ * moe_routed_ffn and the routed ones for moe_shared_ffn).  Workspace: as
+ * moe_expert_ffn; moe_workspace_size(d_model, d_ff, E, T, k) with any k >= 1
+ * suffices for moe_shared_ffn.  Two calls that run at the same time need
+ * separate workspaces.  Errors as moe_expert_ffn.
+ */
+moe_status moe_routed_ffn(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, int32_t k,
+                          const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs, void *ws,
+                          size_t ws_bytes, void *stream);
+moe_status moe_shared_ffn(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, float *y_shared,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/*
  * moe_combine -- merge the expert outputs of each token.
  * [forum] "Strata의 동작 원리": the GPU merges every expert's result, then the
  * next layer starts.

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "_lib", "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_FMT_Q2_B32, MOE_FMT_Q3_B32 = 1, 2
 ENTRY_POINTS = ("moe_route", "moe_dispatch", "moe_dispatch_tail_skip", "moe_route_dispatch",
-                "moe_expert_ffn", "moe_combine", "moe_workspace_size", "moe_workspace_init",
+                "moe_expert_ffn", "moe_routed_ffn", "moe_shared_ffn", "moe_combine", "moe_workspace_size", "moe_workspace_init",
                 "moe_status_string", "moe_abi_version")
 
 
@@ -49,6 +49,8 @@ def _load():
     lib.moe_dispatch_tail_skip.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.moe_route_dispatch.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_expert_ffn.argtypes = [C.POINTER(moe_layer), vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_routed_ffn.argtypes = [C.POINTER(moe_layer), vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.moe_shared_ffn.argtypes = [C.POINTER(moe_layer), vp, i32, vp, vp, sz, vp]
     lib.moe_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
     lib.moe_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.moe_workspace_size.restype = sz
@@ -142,6 +144,19 @@ def moe_expert_ffn(layer, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared,
     st = lib.moe_expert_ffn(C.byref(layer), _ptr(x_bf16), T, k, _ptr(offsets), _ptr(sorted_pair),
                             _ptr(y_pairs), _ptr(y_shared), _ptr(ws), ws_bytes, _stream(stream))
     return _check(st, "moe_expert_ffn") if check else st
+
+
+def moe_routed_ffn(layer, x_bf16, T, k, offsets, sorted_pair, y_pairs, ws, ws_bytes, stream=None,
+                   check=True):
+    st = lib.moe_routed_ffn(C.byref(layer), _ptr(x_bf16), T, k, _ptr(offsets), _ptr(sorted_pair),
+                            _ptr(y_pairs), _ptr(ws), ws_bytes, _stream(stream))
+    return _check(st, "moe_routed_ffn") if check else st
+
+
+def moe_shared_ffn(layer, x_bf16, T, y_shared, ws, ws_bytes, stream=None, check=True):
+    st = lib.moe_shared_ffn(C.byref(layer), _ptr(x_bf16), T, _ptr(y_shared), _ptr(ws), ws_bytes,
+                            _stream(stream))
+    return _check(st, "moe_shared_ffn") if check else st
 
 
 def moe_combine(y_pairs, y_shared, pair_pos, topk_w, T, k, d_model, out, stream=None, check=True):

@@ -160,38 +160,65 @@ moe_status moe_route_dispatch(const uint16_t *x_bf16, const float *w_router, con
     return moe_dispatch(topk_ids, T, E, k, offsets, sorted_pair, pair_pos, ws, ws_bytes, stream);
 }
 
-moe_status moe_expert_ffn(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, int32_t k,
-                          const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
-                          float *y_shared, void *ws, size_t ws_bytes, void *stream) {
+static moe_status ffn_checked(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, int32_t k,
+                              const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
+                              float *y_shared, int parts, void *ws, size_t ws_bytes, void *stream) {
     if (!layer) return MOE_ERR_INVALID_ARGUMENT;
     const moe_layer &L = *layer;
     if (L.format != MOE_FMT_Q2_B32 && L.format != MOE_FMT_Q3_B32) return MOE_ERR_UNSUPPORTED;
     if (!ok_dim(L.d_model) || !ok_dim(L.d_ff)) return MOE_ERR_UNSUPPORTED;
     if (L.n_experts < 1 || L.n_experts > kMaxE) return MOE_ERR_INVALID_ARGUMENT;
-    if (T < 0 || k < 1 || k > L.n_experts) return MOE_ERR_INVALID_ARGUMENT;
+    if (T < 0) return MOE_ERR_INVALID_ARGUMENT;
+    if ((parts & kFfnRouted) && (k < 1 || k > L.n_experts)) return MOE_ERR_INVALID_ARGUMENT;
     if ((int64_t)T * k >= INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
-    if (!check_qmat(L.gate, L.format) || !check_qmat(L.up, L.format) ||
-        !check_qmat(L.down, L.format) || !check_qmat(L.sh_gate, L.format) ||
-        !check_qmat(L.sh_up, L.format) || !check_qmat(L.sh_down, L.format))
-        return MOE_ERR_INVALID_ARGUMENT;
-    if (!x_bf16 || !offsets || !sorted_pair || !y_pairs || !y_shared)
-        return MOE_ERR_INVALID_ARGUMENT;
-    if (!aligned16(x_bf16) || !aligned16(offsets) || !aligned16(sorted_pair) ||
-        !aligned16(y_pairs) || !aligned16(y_shared))
-        return MOE_ERR_INVALID_ARGUMENT;
-    if (!ws || !aligned256(ws) ||
-        ws_bytes < ffn_need(L.d_model, L.d_ff, L.n_experts, T, k))
+    if (!x_bf16 || !aligned16(x_bf16)) return MOE_ERR_INVALID_ARGUMENT;
+    if (parts & kFfnRouted) {
+        if (!check_qmat(L.gate, L.format) || !check_qmat(L.up, L.format) || !check_qmat(L.down, L.format))
+            return MOE_ERR_INVALID_ARGUMENT;
+        if (!offsets || !sorted_pair || !y_pairs) return MOE_ERR_INVALID_ARGUMENT;
+        if (!aligned16(offsets) || !aligned16(sorted_pair) || !aligned16(y_pairs))
+            return MOE_ERR_INVALID_ARGUMENT;
+    }
+    if (parts & kFfnShared) {
+        if (!check_qmat(L.sh_gate, L.format) || !check_qmat(L.sh_up, L.format) ||
+            !check_qmat(L.sh_down, L.format))
+            return MOE_ERR_INVALID_ARGUMENT;
+        if (!y_shared || !aligned16(y_shared)) return MOE_ERR_INVALID_ARGUMENT;
+    }
+    if (!ws || !aligned256(ws) || ws_bytes < ffn_need(L.d_model, L.d_ff, L.n_experts, T, k))
         return MOE_ERR_WORKSPACE;
     if (T == 0) return MOE_OK;
     hipStream_t s = as_stream(stream);
     if (T <= kSmallTMax)
-        return launched(launch_ffn_small(L, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared,
-                                         ws, s));
-    hipError_t e = T <= kPfMidTMax
-                       ? launch_ffn_prefill_mid(L, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, ws, s)
-                       : launch_ffn_prefill(L, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, ws, s);
+        return launched(launch_ffn_small(L, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, ws,
+                                         parts, s));
+    hipError_t e = T <= kPfMidTMax ? launch_ffn_prefill_mid(L, x_bf16, T, k, offsets, sorted_pair, y_pairs,
+                                                            y_shared, ws, parts, s)
+                                   : launch_ffn_prefill(L, x_bf16, T, k, offsets, sorted_pair, y_pairs,
+                                                        y_shared, ws, parts, s);
     if (e == hipErrorNotSupported) return MOE_ERR_UNSUPPORTED;
     return launched(e);
+}
+
+moe_status moe_expert_ffn(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, int32_t k,
+                          const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
+                          float *y_shared, void *ws, size_t ws_bytes, void *stream) {
+    return ffn_checked(layer, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, kFfnBoth, ws, ws_bytes,
+                       stream);
+}
+
+moe_status moe_routed_ffn(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, int32_t k,
+                          const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs, void *ws,
+                          size_t ws_bytes, void *stream) {
+    return ffn_checked(layer, x_bf16, T, k, offsets, sorted_pair, y_pairs, nullptr, kFfnRouted, ws, ws_bytes,
+                       stream);
+}
+
+moe_status moe_shared_ffn(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, float *y_shared,
+                          void *ws, size_t ws_bytes, void *stream) {
+    // k = 0: the workspace holds the shared expert's rows only
+    return ffn_checked(layer, x_bf16, T, 0, nullptr, nullptr, nullptr, y_shared, kFfnShared, ws, ws_bytes,
+                       stream);
 }
 
 moe_status moe_combine(const float *y_pairs, const float *y_shared, const int32_t *pair_pos,

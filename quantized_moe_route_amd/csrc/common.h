@@ -277,21 +277,27 @@ hipError_t launch_dispatch(const int32_t *ids, int T, int E, int k, int tail_fro
                            int32_t *sorted_pair, int32_t *pair_pos, void *ws, hipStream_t s);
 size_t dispatch_ws_bytes(int E, int T, int k);
 
+// Which experts an FFN launch computes: the routed groups, the shared
+// expert, or both.  Without the routed part offsets, sorted_pair and y_pairs
+// are not read (they may be null) and k may be 0; without the shared part
+// y_shared is not written.
+constexpr int kFfnRouted = 1, kFfnShared = 2, kFfnBoth = 3;
+
 hipError_t launch_ffn_small(const moe_layer &L, const uint16_t *x, int T, int k,
                             const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
-                            float *y_shared, void *ws, hipStream_t s);
+                            float *y_shared, void *ws, int parts, hipStream_t s);
 size_t ffn_small_ws_bytes(int d, int f, int E, int T, int k);
 constexpr int kSmallTMax = 16;   // above: the grouped matrix-core path
 
 hipError_t launch_ffn_prefill(const moe_layer &L, const uint16_t *x, int T, int k,
                               const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
-                              float *y_shared, void *ws, hipStream_t s);
+                              float *y_shared, void *ws, int parts, hipStream_t s);
 size_t ffn_prefill_ws_bytes(int d, int f, int E, int T, int k);
 // the same grouped GEMM built for mid-size batches (64-row items, two
 // workgroups per compute unit)
 hipError_t launch_ffn_prefill_mid(const moe_layer &L, const uint16_t *x, int T, int k,
                                   const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
-                                  float *y_shared, void *ws, hipStream_t s);
+                                  float *y_shared, void *ws, int parts, hipStream_t s);
 size_t ffn_prefill_mid_ws_bytes(int d, int f, int E, int T, int k);
 constexpr int kPfMidTMax = 2048;   // T above this: the large-chunk build
 

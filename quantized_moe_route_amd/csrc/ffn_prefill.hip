@@ -93,7 +93,8 @@ static_assert(sizeof(PfItem) == 16, "items are read as one 16-byte vector");
 // (x2 for the shared expert); bitonic sort in LDS over the next power of two
 // >= E + 1 slots (at most PF_SORT).
 __device__ __forceinline__ void build_items_block(const int32_t *__restrict__ offsets, int E, int T, int P,
-                                                  PfItem *__restrict__ items, PfSched *__restrict__ sched) {
+                                                  int parts, PfItem *__restrict__ items,
+                                                  PfSched *__restrict__ sched) {
     __shared__ unsigned long long key[PF_SORT];
     __shared__ int start[PF_SORT / PF_NXCD * PF_NXCD];
     __shared__ int xcount[PF_NXCD];
@@ -105,7 +106,7 @@ __device__ __forceinline__ void build_items_block(const int32_t *__restrict__ of
     for (int g = tid; g < PF_SORT; g += 1024) {
         unsigned long long kk = 0;
         int rows = 0, r0 = 0;
-        if (g < G) {
+        if (g == 0 ? (parts & kFfnShared) != 0 : g < G && (parts & kFfnRouted) != 0) {
             r0 = g == 0 ? 0 : offsets[g - 1];
             rows = g == 0 ? T : offsets[g] - r0;
             const unsigned long long work = g == 0 ? 2ull * rows : (unsigned long long)rows;
@@ -196,12 +197,12 @@ __device__ __forceinline__ void build_items_block(const int32_t *__restrict__ of
 // The two prepasses in one launch: block 0 builds the work items, the other
 // blocks convert x to fp16 (exact for bf16 values in fp16 range).
 __global__ __launch_bounds__(1024) void pf_prep_kernel(const int32_t *__restrict__ offsets, int E, int T,
-                                                       int P, PfItem *__restrict__ items,
+                                                       int P, int parts, PfItem *__restrict__ items,
                                                        PfSched *__restrict__ sched,
                                                        const uint16_t *__restrict__ x,
                                                        uint16_t *__restrict__ x16, size_t n8) {
     if (blockIdx.x == 0) {
-        build_items_block(offsets, E, T, P, items, sched);
+        build_items_block(offsets, E, T, P, parts, items, sched);
         return;
     }
     const size_t stride = (size_t)(gridDim.x - 1) * 1024;
@@ -826,14 +827,14 @@ static int pf_grid(int occ) {
 template <int FMT>
 static void pf_launch_fmt(const moe_layer &L, const uint16_t *x, int T, int k, const int32_t *offsets,
                           const int32_t *sorted_pair, float *y_pairs, float *y_shared, const PfWs &w,
-                          hipStream_t s) {
+                          int parts, hipStream_t s) {
     const int d = L.d_model, f = L.d_ff, E = L.n_experts;
     const int P = T * k;
     const size_t n8 = (size_t)T * d / 8;
     size_t blocks = (n8 + 1023) / 1024;
     if (blocks > 2048) blocks = 2048;
     hipLaunchKernelGGL(pf_prep_kernel, dim3((unsigned)(1 + blocks)), dim3(1024), 0, s, offsets, E, T, P,
-                       w.items, w.sched, x, w.x16, n8);
+                       parts, w.items, w.sched, x, w.x16, n8);
     PfGemmArgs a{};
     a.items = w.items;
     a.sched = w.sched;
@@ -868,13 +869,13 @@ static void pf_launch_fmt(const moe_layer &L, const uint16_t *x, int T, int k, c
 }
 
 static hipError_t launch(const moe_layer &L, const uint16_t *x, int T, int k, const int32_t *offsets,
-                         const int32_t *sorted_pair, float *y_pairs, float *y_shared, void *ws,
+                         const int32_t *sorted_pair, float *y_pairs, float *y_shared, void *ws, int parts,
                          hipStream_t s) {
     const PfWs w = pf_carve(ws, L.d_model, L.d_ff, L.n_experts, T, k);
     if (L.format == MOE_FMT_Q2_B32)
-        pf_launch_fmt<MOE_FMT_Q2_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, w, s);
+        pf_launch_fmt<MOE_FMT_Q2_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, w, parts, s);
     else
-        pf_launch_fmt<MOE_FMT_Q3_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, w, s);
+        pf_launch_fmt<MOE_FMT_Q3_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, w, parts, s);
     return hipGetLastError();
 }
 
@@ -883,9 +884,9 @@ static hipError_t launch(const moe_layer &L, const uint16_t *x, int T, int k, co
 size_t MOE_PF_WS(int d, int f, int E, int T, int k) { return MOE_PF_NS::ws_bytes(d, f, E, T, k); }
 
 hipError_t MOE_PF_LAUNCH(const moe_layer &L, const uint16_t *x, int T, int k, const int32_t *offsets,
-                         const int32_t *sorted_pair, float *y_pairs, float *y_shared, void *ws,
+                         const int32_t *sorted_pair, float *y_pairs, float *y_shared, void *ws, int parts,
                          hipStream_t s) {
-    return MOE_PF_NS::launch(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, ws, s);
+    return MOE_PF_NS::launch(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, ws, parts, s);
 }
 
 }  // namespace moe

@@ -129,6 +129,48 @@ __device__ __forceinline__ void gateup_block(const GateUpUnit<FMT, MT> &U, f32x4
 #endif
 constexpr int kBatch = MOE_DECODE_BATCH;   // units prefetched per wave per batch
 
+constexpr int kPfPieces = 4;   // 16-byte pieces per thread (covers 3 down tiles)
+
+// The down-projection weights of output tiles ot = nt, nt + G, nt + 2G, ...
+// (G gate/up tiles per group: with G and the down grid's width multiples of
+// 8, each such tile's down workgroup runs on the XCD of this one), read while
+// the gate/up work runs so that the down kernel finds them in the caches
+// instead of paying a full memory latency after its group lookup.  The
+// values are only held until the caller consumes them.  Used for single-token
+// batches (11 groups): there the FFN gains ~0.6 us; with 4 or 16 tokens (22
+// to 140 groups) the extra loads slowed gate/up by more than down gained.
+template <int FMT>
+__device__ __forceinline__ void down_prefetch(u32x4 (&pf)[kPfPieces], const QMatDev &down,
+                                              const QMatDev &sdown, int d, int f, const Group &grp,
+                                              int nt, int G) {
+    const QMatDev W = grp.expert < 0 ? sdown : down;
+    const int e = grp.expert < 0 ? 0 : grp.expert;
+    const int KC = f / 128, OT = d / 16;
+    // pieces of one tile: codes (32 per unit), Q3 third bits (16), scales (8), Q2 minimums (8)
+    const int n_lo = KC * 32, n_hi = FMT == MOE_FMT_Q3_B32 ? KC * 16 : 0, n_sc = KC * 8;
+    const int P = n_lo + n_hi + 2 * n_sc - (FMT == MOE_FMT_Q3_B32 ? n_sc : 0);
+    const int ntile = (OT - nt + G - 1) / G;   // tiles nt + G m < OT
+#pragma unroll
+    for (int i = 0; i < kPfPieces; ++i) {
+        int q = (int)threadIdx.x + (int)blockDim.x * i;
+        q = q < ntile * P ? q : 0;   // unconditional loads: spare threads re-read piece 0
+        const int tq = q / P, pp = q - tq * P;
+        int ot = nt + G * tq;
+        ot = ot < OT ? ot : OT - 1;   // (only when no tile is left: f > d)
+        const size_t ub = ((size_t)e * OT + ot) * KC;
+        const uint8_t *src;
+        if (pp < n_lo)
+            src = W.lo + ub * 512 + (size_t)pp * 16;
+        else if (pp < n_lo + n_hi)
+            src = W.hi + ub * 256 + (size_t)(pp - n_lo) * 16;
+        else if (pp < n_lo + n_hi + n_sc)
+            src = reinterpret_cast<const uint8_t *>(W.scale) + ub * 128 + (size_t)(pp - n_lo - n_hi) * 16;
+        else
+            src = reinterpret_cast<const uint8_t *>(W.min) + ub * 128 + (size_t)(pp - n_lo - n_hi - n_sc) * 16;
+        pf[i] = *reinterpret_cast<const u32x4 *>(src);
+    }
+}
+
 // One gate/up task: 16 h columns (row tile nt) of one expert group, for all
 // of the group's rows.  The NW waves of the workgroup split K and meet in LDS
 // (red); wave 0 applies SwiGLU and writes h as fp16 hi + lo.
@@ -143,8 +185,10 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
                                             const QMatDev &sup, const uint16_t *__restrict__ x, int T, int k, int d,
                                             int f, const int32_t *__restrict__ sorted_pair, const Group &grp,
                                             int nt, float (*red)[2][IMAX][64], uint16_t *__restrict__ h_hi,
-                                            uint16_t *__restrict__ h_lo) {
+                                            uint16_t *__restrict__ h_lo, const QMatDev &down,
+                                            const QMatDev &sdown) {
     static_assert(NW > 1, "token rows: K split over waves");
+    constexpr bool kPrefetch = IMAX == 1;   // single-token batch
     const int lane = __lane_id();
     const int wv = wave_uniform(threadIdx.x >> 6);
     const int gq = lane >> 4, rr = lane & 15;
@@ -170,6 +214,7 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
     ag[0] = f32x4{0.f, 0.f, 0.f, 0.f};
     au[0] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint16_t *xrow[1] = {x + (size_t)(rr < T ? rr : T - 1) * d};
+    u32x4 pf[kPfPieces];
     for (int u0 = wv; u0 < KC; u0 += NW * kBatch) {
         GateUpUnit<FMT, 1> U[kBatch];
 #pragma unroll
@@ -182,6 +227,10 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
         for (int b = 0; b < kBatch; ++b) {
             const int u = u0 + NW * b;
             if (u < KC) gateup_load_x(U[b], u, gq, xrow);
+        }
+        if (kPrefetch && u0 == wv) {
+            __asm__ volatile("" ::: "memory");
+            down_prefetch<FMT>(pf, down, sdown, d, f, grp, nt, f / 16);
         }
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
@@ -199,7 +248,12 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
         red[wv][1][i][lane] = au[0][i];
     }
     __syncthreads();
-    if (wv != 0) return;
+    if (wv != 0) {
+        if constexpr (kPrefetch)
+#pragma unroll
+            for (int i = 0; i < kPfPieces; ++i) __asm__ volatile("" ::"v"(pf[i]));
+        return;
+    }
     // output row r = 4 gq + i takes the sums of its token's matrix row
     const int n = nt * 16 + rr;
 #pragma unroll
@@ -221,6 +275,9 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
         h_hi[off] = __builtin_bit_cast(uint16_t, hh);
         h_lo[off] = f32_to_f16_bits(rem);
     }
+    if constexpr (kPrefetch)
+#pragma unroll
+        for (int i = 0; i < kPfPieces; ++i) __asm__ volatile("" ::"v"(pf[i]));
 }
 
 template <int FMT, int MT>
@@ -373,25 +430,26 @@ __device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev 
 }
 
 // ---------------------------------------------------------------- kernels
-// grid: (d_ff/16 row tiles, 1 + min(E, P) group slots); NW waves split K.
-// The first tile of each slot also records the slot's group (nrows 0: none)
-// in `table`, so the down kernel reads it with one load.
+// grid: (d_ff/16 row tiles, group slots slot0 + blockIdx.y: slot 0 the shared
+// expert, slots 1 .. min(E, P) the routed groups); NW waves split K.  The
+// first tile of each slot also records the slot's group (nrows 0: none) in
+// `table`, so the down kernel reads it with one load.
 template <int FMT, int IMAX, int NW>
 __global__ __launch_bounds__(64 * NW) void gateup_small_kernel(
     QMatDev gate, QMatDev up, QMatDev sgate, QMatDev sup, const uint16_t *__restrict__ x, int T,
     int k, int d, int f, int E, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ sorted_pair, uint16_t *__restrict__ h_hi,
-    uint16_t *__restrict__ h_lo, Group *__restrict__ table) {
+    uint16_t *__restrict__ h_lo, Group *__restrict__ table, QMatDev down, QMatDev sdown, int slot0) {
     __shared__ float red[NW][2][IMAX][64];
     Group grp;
-    const bool found = find_group(offsets, E, T, T * k, blockIdx.y, grp);
+    const bool found = find_group(offsets, E, T, T * k, slot0 + (int)blockIdx.y, grp);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         const Group none{0, 0, 0, 0};
         *reinterpret_cast<u32x4 *>(&table[blockIdx.y]) = __builtin_bit_cast(u32x4, found ? grp : none);
     }
     if (!found) return;
     gateup_task<FMT, IMAX, NW>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp, blockIdx.x, red, h_hi,
-                               h_lo);
+                               h_lo, down, sdown);
 }
 
 // grid: (d_model/16 row tiles, group slots); NW waves split K = d_ff.
@@ -424,10 +482,13 @@ size_t ffn_small_ws_bytes(int d, int f, int E, int T, int k) {
 template <int FMT, int MTD, int IMAX>
 static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k,
                              const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
-                             float *y_shared, uint16_t *h_hi, uint16_t *h_lo, Group *table, hipStream_t s) {
+                             float *y_shared, uint16_t *h_hi, uint16_t *h_lo, Group *table, int parts,
+                             hipStream_t s) {
     const int d = L.d_model, f = L.d_ff, E = L.n_experts;
     const int P = T * k;
-    const int slots = 1 + (E < P ? E : P);
+    const int slot0 = (parts & kFfnShared) ? 0 : 1;
+    const int slots = ((parts & kFfnShared) ? 1 : 0) + ((parts & kFfnRouted) ? (E < P ? E : P) : 0);
+    if (slots == 0) return;
 #ifndef MOE_GU_WAVES
 #define MOE_GU_WAVES 4
 #endif
@@ -437,7 +498,8 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
     constexpr int NWG = MOE_GU_WAVES, NWD = MOE_DN_WAVES;   // waves per workgroup (split K)
     hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG>), dim3(f / 16, slots),
                        dim3(64 * NWG), 0, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up), x,
-                       T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, table);
+                       T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, table, qm(L.down), qm(L.sh_down),
+                       slot0);
     hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD>), dim3(d / 16, slots),
                        dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, d, f, table,
                        y_pairs, y_shared);
@@ -446,29 +508,30 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
 template <int FMT>
 static void launch_small_t(const moe_layer &L, const uint16_t *x, int T, int k,
                            const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
-                           float *y_shared, uint16_t *h_hi, uint16_t *h_lo, Group *table, hipStream_t s) {
+                           float *y_shared, uint16_t *h_hi, uint16_t *h_lo, Group *table, int parts,
+                           hipStream_t s) {
     // down M tiles: 8 rows (hi over lo) per tile; gate/up: one 16-token tile
     if (T == 1)
-        launch_small_fmt<FMT, 1, 1>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, s);
+        launch_small_fmt<FMT, 1, 1>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, parts, s);
     else if (T == 2)
-        launch_small_fmt<FMT, 1, 2>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, s);
+        launch_small_fmt<FMT, 1, 2>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, parts, s);
     else if (T <= 8)
-        launch_small_fmt<FMT, 1, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, s);
+        launch_small_fmt<FMT, 1, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, parts, s);
     else   // T <= 16
-        launch_small_fmt<FMT, 2, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, s);
+        launch_small_fmt<FMT, 2, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, parts, s);
 }
 
 hipError_t launch_ffn_small(const moe_layer &L, const uint16_t *x, int T, int k,
                             const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
-                            float *y_shared, void *ws, hipStream_t s) {
+                            float *y_shared, void *ws, int parts, hipStream_t s) {
     const size_t rows = (size_t)T * k + T;
     uint16_t *h_hi = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + kWsHeader);
     uint16_t *h_lo = h_hi + ((rows * L.d_ff + 127) / 128) * 128;
     Group *table = reinterpret_cast<Group *>(h_lo + ((rows * L.d_ff + 127) / 128) * 128);
     if (L.format == MOE_FMT_Q2_B32)
-        launch_small_t<MOE_FMT_Q2_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, s);
+        launch_small_t<MOE_FMT_Q2_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, parts, s);
     else
-        launch_small_t<MOE_FMT_Q3_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, s);
+        launch_small_t<MOE_FMT_Q3_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, parts, s);
     return hipGetLastError();
 }
 

@@ -1,6 +1,6 @@
 """Minimal HIP runtime plumbing through ctypes: stream capture into a graph,
-graph replay, and timing events (including event-record nodes inside a
-graph).  No compute; used by the benchmark and the graph-replay test.
+graph replay, timing events (including event-record nodes inside a graph)
+and cross-stream waits (a fork and join inside a capture).  No compute; used by the benchmark and the graph-replay test.
 """
 from __future__ import annotations
 
@@ -25,6 +25,7 @@ _hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), _vp, _vp]
 _hip.hipEventDestroy.argtypes = [_vp]
 _hip.hipEventSynchronize.argtypes = [_vp]
 _hip.hipStreamSynchronize.argtypes = [_vp]
+_hip.hipStreamWaitEvent.argtypes = [_vp, _vp, C.c_uint]
 _hip.hipGetErrorString.argtypes = [C.c_int]
 _hip.hipGetErrorString.restype = C.c_char_p
 
@@ -101,3 +102,8 @@ class Graph:
 
 def stream_synchronize(stream: int):
     _ok(_hip.hipStreamSynchronize(_vp(stream)), "hipStreamSynchronize")
+
+
+def stream_wait_event(stream: int, event: Event):
+    """Work enqueued on `stream` after this waits for `event`'s last record."""
+    _ok(_hip.hipStreamWaitEvent(_vp(stream), event.h, 0), "hipStreamWaitEvent")

@@ -102,6 +102,34 @@ def test_ffn_validation(q):
     assert f(_layer(q), A, 0, 2, A, A, A, A, A, ws) == q.MOE_OK
 
 
+def test_routed_and_shared_ffn_validation(q):
+    r = lambda L, *a: q.moe_routed_ffn(L, *a, check=False)
+    s = lambda L, *a: q.moe_shared_ffn(L, *a, check=False)
+    ws = 1 << 24
+    good, none = q.make_qmat(A, None, A, A), q.make_qmat(None, None, None, None)
+    routed_only = q.moe_layer(1, 256, 128, 16, good, good, good, none, none, none)
+    shared_only = q.moe_layer(1, 256, 128, 16, none, none, none, good, good, good)
+    # moe_routed_ffn(layer, x, T, k, offsets, sorted_pair, y_pairs, ws, ws_bytes)
+    assert r(_layer(q), A, 4, 2, None, A, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert r(_layer(q), A, 4, 2, A, None, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert r(_layer(q), A, 4, 2, A, A, None, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert r(_layer(q), A, 4, 0, A, A, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert r(_layer(q), A, 4, 2, A, A, A, A, 16) == q.MOE_ERR_WORKSPACE
+    assert r(shared_only, A, 4, 2, A, A, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert r(routed_only, A, 0, 2, A, A, A, A, ws) == q.MOE_OK   # shared matrices not needed
+    # moe_shared_ffn(layer, x, T, y_shared, ws, ws_bytes)
+    assert s(_layer(q), None, 4, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert s(_layer(q), A, 4, None, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert s(_layer(q), A, -1, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert s(_layer(q), A, 4, A, A, 16) == q.MOE_ERR_WORKSPACE
+    assert s(routed_only, A, 4, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert s(shared_only, A, 0, A, A, ws) == q.MOE_OK            # routed matrices not needed
+    # moe_expert_ffn needs both
+    f = lambda L, *a: q.moe_expert_ffn(L, *a, check=False)
+    assert f(routed_only, A, 0, 2, A, A, A, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert f(shared_only, A, 0, 2, A, A, A, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+
+
 def test_workspace_size_monotone(q):
     s1 = q.moe_workspace_size(2048, 768, 512, 1, 10)
     s4 = q.moe_workspace_size(2048, 768, 512, 4, 10)
