@@ -3,7 +3,8 @@
 
 A step is one pass of the whole layer path over one batch of synthetic input:
 moe_route_dispatch (moe_route + moe_dispatch; one launch for batches of up to
-8 tokens) -> moe_expert_ffn -> moe_combine, or with --separate-calls the four
+8 tokens) -> moe_expert_ffn -> moe_combine (for up to 4 tokens the last two as
+moe_expert_ffn_combine, whose down kernel also merges), or with --separate-calls the four
 calls moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine (for the
 48-layer workloads: all 48 layers in sequence).  Inputs are resident in HBM before the
 timed region.  The K timed steps (and the W warm-up steps) are captured into
@@ -48,6 +49,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FUSE_COMBINE_TMAX = 4          # moe_expert_ffn_combine merges inside the down kernel up to here
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix
 METRIC = "MoE-layer tokens/s (decode T=1/4, prefill 8192); % HBM BW or % MFMA peak"
 
@@ -222,7 +224,9 @@ def main():
         log("--overlap-shared goes with the default calls (no --separate-calls / --tail-skip)")
         sys.exit(2)
     side = SideStream(device=dev) if ov else None
-    run_layer(layer_of(0, 0), xs[0][0], buf, stream=sh, tail_from=tf, fused=fused, side=side)
+    fuse_cmb = fused and not ov and w.T <= FUSE_COMBINE_TMAX
+    run_layer(layer_of(0, 0), xs[0][0], buf, stream=sh, tail_from=tf, fused=fused, side=side,
+              fuse_combine=fuse_cmb)
     hip.stream_synchronize(sh)
     x0 = xs[0][0].cpu().numpy().view(np.uint16)
     lg = buf.logits[:w.T].cpu().numpy()
@@ -297,6 +301,9 @@ def main():
                         buf.ids, buf.w, buf.ws, buf.ws_bytes, sh)
         elif c == "dispatch":
             dispatch()
+        elif c == "expert_ffn_combine":
+            q.moe_expert_ffn_combine(L.struct, x, w.T, w.k, buf.offsets, buf.sorted_pair, buf.pair_pos,
+                                     buf.w, buf.y_pairs, buf.y_shared, buf.out, buf.ws, buf.ws_bytes, sh)
         elif c == "expert_ffn":
             q.moe_expert_ffn(L.struct, x, w.T, w.k, buf.offsets, buf.sorted_pair, buf.y_pairs,
                              buf.y_shared, buf.ws, buf.ws_bytes, sh)
@@ -306,6 +313,8 @@ def main():
 
     if ov:
         calls = ["shared_ffn", "route_dispatch", "routed_ffn", "combine"]
+    elif fuse_cmb:
+        calls = ["route_dispatch", "expert_ffn_combine"]
     else:
         calls = (["route_dispatch"] if fused else ["route", "dispatch"]) + ["expert_ffn", "combine"]
 
@@ -366,7 +375,7 @@ def main():
     G = min(K, 8 if prefill else 64)
     avg_us = {}
     side_saved, side = side, None   # per-call timing: every call on the main stream
-    for c in calls + (["expert_ffn"] if ov else []):
+    for c in calls + (["expert_ffn"] if "expert_ffn" not in calls else []):
         with hip.Graph(sh) as gc:
             for s in range(G):
                 call(c, s, s % n_lay if n_lay > 1 else 0)
@@ -397,7 +406,11 @@ def main():
     act_bytes = rows_ffn * w.d_model * (2 + 4)             # x row in, y row out
     ffn_bytes = float(np.mean(groups)) * eb + act_bytes
     ffn_flops = float(rows_ffn) * 6.0 * w.d_model * w.d_ff
-    t_ffn = avg_us["expert_ffn"] * 1e-6
+    ffn_call = "expert_ffn_combine" if "expert_ffn_combine" in calls else "expert_ffn"
+    if ffn_call == "expert_ffn_combine":
+        # + the merge: every y row read back, out written, pair positions and weights
+        ffn_bytes += (rows_ffn * 4 + w.T * 4) * w.d_model + w.T * w.k * 8
+    t_ffn = avg_us[ffn_call] * 1e-6
     # counters were taken at the workload's own T only
     traffic = traffic_for(args.workload) if args.tokens is None else None
     if prefill:
@@ -410,7 +423,10 @@ def main():
                 "hbm_gbs_algorithmic": ffn_bytes / t_ffn / 1e9}
     else:
         achieved = ffn_bytes / t_ffn / 1e9
-        roof = {"bound": "hbm", "kernel": "moe_expert_ffn call: gateup_small, down_small",
+        roof = {"bound": "hbm",
+                "kernel": ("moe_expert_ffn_combine call: gateup_small, down_small with the merge"
+                           if ffn_call == "expert_ffn_combine" else
+                           "moe_expert_ffn call: gateup_small, down_small"),
                 "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "bytes_per_launch": ffn_bytes, "avg_groups": float(np.mean(groups))}

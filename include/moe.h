@@ -240,6 +240,24 @@ moe_status moe_shared_ffn(const moe_layer *layer, const uint16_t *x_bf16, int32_
                           void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_expert_ffn_combine -- moe_expert_ffn followed by moe_combine.
+ * [forum] "Strata의 동작 원리": the GPU merges every expert's result, then the
+ * next layer starts; a decode layer is a chain of small steps, so each launch
+ * saved is time saved per layer.
+ *
+ * Writes exactly what moe_expert_ffn then moe_combine (same arguments) write:
+ * y_pairs, y_shared and out, bit for bit.  With T <= 4 the expert kernels do
+ * the merge themselves (the last workgroup of each 16-column output tile to
+ * finish sums that tile), one launch less than the two calls; otherwise the
+ * two calls are enqueued in turn.  Workspace as moe_expert_ffn; its counters
+ * are zero again when the call ends.  Errors: those of the two calls.
+ */
+moe_status moe_expert_ffn_combine(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, int32_t k,
+                                  const int32_t *offsets, const int32_t *sorted_pair, const int32_t *pair_pos,
+                                  const float *topk_w, float *y_pairs, float *y_shared, float *out, void *ws,
+                                  size_t ws_bytes, void *stream);
+
+/*
  * moe_combine -- merge the expert outputs of each token.
  * [forum] "Strata의 동작 원리": the GPU merges every expert's result, then the
  * next layer starts.

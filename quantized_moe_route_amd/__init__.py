@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(HERE, "_lib", "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_FMT_Q2_B32, MOE_FMT_Q3_B32 = 1, 2
 ENTRY_POINTS = ("moe_route", "moe_dispatch", "moe_dispatch_tail_skip", "moe_route_dispatch",
-                "moe_expert_ffn", "moe_routed_ffn", "moe_shared_ffn", "moe_combine", "moe_workspace_size", "moe_workspace_init",
+                "moe_expert_ffn", "moe_routed_ffn", "moe_shared_ffn", "moe_expert_ffn_combine",
+                "moe_combine", "moe_workspace_size", "moe_workspace_init",
                 "moe_status_string", "moe_abi_version")
 
 
@@ -51,6 +52,8 @@ def _load():
     lib.moe_expert_ffn.argtypes = [C.POINTER(moe_layer), vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_routed_ffn.argtypes = [C.POINTER(moe_layer), vp, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.moe_shared_ffn.argtypes = [C.POINTER(moe_layer), vp, i32, vp, vp, sz, vp]
+    lib.moe_expert_ffn_combine.argtypes = [C.POINTER(moe_layer), vp, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                           vp, sz, vp]
     lib.moe_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
     lib.moe_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.moe_workspace_size.restype = sz
@@ -157,6 +160,14 @@ def moe_shared_ffn(layer, x_bf16, T, y_shared, ws, ws_bytes, stream=None, check=
     st = lib.moe_shared_ffn(C.byref(layer), _ptr(x_bf16), T, _ptr(y_shared), _ptr(ws), ws_bytes,
                             _stream(stream))
     return _check(st, "moe_shared_ffn") if check else st
+
+
+def moe_expert_ffn_combine(layer, x_bf16, T, k, offsets, sorted_pair, pair_pos, topk_w, y_pairs,
+                           y_shared, out, ws, ws_bytes, stream=None, check=True):
+    st = lib.moe_expert_ffn_combine(C.byref(layer), _ptr(x_bf16), T, k, _ptr(offsets),
+                                    _ptr(sorted_pair), _ptr(pair_pos), _ptr(topk_w), _ptr(y_pairs),
+                                    _ptr(y_shared), _ptr(out), _ptr(ws), ws_bytes, _stream(stream))
+    return _check(st, "moe_expert_ffn_combine") if check else st
 
 
 def moe_combine(y_pairs, y_shared, pair_pos, topk_w, T, k, d_model, out, stream=None, check=True):

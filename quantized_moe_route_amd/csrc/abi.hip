@@ -162,7 +162,8 @@ moe_status moe_route_dispatch(const uint16_t *x_bf16, const float *w_router, con
 
 static moe_status ffn_checked(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, int32_t k,
                               const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
-                              float *y_shared, int parts, void *ws, size_t ws_bytes, void *stream) {
+                              float *y_shared, int parts, void *ws, size_t ws_bytes, void *stream,
+                              bool validate_only = false) {
     if (!layer) return MOE_ERR_INVALID_ARGUMENT;
     const moe_layer &L = *layer;
     if (L.format != MOE_FMT_Q2_B32 && L.format != MOE_FMT_Q3_B32) return MOE_ERR_UNSUPPORTED;
@@ -187,7 +188,7 @@ static moe_status ffn_checked(const moe_layer *layer, const uint16_t *x_bf16, in
     }
     if (!ws || !aligned256(ws) || ws_bytes < ffn_need(L.d_model, L.d_ff, L.n_experts, T, k))
         return MOE_ERR_WORKSPACE;
-    if (T == 0) return MOE_OK;
+    if (T == 0 || validate_only) return MOE_OK;
     hipStream_t s = as_stream(stream);
     if (T <= kSmallTMax)
         return launched(launch_ffn_small(L, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, ws,
@@ -219,6 +220,28 @@ moe_status moe_shared_ffn(const moe_layer *layer, const uint16_t *x_bf16, int32_
     // k = 0: the workspace holds the shared expert's rows only
     return ffn_checked(layer, x_bf16, T, 0, nullptr, nullptr, nullptr, y_shared, kFfnShared, ws, ws_bytes,
                        stream);
+}
+
+moe_status moe_expert_ffn_combine(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, int32_t k,
+                                  const int32_t *offsets, const int32_t *sorted_pair, const int32_t *pair_pos,
+                                  const float *topk_w, float *y_pairs, float *y_shared, float *out, void *ws,
+                                  size_t ws_bytes, void *stream) {
+    if (!pair_pos || !topk_w || !out || !aligned16(pair_pos) || !aligned16(topk_w) || !aligned16(out))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (!layer) return MOE_ERR_INVALID_ARGUMENT;
+    if (T > kFuseCombineTMax || T == 0) {
+        // one call after the other
+        const moe_status st = moe_expert_ffn(layer, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, ws,
+                                             ws_bytes, stream);
+        if (st != MOE_OK) return st;
+        return moe_combine(y_pairs, y_shared, pair_pos, topk_w, T, k, layer->d_model, out, stream);
+    }
+    // validation of both calls, then the fused launch
+    const moe_status st = ffn_checked(layer, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, kFfnBoth,
+                                      ws, ws_bytes, stream, /*validate_only=*/true);
+    if (st != MOE_OK) return st;
+    return launched(launch_ffn_small(*layer, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, ws, kFfnBoth,
+                                     as_stream(stream), pair_pos, topk_w, out));
 }
 
 moe_status moe_combine(const float *y_pairs, const float *y_shared, const int32_t *pair_pos,

@@ -19,14 +19,42 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Workspace: the first 4 KiB hold int32 counters that are zero between
-// calls (each user restores them); scratch regions start after it.  A
-// counter that many workgroups hit sits on a 128-byte line of its own:
-// device-scope atomics on one line are served one after another.
-constexpr size_t kWsHeader = 4096;
+// Workspace: a header of int32 counters that are zero between calls (each
+// user restores them), then the scratch regions.  A counter that many
+// workgroups hit sits on a 128-byte line of its own: device-scope atomics on
+// one line are served one after another.  Header: 4 KiB for the router's
+// tiles, then one line per 16-column output tile (d_model <= 16,384) for the
+// down kernel's fused combine.
 constexpr int kCntLine = 32;        // int32 counters per 128-byte line
+constexpr size_t kCombineCnt = 4096;                       // byte offset of the combine counters
+constexpr size_t kWsHeader = kCombineCnt + (16384 / 16) * 128;
 constexpr int kRouteTile = 8;       // tokens per tile of the one-launch router
 // the one-launch router's tile tt counts its arrivals at counters[kCntLine * tt]
+
+// ------------------------------------------------- cross-workgroup hand-off
+// Each XCD has its own L2, so data passed between workgroups is written and
+// read at device scope (the sc1 forms, served by the device-coherent level)
+// instead of paying an agent-scope fence, which writes back the whole L2.
+// Ordering: every thread waits for its own stores to complete, the block
+// synchronises, then one thread bumps the arrival counter.
+__device__ __forceinline__ void store_dev(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev_int(int32_t *p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void publish_then_count(int32_t *counter, int n_arrivals, int &last_flag) {
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = (old == n_arrivals - 1);
+    }
+    __syncthreads();
+}
 
 struct QMatDev {
     const uint8_t *lo;
@@ -283,11 +311,19 @@ size_t dispatch_ws_bytes(int E, int T, int k);
 // y_shared is not written.
 constexpr int kFfnRouted = 1, kFfnShared = 2, kFfnBoth = 3;
 
+// With out given (parts = both), the down kernel also writes moe_combine's
+// out from pair_pos and topk_w, bit-identical to a separate combine.
 hipError_t launch_ffn_small(const moe_layer &L, const uint16_t *x, int T, int k,
                             const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
-                            float *y_shared, void *ws, int parts, hipStream_t s);
+                            float *y_shared, void *ws, int parts, hipStream_t s,
+                            const int32_t *pair_pos = nullptr, const float *topk_w = nullptr,
+                            float *out = nullptr);
 size_t ffn_small_ws_bytes(int d, int f, int E, int T, int k);
 constexpr int kSmallTMax = 16;   // above: the grouped matrix-core path
+// moe_expert_ffn_combine fuses the merge into the down kernel up to this
+// batch (per layer, measured: T = 1 and 4 gain 0.8 and 0.4 us; T = 8 and 16
+// lose, the merge taking longer with more arriving workgroups per tile)
+constexpr int kFuseCombineTMax = 4;
 
 hipError_t launch_ffn_prefill(const moe_layer &L, const uint16_t *x, int T, int k,
                               const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,

@@ -346,7 +346,7 @@ __device__ __forceinline__ void down_load_w(DownW<FMT, MT, NW> &Wt, const QMatDe
 // of weights (units wq + NW b), loaded by the caller.  A tile row rr < 8
 // holds h_hi of group row 8 mt + rr, row 8 + rr its h_lo; D rows 4 gq + i:
 // hi rows in lanes gq = 0, 1 and lo rows in gq = 2, 3.
-template <int FMT, int MT, int IMAX, int NW>
+template <int FMT, int MT, int IMAX, int NW, bool DEV>
 __device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev &down, const QMatDev &sdown,
                                           const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
                                           int d, int f, const Group &grp, int ot, int wq,
@@ -422,11 +422,60 @@ __device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev 
             const float y = acc[mt][i] + __shfl_xor(acc[mt][i], 32, 64);
             const int r = mt * 8 + gq * 4 + i;
             if (gq >= 2 || r >= nrows) continue;
-            if (grp.expert < 0)
-                y_shared[(size_t)r * d + o] = y;
+            float *dst = grp.expert < 0 ? y_shared + (size_t)r * d + o
+                                        : y_pairs + (size_t)(grp.row0 + r) * d + o;
+            if constexpr (DEV)
+                store_dev(dst, y);   // read by another workgroup of this launch
             else
-                y_pairs[(size_t)(grp.row0 + r) * d + o] = y;
+                *dst = y;
         }
+}
+
+// The fused combine (moe_combine's sum for one 16-column output tile).  Every
+// workgroup of the tile (one per group slot, empty slots included) arrives
+// after its y stores have completed at device scope; the last to arrive
+// computes out[t][16 ot .. 16 ot + 16) for every token exactly as the
+// combine kernel does (shared term first, then j order, one fma per pair)
+// and restores the tile's counter to zero.
+struct CombineArgs {
+    const int32_t *pair_pos;
+    const float *w;
+    float *out;
+    int32_t *counters;   // one per tile, kCntLine apart
+    int T, k;
+};
+
+__device__ __forceinline__ void combine_tile(const CombineArgs &cb, const float *y_pairs, const float *y_shared,
+                                             int d, int ot, int n_arrivals) {
+    __shared__ int last;
+    int32_t *counter = cb.counters + (size_t)kCntLine * ot;
+    publish_then_count(counter, n_arrivals, last);
+    if (!last) return;
+    constexpr int B = 8;   // pairs whose rows are loaded together
+    const int k = cb.k;
+    for (int i = threadIdx.x; i < cb.T * 16; i += blockDim.x) {
+        const int t = i >> 4, c = ot * 16 + (i & 15);
+        const int32_t *pp = cb.pair_pos + (size_t)t * k;
+        const float *ww = cb.w + (size_t)t * k;
+        float acc = load_dev(y_shared + (size_t)t * d + c);
+        for (int j0 = 0; j0 < k; j0 += B) {
+            int p[B];
+            float wj[B], v[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const int j = j0 + b < k ? j0 + b : k - 1;
+                p[b] = pp[j];
+                wj[b] = ww[j];
+            }
+#pragma unroll
+            for (int b = 0; b < B; ++b) v[b] = load_dev(y_pairs + (size_t)(p[b] >= 0 ? p[b] : 0) * d + c);
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+                if (j0 + b < k && p[b] >= 0) acc = fmaf(wj[b], v[b], acc);
+        }
+        cb.out[(size_t)t * d + c] = acc;
+    }
+    if (threadIdx.x == 0) store_dev_int(counter, 0);
 }
 
 // ---------------------------------------------------------------- kernels
@@ -452,20 +501,23 @@ __global__ __launch_bounds__(64 * NW) void gateup_small_kernel(
                                h_lo, down, sdown);
 }
 
-// grid: (d_model/16 row tiles, group slots); NW waves split K = d_ff.
-template <int FMT, int MT, int IMAX, int NW>
+// grid: (d_model/16 row tiles, group slots); NW waves split K = d_ff.  FUSE:
+// the last workgroup of each row tile also computes the tile of out.
+template <int FMT, int MT, int IMAX, int NW, bool FUSE>
 __global__ __launch_bounds__(64 * NW) void down_small_kernel(
     QMatDev down, QMatDev sdown, const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
     int d, int f, const Group *__restrict__ table, float *__restrict__ y_pairs,
-    float *__restrict__ y_shared) {
+    float *__restrict__ y_shared, CombineArgs cb) {
     __shared__ float red[NW][MT][IMAX][64];
     const Group grp = table[blockIdx.y];   // written by the gate/up kernel
-    if (grp.nrows == 0) return;
-    const int wq = wave_uniform(threadIdx.x >> 6);
-    DownW<FMT, MT, NW> Wt;
-    down_load_w<FMT, MT, NW>(Wt, down, sdown, d, f, grp, blockIdx.x, wq);
-    down_task<FMT, MT, IMAX, NW>(Wt, down, sdown, h_hi, h_lo, d, f, grp, blockIdx.x, wq, red, y_pairs,
-                                        y_shared);
+    if (grp.nrows != 0) {
+        const int wq = wave_uniform(threadIdx.x >> 6);
+        DownW<FMT, MT, NW> Wt;
+        down_load_w<FMT, MT, NW>(Wt, down, sdown, d, f, grp, blockIdx.x, wq);
+        down_task<FMT, MT, IMAX, NW, FUSE>(Wt, down, sdown, h_hi, h_lo, d, f, grp, blockIdx.x, wq, red,
+                                           y_pairs, y_shared);
+    }
+    if constexpr (FUSE) combine_tile(cb, y_pairs, y_shared, d, blockIdx.x, gridDim.y);
 }
 
 static QMatDev qm(const moe_qmat &m) { return QMatDev{m.lo, m.hi, m.scale, m.min}; }
@@ -483,7 +535,7 @@ template <int FMT, int MTD, int IMAX>
 static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k,
                              const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
                              float *y_shared, uint16_t *h_hi, uint16_t *h_lo, Group *table, int parts,
-                             hipStream_t s) {
+                             const CombineArgs &cb, hipStream_t s) {
     const int d = L.d_model, f = L.d_ff, E = L.n_experts;
     const int P = T * k;
     const int slot0 = (parts & kFfnShared) ? 0 : 1;
@@ -500,38 +552,52 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
                        dim3(64 * NWG), 0, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up), x,
                        T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, table, qm(L.down), qm(L.sh_down),
                        slot0);
-    hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD>), dim3(d / 16, slots),
-                       dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, d, f, table,
-                       y_pairs, y_shared);
+    if (cb.out)
+        hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, true>), dim3(d / 16, slots),
+                           dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, d, f, table,
+                           y_pairs, y_shared, cb);
+    else
+        hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, false>), dim3(d / 16, slots),
+                           dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, d, f, table,
+                           y_pairs, y_shared, cb);
 }
 
 template <int FMT>
 static void launch_small_t(const moe_layer &L, const uint16_t *x, int T, int k,
                            const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
                            float *y_shared, uint16_t *h_hi, uint16_t *h_lo, Group *table, int parts,
-                           hipStream_t s) {
+                           const CombineArgs &cb, hipStream_t s) {
     // down M tiles: 8 rows (hi over lo) per tile; gate/up: one 16-token tile
     if (T == 1)
-        launch_small_fmt<FMT, 1, 1>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, parts, s);
+        launch_small_fmt<FMT, 1, 1>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table,
+                                    parts, cb, s);
     else if (T == 2)
-        launch_small_fmt<FMT, 1, 2>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, parts, s);
+        launch_small_fmt<FMT, 1, 2>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table,
+                                    parts, cb, s);
     else if (T <= 8)
-        launch_small_fmt<FMT, 1, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, parts, s);
+        launch_small_fmt<FMT, 1, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table,
+                                    parts, cb, s);
     else   // T <= 16
-        launch_small_fmt<FMT, 2, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, parts, s);
+        launch_small_fmt<FMT, 2, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table,
+                                    parts, cb, s);
 }
 
 hipError_t launch_ffn_small(const moe_layer &L, const uint16_t *x, int T, int k,
                             const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
-                            float *y_shared, void *ws, int parts, hipStream_t s) {
+                            float *y_shared, void *ws, int parts, hipStream_t s,
+                            const int32_t *pair_pos, const float *topk_w, float *out) {
     const size_t rows = (size_t)T * k + T;
     uint16_t *h_hi = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + kWsHeader);
     uint16_t *h_lo = h_hi + ((rows * L.d_ff + 127) / 128) * 128;
     Group *table = reinterpret_cast<Group *>(h_lo + ((rows * L.d_ff + 127) / 128) * 128);
+    const CombineArgs cb{pair_pos, topk_w, out,
+                         reinterpret_cast<int32_t *>(static_cast<char *>(ws) + kCombineCnt), T, k};
     if (L.format == MOE_FMT_Q2_B32)
-        launch_small_t<MOE_FMT_Q2_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, parts, s);
+        launch_small_t<MOE_FMT_Q2_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table,
+                                        parts, cb, s);
     else
-        launch_small_t<MOE_FMT_Q3_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table, parts, s);
+        launch_small_t<MOE_FMT_Q3_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table,
+                                        parts, cb, s);
     return hipGetLastError();
 }
 

@@ -21,31 +21,6 @@
 
 namespace moe {
 
-// ------------------------------------------------- cross-workgroup hand-off
-// Each XCD has its own L2, so data passed between workgroups is written and
-// read at device scope (the sc1 forms, served by the device-coherent level)
-// instead of paying an agent-scope fence, which writes back the whole L2.
-// Ordering: every thread waits for its own stores to complete, the block
-// synchronises, then one thread bumps the arrival counter.
-__device__ __forceinline__ void store_dev(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_dev_int(int32_t *p, int32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_dev(const float *p) {
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void publish_then_count(int32_t *counter, int n_arrivals, int &last_flag) {
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = (old == n_arrivals - 1);
-    }
-    __syncthreads();
-}
-
 // --------------------------------------------------------------- top-k (wave)
 // Cross-lane steps use DPP (register-file lane permutes) inside each row of
 // 16 lanes and v_readlane across the four rows; no LDS round trips.

@@ -11,8 +11,8 @@ import dataclasses
 import torch
 
 from . import (MOE_FMT_Q2_B32, hip, make_layer, moe_combine, moe_dispatch, moe_dispatch_tail_skip,
-               moe_expert_ffn, moe_route, moe_route_dispatch, moe_routed_ffn, moe_shared_ffn,
-               moe_workspace_init, moe_workspace_size)
+               moe_expert_ffn, moe_expert_ffn_combine, moe_route, moe_route_dispatch, moe_routed_ffn,
+               moe_shared_ffn, moe_workspace_init, moe_workspace_size)
 
 MATS = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
 
@@ -106,13 +106,14 @@ class SideStream:
 
 
 def run_layer(layer: DeviceLayer, x, b: Buffers, stream=None, logits_in=False, tail_from=None,
-              fused=False, side: SideStream | None = None):
+              fused=False, side: SideStream | None = None, fuse_combine=False):
     """x: [T][d] bf16 (or int16 bits) device tensor.  Runs route -> dispatch ->
     expert FFN -> combine; returns b.out.  tail_from (< k) switches on route
     tail-skip in the dispatch step; fused uses moe_route_dispatch for the
     first two steps.  With `side` (and an explicit stream handle) the shared
     expert runs on the side stream beside routing and the routed experts
-    after it; the streams join before the combine."""
+    after it; the streams join before the combine.  fuse_combine uses
+    moe_expert_ffn_combine for the last two steps."""
     T, k = b.T, b.k
     d, E = layer.d_model, layer.n_experts
     if side is not None:
@@ -137,6 +138,11 @@ def run_layer(layer: DeviceLayer, x, b: Buffers, stream=None, logits_in=False, t
     else:
         moe_dispatch_tail_skip(b.ids, T, E, k, tail_from, b.offsets, b.sorted_pair, b.pair_pos, b.ws,
                                b.ws_bytes, stream)
+    if fuse_combine:
+        assert side is None
+        moe_expert_ffn_combine(layer.struct, x, T, k, b.offsets, b.sorted_pair, b.pair_pos, b.w, b.y_pairs,
+                               b.y_shared, b.out, b.ws, b.ws_bytes, stream)
+        return b.out
     if side is not None:
         moe_routed_ffn(layer.struct, x, T, k, b.offsets, b.sorted_pair, b.y_pairs, b.ws, b.ws_bytes,
                        stream)

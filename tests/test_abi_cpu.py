@@ -130,6 +130,21 @@ def test_routed_and_shared_ffn_validation(q):
     assert f(shared_only, A, 0, 2, A, A, A, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
 
 
+def test_ffn_combine_validation(q):
+    f = lambda L, *a: q.moe_expert_ffn_combine(L, *a, check=False)
+    ws = 1 << 24
+    # (x, T, k, offsets, sorted_pair, pair_pos, topk_w, y_pairs, y_shared, out, ws, ws_bytes)
+    assert f(_layer(q), A, 4, 2, A, A, None, A, A, A, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert f(_layer(q), A, 4, 2, A, A, A, None, A, A, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert f(_layer(q), A, 4, 2, A, A, A, A, A, A, None, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert f(_layer(q), A, 4, 2, None, A, A, A, A, A, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert f(_layer(q), A, 4, 2, A, A, A, A, A, None, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
+    assert f(_layer(q), A, 4, 2, A, A, A, A, A, A, A, A, 16) == q.MOE_ERR_WORKSPACE
+    assert f(_layer(q), A, 40, 2, A, A, A, A, A, A, A, A, 16) == q.MOE_ERR_WORKSPACE
+    assert f(_layer(q, fmt=3), A, 4, 2, A, A, A, A, A, A, A, A, ws) == q.MOE_ERR_UNSUPPORTED
+    assert f(_layer(q), A, 0, 2, A, A, A, A, A, A, A, A, ws) == q.MOE_OK
+
+
 def test_workspace_size_monotone(q):
     s1 = q.moe_workspace_size(2048, 768, 512, 1, 10)
     s4 = q.moe_workspace_size(2048, 768, 512, 4, 10)
