@@ -53,13 +53,14 @@ FUSE_COMBINE_TMAX = 4          # moe_expert_ffn_combine merges inside the down k
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix
 METRIC = "MoE-layer tokens/s (decode T=1/4, prefill 8192); % HBM BW or % MFMA peak"
 
-# HBM bytes per moe_expert_ffn call, from two rocprofv3 --pmc runs (FETCH_SIZE,
-# WRITE_SIZE; each scaled by what it reads for a plain 1 GiB copy), keyed by
-# workload.  Each figure is tied to a hash of the kernel sources it was taken
-# on and is reported as null once those sources change.
+# HBM bytes per expert-FFN call of the step (moe_expert_ffn_combine for
+# workload 1, moe_expert_ffn for workload 3), from two rocprofv3 --pmc runs
+# (FETCH_SIZE, WRITE_SIZE; each scaled by what it reads for a plain 1 GiB
+# copy), keyed by workload.  Each figure is tied to a hash of the kernel
+# sources it was taken on and is reported as null once those sources change.
 TRAFFIC = {
-    1: (("common.h", "ffn_small.hip"), "6f334f1e7404a4f1", 20235065),
-    3: (("common.h", "ffn_prefill.hip"), "5203ecea8941c188", 2602553195),
+    1: (("common.h", "ffn_small.hip"), "d9371b0e5b75b55a", 26926503),
+    3: (("common.h", "ffn_prefill.hip"), "199ec1edcb92df78", 2601345659),
 }
 
 
