@@ -96,6 +96,17 @@ def clone_layer(dl):
                        None if dl.bias is None else dl.bias.clone())
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, host_layer, router, bias, xs_host, seconds):
     """The oracle, as is, on a bounded sample of the same workload."""
     import oracle
@@ -366,6 +377,21 @@ def main():
     gpu_ms = ev_start.elapsed_ms(ev_end)
     out_graph = buf.out[:w.T].clone()
 
+    # spread: the timed graph replayed four more times, each replay timed
+    # with HIP events on the launch stream (per-step microseconds per replay)
+    step_us = None
+    if not args.eager:
+        per_run = [1e3 * gpu_ms / K]
+        for _ in range(4):
+            ev_start.record(sh)
+            g_timed.launch()
+            ev_end.record(sh)
+            hip.stream_synchronize(sh)
+            per_run.append(1e3 * ev_start.elapsed_ms(ev_end) / K)
+        pr = np.array(per_run)
+        step_us = {"median": float(np.median(pr)), "p10": float(np.percentile(pr, 10)),
+                   "p90": float(np.percentile(pr, 90)), "replays": len(per_run), "steps_each": K}
+
     # replay check: the last timed step again, eagerly; deterministic kernels
     enqueue(K - 1, 1)
     hip.stream_synchronize(sh)
@@ -454,7 +480,7 @@ def main():
                 if prefill else f"{n} oracle layer evaluations of T={w.T} token(s)")
         cpu = {"value": rate / n_lay,
                "unit": "tokens/s" + (" (through the 48-layer stack)" if n_lay > 1 else ""),
-               "cores": orc.num_threads(), "kind": "oracle",
+               "cores": orc.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
                "sample": f"{what} on layer 0 ({el:.1f} s)" +
                          (f"; stack rate = per-layer rate / {n_lay}" if n_lay > 1 else "")}
 
@@ -478,6 +504,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "gpu_ms_per_step": gpu_ms / K,
+        "step_us": step_us,
         "per_call_us": avg_us,
         ("layer_mfma_frac" if prefill else "layer_hbm_frac"):
             (ffn_flops * n_lay / (gpu_ms / K * 1e-3) / 1e12 / BF16_PEAK_TFLOPS) if prefill else

@@ -85,12 +85,15 @@ def _check_layer(q, w, L, x_bits, b):
     return err
 
 
-@pytest.mark.parametrize("wid", [0, 1, 2, 5])
-def test_workload_layer_parity(q, wid):
+@pytest.mark.parametrize("wid,layer", [(0, 0), (1, 0), (2, 0), (2, 23), (2, 47), (5, 0)])
+def test_workload_layer_parity(q, wid, layer):
+    """Every token of the layer against the oracle; for the 48-layer MTP
+    stack, the first, a middle and the last layer (each has its own weights
+    and Zipf router bias)."""
     w = synth.WORKLOADS[wid]
-    print(f"workload {w.name}", flush=True)
-    L = synth.gen_layer(w, layer=0)
-    x = synth.gen_x(w, layer=0)
+    print(f"workload {w.name} layer {layer}", flush=True)
+    L = synth.gen_layer(w, layer=layer)
+    x = synth.gen_x(w, layer=layer)
     dl = _upload(L, w)
     b = _run(q, dl, w, x)
     err = _check_layer(q, w, L, x, b)

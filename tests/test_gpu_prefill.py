@@ -90,17 +90,18 @@ def test_prefill_shape_sweep(q, fmt, T, E, k, d, f):
     print(f"max|err|/rms = {err:.3e}")
 
 
-@pytest.mark.parametrize("wid", [3, 4, 6])
-def test_prefill_full_workload_sampled(q, wid):
+@pytest.mark.parametrize("wid,layer", [(3, 0), (4, 0), (4, 23), (4, 47), (6, 0)])
+def test_prefill_full_workload_sampled(q, wid, layer):
     """T = 8,192 at d=2048, f=768, top-10 (+ shared): E=512 with Q2 uniform
-    routing and Q3 Zipf(1.3) routing (layer 0), and the E=256 variant with Q2.
-    64 sampled tokens against the oracle."""
+    routing, Q3 Zipf(1.3) routing (the first, a middle and the last layer of
+    the 48-layer stack), and the E=256 variant with Q2.  ids and the
+    permutation in full, 64 sampled tokens against the oracle."""
     w = synth.WORKLOADS[wid]
-    print(f"workload {w.name}", flush=True)
-    L = synth.gen_layer(w, layer=0)
-    x = synth.gen_x(w, layer=0)
+    print(f"workload {w.name} layer {layer}", flush=True)
+    L = synth.gen_layer(w, layer=layer)
+    x = synth.gen_x(w, layer=layer)
     _, b = _run_layer(w, L, x)
-    rng = np.random.default_rng(wid)
+    rng = np.random.default_rng(wid * 100 + layer)
     sample = np.sort(rng.choice(w.T, size=64, replace=False))
     err = _check(w, L, x, b, sample=sample)
     print(f"max|err|/rms (sampled) = {err:.3e}")
