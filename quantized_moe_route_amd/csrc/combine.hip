@@ -6,15 +6,17 @@
 //   out[t] = y_shared[t] + sum_j w[t][j] * y_pairs[pair_pos[t*k+j]]
 // A pure streaming gather: one thread per 4 output columns, fp32, shared term
 // first then j = 0..k-1 (fixed order, deterministic).  The pair positions and
-// weights of a batch of 8 j are loaded first, then the batch's 8 rows all at
-// once, so each thread keeps 8 row loads in flight instead of one.  A pair
+// weights of a batch of 10 j are loaded first, then the batch's 10 rows all
+// at once (nontemporal: each row is read once), so each thread keeps 10 row
+// loads in flight instead of one.  A pair
 // that route tail-skip dropped (pair_pos -1) adds nothing (its load reads
 // row 0, unused).
 #include "common.h"
 
 namespace moe {
 
-constexpr int kCombineBatch = 8;
+// pairs whose rows are loaded together: a top-10 token's rows all at once
+constexpr int kCombineBatch = 10;
 
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y_pairs,
                                                       const float *__restrict__ y_shared,
@@ -38,8 +40,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
         }
         float4 v[kCombineBatch];
 #pragma unroll
-        for (int i = 0; i < kCombineBatch; ++i)
-            v[i] = *reinterpret_cast<const float4 *>(y_pairs + (size_t)(p[i] >= 0 ? p[i] : 0) * d + c);
+        for (int i = 0; i < kCombineBatch; ++i) {
+            // each y row is read once: nontemporal loads keep it out of the caches
+            const f32x4 t = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4 *>(y_pairs + (size_t)(p[i] >= 0 ? p[i] : 0) * d + c));
+            v[i] = make_float4(t[0], t[1], t[2], t[3]);
+        }
 #pragma unroll
         for (int i = 0; i < kCombineBatch; ++i) {
             if (j0 + i < k && p[i] >= 0) {

@@ -691,7 +691,9 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
                     const int row = it * (64 / LPR) + l / LPR;
                     const int grow = m * 32 + row;
                     const f32x4 v = *reinterpret_cast<const f32x4 *>(ep + row * G::EP1_PITCH + (l % LPR) * 4);
-                    if (grow < nrows) *reinterpret_cast<f32x4 *>(out + (size_t)(item.row0 + grow) * a.d + c0) = v;
+                    // y is read once, by the merge: nontemporal stores
+                    if (grow < nrows)
+                        __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(out + (size_t)(item.row0 + grow) * a.d + c0));
                 }
             }
             // the next m-tile overwrites the region: finish reading it first
