@@ -454,18 +454,21 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
         const QMatDev &W = (MODE == 0 && n >= NTW / 2) ? W1 : W0;
         const size_t u = ub[n] + kc;
         const uint8_t *lo = W.lo + u * 512;
-        br[n][0].lo = *reinterpret_cast<const u32x2 *>(lo + (h * 16 + rr) * 8);
-        br[n][1].lo = *reinterpret_cast<const u32x2 *>(lo + ((2 + h) * 16 + rr) * 8);
+        // a routed expert's weights are mostly read by one item: nontemporal
+        // (the shared expert's are re-read by every item: cached)
+        auto ld = [&](const auto *p) { return SH ? *p : __builtin_nontemporal_load(p); };
+        br[n][0].lo = ld(reinterpret_cast<const u32x2 *>(lo + (h * 16 + rr) * 8));
+        br[n][1].lo = ld(reinterpret_cast<const u32x2 *>(lo + ((2 + h) * 16 + rr) * 8));
         if constexpr (FMT == MOE_FMT_Q3_B32) {
             const uint8_t *hp = W.hi + u * 256;
-            br[n][0].hi = *reinterpret_cast<const uint32_t *>(hp + (h * 16 + rr) * 4);
-            br[n][1].hi = *reinterpret_cast<const uint32_t *>(hp + ((2 + h) * 16 + rr) * 4);
+            br[n][0].hi = ld(reinterpret_cast<const uint32_t *>(hp + (h * 16 + rr) * 4));
+            br[n][1].hi = ld(reinterpret_cast<const uint32_t *>(hp + ((2 + h) * 16 + rr) * 4));
         }
-        const u32x2 sc = *reinterpret_cast<const u32x2 *>(W.scale + u * 64 + rr * 4);
+        const u32x2 sc = ld(reinterpret_cast<const u32x2 *>(W.scale + u * 64 + rr * 4));
         br[n][0].sc = sc;
         br[n][1].sc = sc;
         if constexpr (FMT == MOE_FMT_Q2_B32) {
-            const u32x2 mn = *reinterpret_cast<const u32x2 *>(W.min + u * 64 + rr * 4);
+            const u32x2 mn = ld(reinterpret_cast<const u32x2 *>(W.min + u * 64 + rr * 4));
             br[n][0].mn = mn;
             br[n][1].mn = mn;
         }
