@@ -52,17 +52,19 @@ struct GateUpUnit {
 template <int FMT, int MT>
 __device__ __forceinline__ void gateup_load_w(GateUpUnit<FMT, MT> &U, const QMatDev &Wg,
                                               const QMatDev &Wu, size_t unit, int lane, int rr) {
-    U.lg = *reinterpret_cast<const u32x2 *>(Wg.lo + unit * 512 + lane * 8);
-    U.lu = *reinterpret_cast<const u32x2 *>(Wu.lo + unit * 512 + lane * 8);
+    // each weight is read once per call: nontemporal
+    auto ld = [](const auto *p) { return __builtin_nontemporal_load(p); };
+    U.lg = ld(reinterpret_cast<const u32x2 *>(Wg.lo + unit * 512 + lane * 8));
+    U.lu = ld(reinterpret_cast<const u32x2 *>(Wu.lo + unit * 512 + lane * 8));
     if constexpr (FMT == MOE_FMT_Q3_B32) {
-        U.hg = *reinterpret_cast<const uint32_t *>(Wg.hi + unit * 256 + lane * 4);
-        U.hu = *reinterpret_cast<const uint32_t *>(Wu.hi + unit * 256 + lane * 4);
+        U.hg = ld(reinterpret_cast<const uint32_t *>(Wg.hi + unit * 256 + lane * 4));
+        U.hu = ld(reinterpret_cast<const uint32_t *>(Wu.hi + unit * 256 + lane * 4));
     }
-    U.sg = *reinterpret_cast<const u32x2 *>(Wg.scale + unit * 64 + rr * 4);
-    U.su = *reinterpret_cast<const u32x2 *>(Wu.scale + unit * 64 + rr * 4);
+    U.sg = ld(reinterpret_cast<const u32x2 *>(Wg.scale + unit * 64 + rr * 4));
+    U.su = ld(reinterpret_cast<const u32x2 *>(Wu.scale + unit * 64 + rr * 4));
     if constexpr (FMT == MOE_FMT_Q2_B32) {
-        U.mg = *reinterpret_cast<const u32x2 *>(Wg.min + unit * 64 + rr * 4);
-        U.mu = *reinterpret_cast<const u32x2 *>(Wu.min + unit * 64 + rr * 4);
+        U.mg = ld(reinterpret_cast<const u32x2 *>(Wg.min + unit * 64 + rr * 4));
+        U.mu = ld(reinterpret_cast<const u32x2 *>(Wu.min + unit * 64 + rr * 4));
     }
 }
 
@@ -334,10 +336,11 @@ __device__ __forceinline__ void down_load_w(DownW<FMT, MT, NW> &Wt, const QMatDe
         int u = u0 + NW * b;
         u = u < KC ? u : KC - 1;   // clamped: unconditional loads, unused past KC
         const size_t unit = ubase + u;
-        Wt.lw[b] = *reinterpret_cast<const u32x2 *>(W.lo + unit * 512 + lane * 8);
-        if constexpr (FMT == MOE_FMT_Q3_B32) Wt.hw[b] = *reinterpret_cast<const uint32_t *>(W.hi + unit * 256 + lane * 4);
-        Wt.sw[b] = *reinterpret_cast<const u32x2 *>(W.scale + unit * 64 + rr * 4);
-        if constexpr (FMT == MOE_FMT_Q2_B32) Wt.mw[b] = *reinterpret_cast<const u32x2 *>(W.min + unit * 64 + rr * 4);
+        auto ld = [](const auto *p) { return __builtin_nontemporal_load(p); };   // read once
+        Wt.lw[b] = ld(reinterpret_cast<const u32x2 *>(W.lo + unit * 512 + lane * 8));
+        if constexpr (FMT == MOE_FMT_Q3_B32) Wt.hw[b] = ld(reinterpret_cast<const uint32_t *>(W.hi + unit * 256 + lane * 4));
+        Wt.sw[b] = ld(reinterpret_cast<const u32x2 *>(W.scale + unit * 64 + rr * 4));
+        if constexpr (FMT == MOE_FMT_Q2_B32) Wt.mw[b] = ld(reinterpret_cast<const u32x2 *>(W.min + unit * 64 + rr * 4));
     }
 }
 
