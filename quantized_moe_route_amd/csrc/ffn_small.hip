@@ -131,6 +131,7 @@ __device__ __forceinline__ void gateup_block(const GateUpUnit<FMT, MT> &U, f32x4
 #endif
 constexpr int kBatch = MOE_DECODE_BATCH;   // units prefetched per wave per batch
 
+constexpr size_t kXsMaxBytes = 32768;   // x staged in LDS by the gate/up kernel (2..8 tokens)
 constexpr int kPfPieces = 4;   // 16-byte pieces per thread (covers 3 down tiles)
 
 // The down-projection weights of output tiles ot = nt, nt + G, nt + 2G, ...
@@ -182,13 +183,13 @@ __device__ __forceinline__ void down_prefetch(u32x4 (&pf)[kPfPieces], const QMat
 // the weights; a group row's token (its pair's entry in sorted_pair) is
 // needed only when wave 0 picks its row out of the sums.  Each output row is
 // the same dot product either way.
-template <int FMT, int IMAX, int NW>
+template <int FMT, int IMAX, int NW, bool XL>
 __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &up, const QMatDev &sgate,
                                             const QMatDev &sup, const uint16_t *__restrict__ x, int T, int k, int d,
                                             int f, const int32_t *__restrict__ sorted_pair, const Group &grp,
                                             int nt, float (*red)[2][IMAX][64], uint16_t *__restrict__ h_hi,
                                             uint16_t *__restrict__ h_lo, const QMatDev &down,
-                                            const QMatDev &sdown) {
+                                            const QMatDev &sdown, uint16_t *xs) {
     static_assert(NW > 1, "token rows: K split over waves");
     constexpr bool kPrefetch = IMAX == 1;   // single-token batch
     const int lane = __lane_id();
@@ -215,20 +216,46 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
     f32x4 ag[1], au[1];
     ag[0] = f32x4{0.f, 0.f, 0.f, 0.f};
     au[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t *xrow[1] = {x + (size_t)(rr < T ? rr : T - 1) * d};
+    const int xr = rr < T ? rr : T - 1;   // the token row of this lane's matrix row
+    const uint16_t *xrow[1] = {x + (size_t)xr * d};
+    const int cpr = d / 8;                // 16-byte chunks per x row
     u32x4 pf[kPfPieces];
-    for (int u0 = wv; u0 < KC; u0 += NW * kBatch) {
-        GateUpUnit<FMT, 1> U[kBatch];
+    GateUpUnit<FMT, 1> U[kBatch];
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int u = u0 + NW * b;
-            if (u < KC) gateup_load_w(U[b], Wg, Wu, ubase + u, lane, rr);
+    for (int b = 0; b < kBatch; ++b) {
+        const int u = wv + NW * b;
+        if (u < KC) gateup_load_w(U[b], Wg, Wu, ubase + u, lane, rr);
+    }
+    if constexpr (XL) {
+        // x [T][d] into LDS once per workgroup by global-to-LDS copies (no
+        // registers held): chunk c of row r goes to r * cpr + (c ^ (r & 7)),
+        // so the T rows read at one column fall in different banks
+        const int nch = T * cpr;
+        for (int q = wv; q * 64 < nch; q += NW) {
+            const int L = q * 64 + lane;
+            if (L < nch) {
+                const int r = L / cpr, cs = L - r * cpr;
+                copy_to_lds16(x + (size_t)r * d + (size_t)(cs ^ (r & 7)) * 8, xs + (size_t)q * 512);
+            }
+        }
+        wait_vm<0>();   // the copies and the first weights
+        __syncthreads();
+    }
+    for (int u0 = wv; u0 < KC; u0 += NW * kBatch) {
+        if (u0 != wv) {
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int u = u0 + NW * b;
+                if (u < KC) gateup_load_w(U[b], Wg, Wu, ubase + u, lane, rr);
+            }
         }
         __asm__ volatile("" ::: "memory");
+        if constexpr (!XL) {
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int u = u0 + NW * b;
-            if (u < KC) gateup_load_x(U[b], u, gq, xrow);
+            for (int b = 0; b < kBatch; ++b) {
+                const int u = u0 + NW * b;
+                if (u < KC) gateup_load_x(U[b], u, gq, xrow);
+            }
         }
         if (kPrefetch && u0 == wv) {
             __asm__ volatile("" ::: "memory");
@@ -237,6 +264,15 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
             if (u0 + NW * b < KC) {
+                if constexpr (XL) {
+                    const int u = u0 + NW * b;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int c = u * 16 + j * 4 + gq;
+                        U[b].A[0][j] = *reinterpret_cast<const u32x4 *>(
+                            xs + ((size_t)xr * cpr + (c ^ (xr & 7))) * 8);
+                    }
+                }
                 gateup_block<FMT, 1, IMAX, 0>(U[b], ag, au);
                 gateup_block<FMT, 1, IMAX, 1>(U[b], ag, au);
                 gateup_block<FMT, 1, IMAX, 2>(U[b], ag, au);
@@ -486,13 +522,14 @@ __device__ __forceinline__ void combine_tile(const CombineArgs &cb, const float 
 // expert, slots 1 .. min(E, P) the routed groups); NW waves split K.  The
 // first tile of each slot also records the slot's group (nrows 0: none) in
 // `table`, so the down kernel reads it with one load.
-template <int FMT, int IMAX, int NW>
+template <int FMT, int IMAX, int NW, bool XL>
 __global__ __launch_bounds__(64 * NW) void gateup_small_kernel(
     QMatDev gate, QMatDev up, QMatDev sgate, QMatDev sup, const uint16_t *__restrict__ x, int T,
     int k, int d, int f, int E, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ sorted_pair, uint16_t *__restrict__ h_hi,
     uint16_t *__restrict__ h_lo, Group *__restrict__ table, QMatDev down, QMatDev sdown, int slot0) {
     __shared__ float red[NW][2][IMAX][64];
+    extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];   // XL: x, T * d halves
     Group grp;
     const bool found = find_group(offsets, E, T, T * k, slot0 + (int)blockIdx.y, grp);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -500,8 +537,8 @@ __global__ __launch_bounds__(64 * NW) void gateup_small_kernel(
         *reinterpret_cast<u32x4 *>(&table[blockIdx.y]) = __builtin_bit_cast(u32x4, found ? grp : none);
     }
     if (!found) return;
-    gateup_task<FMT, IMAX, NW>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp, blockIdx.x, red, h_hi,
-                               h_lo, down, sdown);
+    gateup_task<FMT, IMAX, NW, XL>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp, blockIdx.x, red, h_hi,
+                                   h_lo, down, sdown, xs_dyn);
 }
 
 // grid: (d_model/16 row tiles, group slots); NW waves split K = d_ff.  FUSE:
@@ -551,10 +588,19 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
 #define MOE_DN_WAVES 2
 #endif
     constexpr int NWG = MOE_GU_WAVES, NWD = MOE_DN_WAVES;   // waves per workgroup (split K)
-    hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG>), dim3(f / 16, slots),
-                       dim3(64 * NWG), 0, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up), x,
-                       T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, table, qm(L.down), qm(L.sh_down),
-                       slot0);
+    // two to eight tokens: x staged in LDS (32 KiB at most), which frees the
+    // registers that held it, so more waves keep weight loads in flight
+    const size_t xbytes = (size_t)T * d * 2;
+    if (IMAX >= 2 && T <= 8 && xbytes <= kXsMaxBytes)
+        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, IMAX >= 2>), dim3(f / 16, slots),
+                           dim3(64 * NWG), (unsigned)xbytes, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up),
+                           x, T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, table, qm(L.down), qm(L.sh_down),
+                           slot0);
+    else
+        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, false>), dim3(f / 16, slots),
+                           dim3(64 * NWG), 0, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up), x,
+                           T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, table, qm(L.down), qm(L.sh_down),
+                           slot0);
     if (cb.out)
         hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, true>), dim3(d / 16, slots),
                            dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, d, f, table,
