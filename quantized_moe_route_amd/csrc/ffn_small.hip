@@ -130,6 +130,9 @@ __device__ __forceinline__ void gateup_block(const GateUpUnit<FMT, MT> &U, f32x4
 #define MOE_DECODE_BATCH 4
 #endif
 constexpr int kBatch = MOE_DECODE_BATCH;   // units prefetched per wave per batch
+// down: K = d_ff = 768 is 6 units, 3 per wave of two; a batch of 4 held a
+// fourth, unused unit's registers (166 -> 128 VGPRs at 16 tokens)
+constexpr int kDownBatch = 3;
 
 constexpr size_t kXsMaxBytes = 32768;   // x staged in LDS by the gate/up kernel (2..8 tokens)
 constexpr int kPfPieces = 4;   // 16-byte pieces per thread (covers 3 down tiles)
@@ -353,7 +356,7 @@ __device__ __forceinline__ void down_block(const DownUnit<FMT, MT> &U, f32x4 *ac
 // loadable before h is needed: the weights do not depend on it.
 template <int FMT, int MT, int NW>
 struct DownW {
-    static constexpr int NB = kBatch;
+    static constexpr int NB = kDownBatch;
     u32x2 lw[NB], sw[NB], mw[NB];
     uint32_t hw[NB];
 };
