@@ -186,7 +186,7 @@ __device__ __forceinline__ void down_prefetch(u32x4 (&pf)[kPfPieces], const QMat
 // the weights; a group row's token (its pair's entry in sorted_pair) is
 // needed only when wave 0 picks its row out of the sums.  Each output row is
 // the same dot product either way.
-template <int FMT, int IMAX, int NW, bool XL>
+template <int FMT, int IMAX, int NW, bool XL, int TPW>
 __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &up, const QMatDev &sgate,
                                             const QMatDev &sup, const uint16_t *__restrict__ x, int T, int k, int d,
                                             int f, const int32_t *__restrict__ sorted_pair, const Group &grp,
@@ -194,9 +194,14 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
                                             uint16_t *__restrict__ h_lo, const QMatDev &down,
                                             const QMatDev &sdown, uint16_t *xs) {
     static_assert(NW > 1, "token rows: K split over waves");
-    constexpr bool kPrefetch = IMAX == 1;   // single-token batch
+    static_assert(TPW == 1 || XL, "several tiles per workgroup share the staged x");
+    constexpr bool kPrefetch = IMAX == 1 && TPW == 1;   // single-token batch
     const int lane = __lane_id();
-    const int wv = wave_uniform(threadIdx.x >> 6);
+    // TPW tiles per workgroup: waves [NW g, NW g + NW) take tile nt + g
+    const int wall = wave_uniform(threadIdx.x >> 6);
+    const int wv = wall % NW, tg = wall / NW;
+    nt += tg;
+    red += tg * NW;
     const int gq = lane >> 4, rr = lane & 15;
     const bool shared = grp.expert < 0;
     const QMatDev Wg = shared ? sgate : gate;
@@ -234,7 +239,7 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
         // registers held): chunk c of row r goes to r * cpr + (c ^ (r & 7)),
         // so the T rows read at one column fall in different banks
         const int nch = T * cpr;
-        for (int q = wv; q * 64 < nch; q += NW) {
+        for (int q = wall; q * 64 < nch; q += NW * TPW) {
             const int L = q * 64 + lane;
             if (L < nch) {
                 const int r = L / cpr, cs = L - r * cpr;
@@ -557,13 +562,13 @@ __device__ __forceinline__ void combine_tile(const CombineArgs &cb, const float 
 // expert, slots 1 .. min(E, P) the routed groups); NW waves split K.  The
 // first tile of each slot also records the slot's group (nrows 0: none) in
 // `table`, so the down kernel reads it with one load.
-template <int FMT, int IMAX, int NW, bool XL>
-__global__ __launch_bounds__(64 * NW) void gateup_small_kernel(
+template <int FMT, int IMAX, int NW, bool XL, int TPW>
+__global__ __launch_bounds__(64 * NW * TPW) void gateup_small_kernel(
     QMatDev gate, QMatDev up, QMatDev sgate, QMatDev sup, const uint16_t *__restrict__ x, int T,
     int k, int d, int f, int E, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ sorted_pair, uint16_t *__restrict__ h_hi,
     uint16_t *__restrict__ h_lo, Group *__restrict__ table, QMatDev down, QMatDev sdown, int slot0) {
-    __shared__ float red[NW][2][IMAX][64];
+    __shared__ float red[NW * TPW][2][IMAX][64];
     extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];   // XL: x, T * d halves
     Group grp;
     const bool found = find_group(offsets, E, T, T * k, slot0 + (int)blockIdx.y, grp);
@@ -572,8 +577,8 @@ __global__ __launch_bounds__(64 * NW) void gateup_small_kernel(
         *reinterpret_cast<u32x4 *>(&table[blockIdx.y]) = __builtin_bit_cast(u32x4, found ? grp : none);
     }
     if (!found) return;
-    gateup_task<FMT, IMAX, NW, XL>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp, blockIdx.x, red, h_hi,
-                                   h_lo, down, sdown, xs_dyn);
+    gateup_task<FMT, IMAX, NW, XL, TPW>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp,
+                                        (int)blockIdx.x * TPW, red, h_hi, h_lo, down, sdown, xs_dyn);
 }
 
 // grid: (d_model/16 row tiles, group slots); NW waves split K = d_ff.  FUSE:
@@ -628,12 +633,19 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
     // registers that held it, so more waves keep weight loads in flight
     const size_t xbytes = (size_t)T * d * 2;
     if (IMAX >= 2 && T <= 8 && xbytes <= kXsMaxBytes)
-        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, IMAX >= 2>), dim3(f / 16, slots),
+        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, IMAX >= 2, 1>), dim3(f / 16, slots),
                            dim3(64 * NWG), (unsigned)xbytes, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up),
                            x, T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, table, qm(L.down), qm(L.sh_down),
                            slot0);
+    else if (IMAX >= 2 && T <= 16 && xbytes <= 2 * kXsMaxBytes && (f / 16) % 2 == 0)
+        // 9 to 16 tokens: x takes up to 64 KiB, so one workgroup of eight
+        // waves serves two column tiles with one copy
+        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, IMAX >= 2, IMAX >= 2 ? 2 : 1>), dim3(f / 32, slots),
+                           dim3(2 * 64 * NWG), (unsigned)xbytes, s, qm(L.gate), qm(L.up), qm(L.sh_gate),
+                           qm(L.sh_up), x, T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, table, qm(L.down),
+                           qm(L.sh_down), slot0);
     else
-        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, false>), dim3(f / 16, slots),
+        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, false, 1>), dim3(f / 16, slots),
                            dim3(64 * NWG), 0, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up), x,
                            T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, table, qm(L.down), qm(L.sh_down),
                            slot0);
