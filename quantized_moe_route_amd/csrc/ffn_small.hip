@@ -134,7 +134,7 @@ constexpr int kBatch = MOE_DECODE_BATCH;   // units prefetched per wave per batc
 // fourth, unused unit's registers (166 -> 128 VGPRs at 16 tokens)
 constexpr int kDownBatch = 3;
 
-constexpr size_t kXsMaxBytes = 32768;   // x staged in LDS by the gate/up kernel (2..8 tokens)
+constexpr size_t kXsMaxBytes = 32768;   // x staged in LDS by the gate/up kernel (up to 8 tokens)
 constexpr int kPfPieces = 4;   // 16-byte pieces per thread (covers 3 down tiles)
 
 // The down-projection weights of output tiles ot = nt, nt + G, nt + 2G, ...
@@ -629,11 +629,13 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
 #define MOE_DN_WAVES 2
 #endif
     constexpr int NWG = MOE_GU_WAVES, NWD = MOE_DN_WAVES;   // waves per workgroup (split K)
-    // two to eight tokens: x staged in LDS (32 KiB at most), which frees the
-    // registers that held it, so more waves keep weight loads in flight
+    // up to eight tokens: x staged in LDS (32 KiB at most), which frees the
+    // registers that held it, so more waves keep weight loads in flight, and
+    // reads each x byte from L2 once per workgroup instead of once per wave
+    // and lane group
     const size_t xbytes = (size_t)T * d * 2;
-    if (IMAX >= 2 && T <= 8 && xbytes <= kXsMaxBytes)
-        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, IMAX >= 2, 1>), dim3(f / 16, slots),
+    if (T <= 8 && xbytes <= kXsMaxBytes)
+        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, true, 1>), dim3(f / 16, slots),
                            dim3(64 * NWG), (unsigned)xbytes, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up),
                            x, T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, table, qm(L.down), qm(L.sh_down),
                            slot0);
