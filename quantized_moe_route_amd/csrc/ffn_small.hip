@@ -651,11 +651,11 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
                            dim3(64 * NWG), 0, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up), x,
                            T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, table, qm(L.down), qm(L.sh_down),
                            slot0);
-    // two to four tokens: the group's h rows (at most T of hi and of lo)
-    // staged in LDS (measured: T = 2 +9%, T = 4 +3% on Q2, neutral on Q3;
-    // at T = 8 it lost 1.5%)
+    // up to four tokens: the group's h rows (at most T of hi and of lo)
+    // staged in LDS (measured: T = 1 +0.7%, T = 2 +9%, T = 4 +3% on Q2,
+    // neutral on Q3; at T = 8 it lost 1.5%)
     const size_t hbytes = (size_t)2 * T * f * 2;
-    constexpr bool HLOK = IMAX >= 2 && MTD == 1;
+    constexpr bool HLOK = MTD == 1;
     const bool hl = HLOK && T <= 4 && hbytes <= kXsMaxBytes;
     if (cb.out && hl)
         hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, true, HLOK>), dim3(d / 16, slots),
