@@ -28,6 +28,10 @@
 //     tile, so one fp16 matrix-core step covers both halves.
 //   - four waves of a workgroup split K; partial sums meet in LDS in a fixed
 //     order.
+//   - up to 8 (gate/up: 16) tokens the activation rows are staged in LDS once
+//     per workgroup instead of being loaded into each wave's registers: fewer
+//     registers, more resident waves, and each byte read from L2 once per
+//     workgroup.
 #include "common.h"
 
 namespace moe {
@@ -185,7 +189,10 @@ __device__ __forceinline__ void down_prefetch(u32x4 (&pf)[kPfPieces], const QMat
 // group's rows, so the activation loads depend on nothing and go out with
 // the weights; a group row's token (its pair's entry in sorted_pair) is
 // needed only when wave 0 picks its row out of the sums.  Each output row is
-// the same dot product either way.
+// the same dot product either way.  XL: x is first copied into LDS once per
+// workgroup (global-to-LDS, no registers held) and the activation operands
+// are read from there; TPW > 1: one workgroup of TPW x NW waves serves TPW
+// column tiles with that one copy.
 template <int FMT, int IMAX, int NW, bool XL, int TPW>
 __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &up, const QMatDev &sgate,
                                             const QMatDev &sup, const uint16_t *__restrict__ x, int T, int k, int d,
