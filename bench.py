@@ -149,8 +149,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the library has "
+              "no multi-GPU path (the expert-parallel sharding it would use is not implemented).",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
