@@ -231,13 +231,13 @@ def main():
     if tf is not None and not 0 <= tf <= w.k:
         log(f"--tail-skip must lie in [0, {w.k}]")
         sys.exit(2)
-    fused = not args.separate_calls and tf is None
+    fused = not args.separate_calls
     ov = args.overlap_shared
-    if ov and not fused:
+    if ov and (not fused or tf is not None):
         log("--overlap-shared goes with the default calls (no --separate-calls / --tail-skip)")
         sys.exit(2)
     side = SideStream(device=dev) if ov else None
-    fuse_cmb = fused and not ov and w.T <= FUSE_COMBINE_TMAX
+    fuse_cmb = not args.separate_calls and not ov and w.T <= FUSE_COMBINE_TMAX
     run_layer(layer_of(0, 0), xs[0][0], buf, stream=sh, tail_from=tf, fused=fused, side=side,
               fuse_combine=fuse_cmb)
     hip.stream_synchronize(sh)
@@ -299,7 +299,11 @@ def main():
     def call(c, s, li):
         L = layer_of(s, li)
         x = xs[s][li]
-        if c == "shared_ffn":
+        if c == "route_dispatch" and tf is not None:
+            q.moe_route_dispatch_tail_skip(x, L.router, L.bias, buf.logits, w.T, w.d_model, w.n_experts, w.k,
+                                           tf, buf.ids, buf.w, buf.offsets, buf.sorted_pair, buf.pair_pos,
+                                           buf.ws, buf.ws_bytes, sh)
+        elif c == "shared_ffn":
             q.moe_shared_ffn(L.struct, x, w.T, buf.y_shared, buf.ws_sh, buf.ws_sh_bytes,
                              side.handle if side is not None else sh)
         elif c == "routed_ffn":
@@ -327,7 +331,7 @@ def main():
     if ov:
         calls = ["shared_ffn", "route_dispatch", "routed_ffn", "combine"]
     elif fuse_cmb:
-        calls = ["route_dispatch", "expert_ffn_combine"]
+        calls = (["route_dispatch"] if fused else ["route", "dispatch"]) + ["expert_ffn_combine"]
     else:
         calls = (["route_dispatch"] if fused else ["route", "dispatch"]) + ["expert_ffn", "combine"]
 

@@ -195,6 +195,18 @@ moe_status moe_route_dispatch(const uint16_t *x_bf16, const float *w_router, con
                               int32_t *pair_pos, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_route_dispatch_tail_skip -- moe_route followed by moe_dispatch_tail_skip
+ * (same tail_from), in one launch where the batch allows it (T <= 8 and
+ * k <= 64), as moe_route_dispatch does for moe_dispatch.  Writes exactly what
+ * the two calls write; tail_from outside [0, k] is MOE_ERR_INVALID_ARGUMENT.
+ */
+moe_status moe_route_dispatch_tail_skip(const uint16_t *x_bf16, const float *w_router, const float *bias,
+                                        float *logits, int32_t T, int32_t d_model, int32_t E, int32_t k,
+                                        int32_t tail_from, int32_t *topk_ids, float *topk_w, int32_t *offsets,
+                                        int32_t *sorted_pair, int32_t *pair_pos, void *ws, size_t ws_bytes,
+                                        void *stream);
+
+/*
  * moe_expert_ffn -- the selected experts and the shared expert.
  * [forum] "Strata의 동작 원리" and [guide] "Strata, Qwen, GSQ-RCO…": 10 routed
  * experts plus one shared expert per token per layer; [video] "픽업": the

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "_lib", "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_FMT_Q2_B32, MOE_FMT_Q3_B32 = 1, 2
 ENTRY_POINTS = ("moe_route", "moe_dispatch", "moe_dispatch_tail_skip", "moe_route_dispatch",
+                "moe_route_dispatch_tail_skip",
                 "moe_expert_ffn", "moe_routed_ffn", "moe_shared_ffn", "moe_expert_ffn_combine",
                 "moe_combine", "moe_workspace_size", "moe_workspace_init",
                 "moe_status_string", "moe_abi_version")
@@ -49,6 +50,8 @@ def _load():
     lib.moe_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.moe_dispatch_tail_skip.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.moe_route_dispatch.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_route_dispatch_tail_skip.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                                 vp, sz, vp]
     lib.moe_expert_ffn.argtypes = [C.POINTER(moe_layer), vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_routed_ffn.argtypes = [C.POINTER(moe_layer), vp, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.moe_shared_ffn.argtypes = [C.POINTER(moe_layer), vp, i32, vp, vp, sz, vp]
@@ -140,6 +143,15 @@ def moe_route_dispatch(x_bf16, w_router, bias, logits, T, d_model, E, k, topk_id
                                 _ptr(topk_ids), _ptr(topk_w), _ptr(offsets), _ptr(sorted_pair),
                                 _ptr(pair_pos), _ptr(ws), ws_bytes, _stream(stream))
     return _check(st, "moe_route_dispatch") if check else st
+
+def moe_route_dispatch_tail_skip(x_bf16, w_router, bias, logits, T, d_model, E, k, tail_from, topk_ids,
+                                 topk_w, offsets, sorted_pair, pair_pos, ws, ws_bytes, stream=None,
+                                 check=True):
+    st = lib.moe_route_dispatch_tail_skip(_ptr(x_bf16), _ptr(w_router), _ptr(bias), _ptr(logits), T, d_model,
+                                          E, k, tail_from, _ptr(topk_ids), _ptr(topk_w), _ptr(offsets),
+                                          _ptr(sorted_pair), _ptr(pair_pos), _ptr(ws), ws_bytes,
+                                          _stream(stream))
+    return _check(st, "moe_route_dispatch_tail_skip") if check else st
 
 
 def moe_expert_ffn(layer, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, ws, ws_bytes,

@@ -134,12 +134,14 @@ moe_status moe_dispatch_tail_skip(const int32_t *topk_ids, int32_t T, int32_t E,
                             stream);
 }
 
-moe_status moe_route_dispatch(const uint16_t *x_bf16, const float *w_router, const float *bias,
-                              float *logits, int32_t T, int32_t d_model, int32_t E, int32_t k,
-                              int32_t *topk_ids, float *topk_w, int32_t *offsets, int32_t *sorted_pair,
-                              int32_t *pair_pos, void *ws, size_t ws_bytes, void *stream) {
+static moe_status route_dispatch_checked(const uint16_t *x_bf16, const float *w_router, const float *bias,
+                                         float *logits, int32_t T, int32_t d_model, int32_t E, int32_t k,
+                                         int32_t tail_from, int32_t *topk_ids, float *topk_w, int32_t *offsets,
+                                         int32_t *sorted_pair, int32_t *pair_pos, void *ws, size_t ws_bytes,
+                                         void *stream) {
     // the checks of both calls, before anything is enqueued
     if (T < 0 || E < 1 || E > kMaxE || k < 1 || k > E) return MOE_ERR_INVALID_ARGUMENT;
+    if (tail_from < 0 || tail_from > k) return MOE_ERR_INVALID_ARGUMENT;
     if ((int64_t)T * k >= INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
     if (!w_router || !x_bf16 || !logits || !topk_ids || !topk_w || !offsets || !sorted_pair || !pair_pos)
         return MOE_ERR_INVALID_ARGUMENT;
@@ -153,11 +155,29 @@ moe_status moe_route_dispatch(const uint16_t *x_bf16, const float *w_router, con
     if (T == 0) return MOE_OK;
     if (T <= kRouteTile && k <= kWaveTopkMaxK)
         return launched(launch_route_small(x_bf16, w_router, bias, logits, T, d_model, E, k, topk_ids,
-                                           topk_w, ws, as_stream(stream), offsets, sorted_pair, pair_pos));
+                                           topk_w, ws, as_stream(stream), offsets, sorted_pair, pair_pos,
+                                           tail_from));
     const moe_status st = moe_route(x_bf16, w_router, bias, logits, T, d_model, E, k, topk_ids, topk_w, ws,
                                     ws_bytes, stream);
     if (st != MOE_OK) return st;
-    return moe_dispatch(topk_ids, T, E, k, offsets, sorted_pair, pair_pos, ws, ws_bytes, stream);
+    return dispatch_checked(topk_ids, T, E, k, tail_from, offsets, sorted_pair, pair_pos, ws, ws_bytes, stream);
+}
+
+moe_status moe_route_dispatch(const uint16_t *x_bf16, const float *w_router, const float *bias,
+                              float *logits, int32_t T, int32_t d_model, int32_t E, int32_t k,
+                              int32_t *topk_ids, float *topk_w, int32_t *offsets, int32_t *sorted_pair,
+                              int32_t *pair_pos, void *ws, size_t ws_bytes, void *stream) {
+    return route_dispatch_checked(x_bf16, w_router, bias, logits, T, d_model, E, k, k, topk_ids, topk_w, offsets,
+                                  sorted_pair, pair_pos, ws, ws_bytes, stream);
+}
+
+moe_status moe_route_dispatch_tail_skip(const uint16_t *x_bf16, const float *w_router, const float *bias,
+                                        float *logits, int32_t T, int32_t d_model, int32_t E, int32_t k,
+                                        int32_t tail_from, int32_t *topk_ids, float *topk_w, int32_t *offsets,
+                                        int32_t *sorted_pair, int32_t *pair_pos, void *ws, size_t ws_bytes,
+                                        void *stream) {
+    return route_dispatch_checked(x_bf16, w_router, bias, logits, T, d_model, E, k, tail_from, topk_ids, topk_w,
+                                  offsets, sorted_pair, pair_pos, ws, ws_bytes, stream);
 }
 
 static moe_status ffn_checked(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, int32_t k,

@@ -289,7 +289,7 @@ __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + _
 hipError_t launch_route_small(const uint16_t *x, const float *wr, const float *bias, float *logits,
                               int T, int d, int E, int k, int32_t *ids, float *w, void *ws,
                               hipStream_t s, int32_t *offsets = nullptr, int32_t *sorted_pair = nullptr,
-                              int32_t *pair_pos = nullptr);
+                              int32_t *pair_pos = nullptr, int tail_from = -1);
 hipError_t launch_router_gemm(const uint16_t *x, const float *wr, const float *bias, float *logits,
                               int T, int d, int E, void *ws, hipStream_t s);
 size_t router_gemm_ws_bytes(int d, int E);

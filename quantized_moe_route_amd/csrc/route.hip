@@ -297,7 +297,8 @@ __global__ __launch_bounds__(512) void route_small_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
     float *__restrict__ logits, int T, int d, int E, int k, int32_t *__restrict__ ids,
     float *__restrict__ w, int32_t *__restrict__ counters, float *__restrict__ partial,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pair_pos) {
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pair_pos,
+    int tail_from) {
     __shared__ float red[8][kMaxSmallT][64];
     __shared__ int32_t sel_ids[kMaxSmallT * kWaveTopkMaxK];   // the batch's picks, for the listing
     __shared__ uint32_t emask[1024];                          // listing: tokens (bits) per expert
@@ -414,15 +415,19 @@ __global__ __launch_bounds__(512) void route_small_kernel(
         // The listing: a token picks an expert at most once, so the pairs of
         // expert e are the tokens in emask[e]; pair p = t k + j goes to
         // (pairs of lower experts) + (tokens before t in emask[e]), the
-        // position a stable sort by expert gives.
+        // position a stable sort by expert gives.  Bit 31 marks an expert
+        // some token picked at a rank below tail_from (route tail-skip; with
+        // tail_from = k every picked expert): the others list no pairs.
+        constexpr uint32_t KEEP = 1u << 31;
         for (int e = tid; e < 1024; e += 512) emask[e] = 0u;
         __syncthreads();
         const int P = T * k;
-        if (tid < P) atomicOr(&emask[sel_ids[tid]], 1u << (tid / k));
+        if (tid < P) atomicOr(&emask[sel_ids[tid]], (1u << (tid / k)) | (tid % k < tail_from ? KEEP : 0u));
         __syncthreads();
         // exclusive scan of the per-expert counts, two experts per thread
         const int e0 = 2 * tid;
-        const int c0 = __popc(emask[e0]), c1 = __popc(emask[e0 + 1]);
+        auto kept_count = [](uint32_t m) { return (m & KEEP) ? __popc(m & ~KEEP) : 0; };
+        const int c0 = kept_count(emask[e0]), c1 = kept_count(emask[e0 + 1]);
         const int incl = wave_incl_scan(c0 + c1);
         if (__lane_id() == 63) wtot[wv] = incl;
         __syncthreads();
@@ -437,9 +442,14 @@ __global__ __launch_bounds__(512) void route_small_kernel(
         __syncthreads();
         if (tid < P) {
             const int e = sel_ids[tid], t = tid / k;
-            const int pos = eoff[e] + __popc(emask[e] & ((1u << t) - 1u));
-            sorted_pair[pos] = tid;
-            pair_pos[tid] = pos;
+            const uint32_t m = emask[e];
+            if (m & KEEP) {
+                const int pos = eoff[e] + __popc(m & ((1u << t) - 1u));
+                sorted_pair[pos] = tid;
+                pair_pos[tid] = pos;
+            } else {
+                pair_pos[tid] = -1;
+            }
         }
         return;
     }
@@ -457,12 +467,13 @@ size_t route_ws_bytes(int d, int E, int T) {
 
 hipError_t launch_route_small(const uint16_t *x, const float *wr, const float *bias, float *logits,
                               int T, int d, int E, int k, int32_t *ids, float *w, void *ws,
-                              hipStream_t s, int32_t *offsets, int32_t *sorted_pair, int32_t *pair_pos) {
+                              hipStream_t s, int32_t *offsets, int32_t *sorted_pair, int32_t *pair_pos,
+                              int tail_from) {
     int32_t *counters = reinterpret_cast<int32_t *>(ws);
     float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + kWsHeader);
     dim3 grid((E + 63) / 64, d / 128, (T + kRouteTile - 1) / kRouteTile);
     hipLaunchKernelGGL(route_small_kernel, grid, dim3(512), 0, s, x, wr, bias, logits, T, d, E, k,
-                       ids, w, counters, partial, offsets, sorted_pair, pair_pos);
+                       ids, w, counters, partial, offsets, sorted_pair, pair_pos, tail_from < 0 ? k : tail_from);
     return hipGetLastError();
 }
 

@@ -11,8 +11,9 @@ import dataclasses
 import torch
 
 from . import (MOE_FMT_Q2_B32, hip, make_layer, moe_combine, moe_dispatch, moe_dispatch_tail_skip,
-               moe_expert_ffn, moe_expert_ffn_combine, moe_route, moe_route_dispatch, moe_routed_ffn,
-               moe_shared_ffn, moe_workspace_init, moe_workspace_size)
+               moe_expert_ffn, moe_expert_ffn_combine, moe_route, moe_route_dispatch,
+               moe_route_dispatch_tail_skip, moe_routed_ffn, moe_shared_ffn, moe_workspace_init,
+               moe_workspace_size)
 
 MATS = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
 
@@ -122,8 +123,12 @@ def run_layer(layer: DeviceLayer, x, b: Buffers, stream=None, logits_in=False, t
         hip.stream_wait_event(side.handle, side.fork)
         moe_shared_ffn(layer.struct, x, T, b.y_shared, b.ws_sh, b.ws_sh_bytes, side.handle)
         side.join.record(side.handle)
-    if fused:
-        assert not logits_in and tail_from is None
+    if fused and tail_from is not None:
+        assert not logits_in
+        moe_route_dispatch_tail_skip(x, layer.router, layer.bias, b.logits, T, d, E, k, tail_from, b.ids,
+                                     b.w, b.offsets, b.sorted_pair, b.pair_pos, b.ws, b.ws_bytes, stream)
+    elif fused:
+        assert not logits_in
         moe_route_dispatch(x, layer.router, layer.bias, b.logits, T, d, E, k, b.ids, b.w, b.offsets,
                            b.sorted_pair, b.pair_pos, b.ws, b.ws_bytes, stream)
     elif logits_in:

@@ -130,6 +130,15 @@ def test_routed_and_shared_ffn_validation(q):
     assert f(shared_only, A, 0, 2, A, A, A, A, A, ws) == q.MOE_ERR_INVALID_ARGUMENT
 
 
+def test_route_dispatch_tail_skip_validation(q):
+    rd = lambda *a: q.moe_route_dispatch_tail_skip(*a, check=False)
+    # (x, wr, bias, logits, T, d, E, k, tail_from, ids, w, offsets, sorted_pair, pair_pos, ws, ws_bytes)
+    assert rd(A, A, None, A, 1, 2048, 16, 2, 3, A, A, A, A, A, A, 1 << 24) == q.MOE_ERR_INVALID_ARGUMENT
+    assert rd(A, A, None, A, 1, 2048, 16, 2, -1, A, A, A, A, A, A, 1 << 24) == q.MOE_ERR_INVALID_ARGUMENT
+    assert rd(A, A, None, A, 1, 2048, 16, 2, 1, A, A, A, A, A, A, 4096) == q.MOE_ERR_WORKSPACE
+    assert rd(A, A, None, A, 0, 2048, 16, 2, 1, A, A, A, A, A, A, 1 << 24) == q.MOE_OK
+
+
 def test_ffn_combine_validation(q):
     f = lambda L, *a: q.moe_expert_ffn_combine(L, *a, check=False)
     ws = 1 << 24

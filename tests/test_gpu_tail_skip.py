@@ -114,3 +114,37 @@ def test_layer_tail_skip_shapes(q, fmt, T, E, k, tail_from):
     err, kept = _layer_case(w, L, x, tail_from, sample=sample)
     assert kept < T * k
     print(f"kept pairs {kept} of {T * k}, max|err|/rms = {err:.3e}")
+
+
+@pytest.mark.parametrize("T,tail_from", [(1, 6), (4, 3), (8, 0), (8, 10), (12, 6)])
+def test_route_dispatch_tail_skip_equals_two_calls(q, T, tail_from):
+    """moe_route_dispatch_tail_skip (one launch up to 8 tokens) writes what
+    moe_route then moe_dispatch_tail_skip write, bit for bit."""
+    E, k, d = 64, 10, 512
+    w = synth.custom(d, 256, E, k, T, fmt=1, zipf_s=1.3, wid=900 + T)
+    x = torch.from_numpy(synth.gen_x(w).view(np.int16)).cuda()
+    wr = torch.from_numpy(synth.gen_router(w)).cuda()
+    n_ws = q.moe_workspace_size(d, 256, E, T, k)
+    outs = []
+    for fused in (False, True):
+        ws = torch.zeros(n_ws + 256, dtype=torch.uint8, device="cuda")
+        ws = ws[(-ws.data_ptr()) % 256:][:n_ws]
+        lg = torch.full((T, E), 3.0, device="cuda")
+        ids = torch.full((T, k), -5, dtype=torch.int32, device="cuda")
+        wt = torch.full((T, k), -5.0, device="cuda")
+        off = torch.full((E + 1,), -5, dtype=torch.int32, device="cuda")
+        sp = torch.full((T * k,), -5, dtype=torch.int32, device="cuda")
+        pp = torch.full((T * k,), -5, dtype=torch.int32, device="cuda")
+        if fused:
+            q.moe_route_dispatch_tail_skip(x, wr, None, lg, T, d, E, k, tail_from, ids, wt, off, sp, pp, ws, n_ws)
+        else:
+            q.moe_route(x, wr, None, lg, T, d, E, k, ids, wt, ws, n_ws)
+            q.moe_dispatch_tail_skip(ids, T, E, k, tail_from, off, sp, pp, ws, n_ws)
+        torch.cuda.synchronize()
+        n = int(off[E].item())
+        outs.append([lg.cpu().numpy(), ids.cpu().numpy(), wt.cpu().numpy(), off.cpu().numpy(),
+                     sp[:n].cpu().numpy(), pp.cpu().numpy()])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    ref_off, ref_sp, ref_pp = oracle.dispatch_tail_skip(outs[1][1], E, tail_from)
+    assert np.array_equal(outs[1][3], ref_off) and np.array_equal(outs[1][5], ref_pp)
