@@ -278,9 +278,14 @@ void oracle_swiglu_row(const double *Wg, const double *Wu, const double *Wd, int
 
 /* Rows of the expert FFN for explicit (expert, token) pairs.  Row r uses
  * expert row_expert[r] (-1 = the shared expert) on token row_token[r].
- * Each distinct expert is dequantised once to dense doubles, then its rows are
- * evaluated with oracle_swiglu_row.  Results (double) go to y[r][0..d) and, if
- * h != NULL, h[r][0..f). */
+ * The rows are grouped by expert and cut into chunks of at most
+ * ORACLE_ROW_CHUNK rows; each chunk dequantises its expert to dense doubles
+ * and evaluates its rows with oracle_swiglu_row.  Chunks run in parallel (an
+ * expert used by thousands of rows, such as the shared one, is split over
+ * threads); every row is computed the same way whichever thread takes it.
+ * Results (double) go to y[r][0..d) and, if h != NULL, h[r][0..f). */
+#define ORACLE_ROW_CHUNK 128
+
 void oracle_expert_rows_f64(const oracle_qmat *gate, const oracle_qmat *up,
                             const oracle_qmat *down, const oracle_qmat *sh_gate,
                             const oracle_qmat *sh_up, const oracle_qmat *sh_down, int fmt,
@@ -288,43 +293,65 @@ void oracle_expert_rows_f64(const oracle_qmat *gate, const oracle_qmat *up,
                             const int32_t *row_expert, const int32_t *row_token, double *y,
                             double *h)
 {
-    /* experts in use: index E stands for the shared expert */
-    char *used = calloc((size_t)E + 1, 1);
+    /* rows listed expert by expert (index E stands for the shared expert) */
+    long *count = calloc((size_t)E + 2, sizeof(long));
     for (int r = 0; r < n_rows; ++r)
-        used[row_expert[r] < 0 ? E : row_expert[r]] = 1;
-    int n_used = 0;
-    int *list = malloc(sizeof(int) * ((size_t)E + 1));
+        count[(row_expert[r] < 0 ? E : row_expert[r]) + 1] += 1;
     for (int e = 0; e <= E; ++e)
-        if (used[e])
-            list[n_used++] = e;
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int i = 0; i < n_used; ++i) {
-        int e = list[i];
+        count[e + 1] += count[e];
+    int *by_expert = malloc(sizeof(int) * ((size_t)n_rows + 1));
+    long *fill = malloc(sizeof(long) * ((size_t)E + 1));
+    memcpy(fill, count, sizeof(long) * ((size_t)E + 1));
+    for (int r = 0; r < n_rows; ++r)
+        by_expert[fill[row_expert[r] < 0 ? E : row_expert[r]]++] = r;
+    /* chunks: (expert, first listed row, number of rows) */
+    long n_chunks = 0;
+    for (int e = 0; e <= E; ++e)
+        n_chunks += (count[e + 1] - count[e] + ORACLE_ROW_CHUNK - 1) / ORACLE_ROW_CHUNK;
+    long *chunk = malloc(sizeof(long) * 3 * ((size_t)n_chunks + 1));
+    long c = 0;
+    for (int e = 0; e <= E; ++e)
+        for (long i = count[e]; i < count[e + 1]; i += ORACLE_ROW_CHUNK) {
+            chunk[3 * c] = e;
+            chunk[3 * c + 1] = i;
+            chunk[3 * c + 2] = count[e + 1] - i < ORACLE_ROW_CHUNK ? count[e + 1] - i : ORACLE_ROW_CHUNK;
+            ++c;
+        }
+#pragma omp parallel
+    {
         double *Wg = malloc(sizeof(double) * (size_t)f * d);
         double *Wu = malloc(sizeof(double) * (size_t)f * d);
         double *Wd = malloc(sizeof(double) * (size_t)d * f);
-        if (e == E) {
-            oracle_dequant_matrix(sh_gate, fmt, f, d, 0, Wg);
-            oracle_dequant_matrix(sh_up, fmt, f, d, 0, Wu);
-            oracle_dequant_matrix(sh_down, fmt, d, f, 0, Wd);
-        } else {
-            oracle_dequant_matrix(gate, fmt, f, d, e, Wg);
-            oracle_dequant_matrix(up, fmt, f, d, e, Wu);
-            oracle_dequant_matrix(down, fmt, d, f, e, Wd);
-        }
-        for (int r = 0; r < n_rows; ++r) {
-            int re = row_expert[r] < 0 ? E : row_expert[r];
-            if (re != e)
-                continue;
-            oracle_swiglu_row(Wg, Wu, Wd, d, f, x + (long)row_token[r] * d,
-                              h ? h + (long)r * f : NULL, y + (long)r * d);
+        long have = -1; /* expert held in Wg, Wu, Wd by this thread */
+#pragma omp for schedule(dynamic, 1)
+        for (long i = 0; i < n_chunks; ++i) {
+            const long e = chunk[3 * i];
+            if (e != have) {
+                if (e == E) {
+                    oracle_dequant_matrix(sh_gate, fmt, f, d, 0, Wg);
+                    oracle_dequant_matrix(sh_up, fmt, f, d, 0, Wu);
+                    oracle_dequant_matrix(sh_down, fmt, d, f, 0, Wd);
+                } else {
+                    oracle_dequant_matrix(gate, fmt, f, d, (int)e, Wg);
+                    oracle_dequant_matrix(up, fmt, f, d, (int)e, Wu);
+                    oracle_dequant_matrix(down, fmt, d, f, (int)e, Wd);
+                }
+                have = e;
+            }
+            for (long q = chunk[3 * i + 1]; q < chunk[3 * i + 1] + chunk[3 * i + 2]; ++q) {
+                const int r = by_expert[q];
+                oracle_swiglu_row(Wg, Wu, Wd, d, f, x + (long)row_token[r] * d,
+                                  h ? h + (long)r * f : NULL, y + (long)r * d);
+            }
         }
         free(Wd);
         free(Wu);
         free(Wg);
     }
-    free(list);
-    free(used);
+    free(chunk);
+    free(fill);
+    free(by_expert);
+    free(count);
 }
 
 /* fp32-stored variant of oracle_expert_rows_f64 (y and h rounded once). */
