@@ -82,6 +82,15 @@ extern "C" {
 
 #define MOE_ABI_VERSION 1
 
+/* The workspace's error word: an int32 at this byte offset of every
+ * workspace.  Kernels that find their device-side input breaking a stated
+ * precondition set bits here instead of touching memory out of bounds; the
+ * bits stay set until moe_workspace_init clears the workspace.  A caller that
+ * wants to know reads the 4 bytes back (e.g. after a synchronisation). */
+#define MOE_WS_ERROR_OFFSET 3968
+#define MOE_WS_ERR_ID_RANGE 1  /* moe_dispatch*: an id outside [0, E)   */
+#define MOE_WS_ERR_ID_REPEAT 2 /* moe_dispatch*: a token names an expert twice */
+
 typedef enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARGUMENT = 1,
@@ -149,7 +158,13 @@ moe_status moe_route(const uint16_t *x_bf16, const float *w_router, const float 
  *               expert (stable).   pair_pos [P] int32: inverse permutation,
  *               sorted_pair[pair_pos[p]] == p.
  * Every id must lie in [0, E) and a token's k ids must be distinct (as
- * moe_route produces them); other input is a precondition violation.
+ * moe_route produces them); other input is a precondition violation.  It is
+ * detected on the device: a pair whose id lies outside [0, E) is left out of
+ * the listing (pair_pos = -1, offsets[E] counts the listed pairs) and sets
+ * MOE_WS_ERR_ID_RANGE in the workspace's error word; a repeated id sets
+ * MOE_WS_ERR_ID_REPEAT (both pairs then share one position).  Either way every
+ * listed entry is a valid pair, so the later calls stay in bounds.
+ * moe_validate_ids checks the same conditions on a host copy.
  */
 moe_status moe_dispatch(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k,
                         int32_t *offsets, int32_t *sorted_pair, int32_t *pair_pos, void *ws,
@@ -280,6 +295,15 @@ moe_status moe_expert_ffn_combine(const moe_layer *layer, const uint16_t *x_bf16
 moe_status moe_combine(const float *y_pairs, const float *y_shared, const int32_t *pair_pos,
                        const float *topk_w, int32_t T, int32_t k, int32_t d_model, float *out,
                        void *stream);
+
+/*
+ * moe_validate_ids -- host-side check of the routing ids that moe_dispatch
+ * expects: topk_ids_host is a HOST array [T][k]; every id must lie in [0, E)
+ * and a token's k ids must be distinct.  Returns MOE_OK, or
+ * MOE_ERR_INVALID_ARGUMENT (bad sizes, a null pointer, or an id that breaks
+ * the conditions).  Touches no device and enqueues nothing.
+ */
+moe_status moe_validate_ids(const int32_t *topk_ids_host, int32_t T, int32_t E, int32_t k);
 
 /* Workspace bytes that suffice for every call above with these sizes. */
 size_t moe_workspace_size(int32_t d_model, int32_t d_ff, int32_t E, int32_t T, int32_t k);

@@ -20,8 +20,10 @@ MOE_FMT_Q2_B32, MOE_FMT_Q3_B32 = 1, 2
 ENTRY_POINTS = ("moe_route", "moe_dispatch", "moe_dispatch_tail_skip", "moe_route_dispatch",
                 "moe_route_dispatch_tail_skip",
                 "moe_expert_ffn", "moe_routed_ffn", "moe_shared_ffn", "moe_expert_ffn_combine",
-                "moe_combine", "moe_workspace_size", "moe_workspace_init",
+                "moe_combine", "moe_validate_ids", "moe_workspace_size", "moe_workspace_init",
                 "moe_status_string", "moe_abi_version")
+MOE_WS_ERROR_OFFSET = 3968                          # byte offset of the workspace's error word
+MOE_WS_ERR_ID_RANGE, MOE_WS_ERR_ID_REPEAT = 1, 2    # its bits
 
 
 class MoeError(RuntimeError):
@@ -58,6 +60,8 @@ def _load():
     lib.moe_expert_ffn_combine.argtypes = [C.POINTER(moe_layer), vp, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                            vp, sz, vp]
     lib.moe_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
+    lib.moe_validate_ids.argtypes = [vp, i32, i32, i32]
+    lib.moe_validate_ids.restype = C.c_int
     lib.moe_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.moe_workspace_size.restype = sz
     lib.moe_workspace_init.argtypes = [vp, sz, vp]
@@ -106,6 +110,14 @@ def moe_abi_version() -> int:
 
 def moe_status_string(st: int) -> str:
     return status_string(st)
+
+
+def moe_validate_ids(topk_ids_host, T, E, k, check=True):
+    """topk_ids_host: a HOST int32 array [T][k] (numpy), checked on the host."""
+    import numpy as np
+    a = None if topk_ids_host is None else np.ascontiguousarray(topk_ids_host, dtype=np.int32)
+    st = lib.moe_validate_ids(None if a is None else a.ctypes.data, T, E, k)
+    return _check(st, "moe_validate_ids") if check else st
 
 
 def moe_workspace_size(d_model, d_ff, E, T, k) -> int:

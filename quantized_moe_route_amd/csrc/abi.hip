@@ -62,6 +62,22 @@ const char *moe_status_string(moe_status s) {
     return "unknown status";
 }
 
+moe_status moe_validate_ids(const int32_t *topk_ids_host, int32_t T, int32_t E, int32_t k) {
+    if (T < 0 || E < 1 || E > kMaxE || k < 1 || k > E) return MOE_ERR_INVALID_ARGUMENT;
+    if ((int64_t)T * k >= INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
+    if (T == 0) return MOE_OK;
+    if (!topk_ids_host) return MOE_ERR_INVALID_ARGUMENT;
+    // seen[e] holds the last token (+1) that named expert e
+    int32_t seen[kMaxE] = {0};
+    for (int32_t t = 0; t < T; ++t)
+        for (int32_t j = 0; j < k; ++j) {
+            const int32_t e = topk_ids_host[(int64_t)t * k + j];
+            if (e < 0 || e >= E || seen[e] == t + 1) return MOE_ERR_INVALID_ARGUMENT;
+            seen[e] = t + 1;
+        }
+    return MOE_OK;
+}
+
 size_t moe_workspace_size(int32_t d_model, int32_t d_ff, int32_t E, int32_t T, int32_t k) {
     if (d_model <= 0 || d_ff <= 0 || E <= 0 || T < 0 || k <= 0) return 0;
     size_t need = route_need(d_model, E, T);

@@ -30,6 +30,13 @@ constexpr size_t kCombineCnt = 4096;                       // byte offset of the
 constexpr size_t kWsHeader = kCombineCnt + (16384 / 16) * 128;
 constexpr int kRouteTile = 8;       // tokens per tile of the one-launch router
 // the one-launch router's tile tt counts its arrivals at counters[kCntLine * tt]
+// (tiles 0..15: bytes 0..2047)
+// The error word: sticky bits set by kernels that find a precondition
+// violated in their device-side input (zeroed by moe_workspace_init only).
+constexpr size_t kWsErrorWord = MOE_WS_ERROR_OFFSET;
+constexpr int kErrIdRange = MOE_WS_ERR_ID_RANGE;
+constexpr int kErrIdRepeat = MOE_WS_ERR_ID_REPEAT;
+static_assert(kWsErrorWord >= 2048 && kWsErrorWord + 4 <= kCombineCnt, "error word inside the router's 4 KiB");
 
 // ------------------------------------------------- cross-workgroup hand-off
 // Each XCD has its own L2, so data passed between workgroups is written and
@@ -295,7 +302,7 @@ hipError_t launch_router_gemm(const uint16_t *x, const float *wr, const float *b
 size_t router_gemm_ws_bytes(int d, int E);
 constexpr int kRouteSmallTMax = 128;   // T above this: router GEMM + top-k kernel
 constexpr int kWaveTopkMaxK = 64;      // register top-k (one wave per token) up to this k
-static_assert(kRouteSmallTMax / kRouteTile * kCntLine * 4 <= (int)kWsHeader, "tile counters exceed the header");
+static_assert(kRouteSmallTMax / kRouteTile * kCntLine * 4 <= 2048, "tile counters run into the error word");
 hipError_t launch_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w,
                        hipStream_t s);
 size_t route_ws_bytes(int d, int E, int T);

@@ -19,6 +19,12 @@
 // picks it at a rank j < tail_from; the pairs of the other experts are left
 // out of the listing (pair_pos = -1) and offsets count kept pairs only.  The
 // kernels take a keep flag per expert (nullptr: every pair is kept).
+//
+// Ids are caller input here, so every id is range-checked before it indexes
+// anything: a pair whose id lies outside [0, E) is left out of the listing
+// (pair_pos = -1) and sets bit kErrIdRange of the workspace's error word; a
+// token that names one expert twice sets bit kErrIdRepeat (its two pairs then
+// share one position, so every listed entry is still a valid pair).
 #include "common.h"
 
 namespace moe {
@@ -27,26 +33,38 @@ __device__ __forceinline__ unsigned long long below_mask(int lane) {
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+__device__ __forceinline__ bool id_ok(int e, int E) { return (unsigned)e < (unsigned)E; }
+
 // one wave: OR each token's bit into masks[e] for its k experts (kept ones,
 // if keep is given); with mark given, also flag mark[e] for the experts
-// picked at a rank below tail_from
-__device__ __forceinline__ void build_chunk_masks(const int32_t *__restrict__ ids, int T, int k,
+// picked at a rank below tail_from.  Ids outside [0, E) and repeated ids are
+// reported in *err (the workspace's error word).
+__device__ __forceinline__ void build_chunk_masks(const int32_t *__restrict__ ids, int T, int E, int k,
                                                   int chunk, unsigned long long *masks,
-                                                  const int32_t *keep, int32_t *mark = nullptr,
-                                                  int tail_from = 0) {
+                                                  const int32_t *keep, int32_t *err,
+                                                  int32_t *mark = nullptr, int tail_from = 0) {
     const int lane = __lane_id();
     const int t = chunk * 64 + lane;
     if (t < T) {
         const unsigned long long bit = 1ull << lane;
+        int bad = 0;
         for (int j = 0; j < k; ++j) {
             const int e = ids[(size_t)t * k + j];
-            if (!keep || keep[e]) atomicOr(&masks[e], bit);
+            if (!id_ok(e, E)) {
+                bad |= kErrIdRange;
+                continue;
+            }
+            if (!keep || keep[e]) {
+                const unsigned long long old = atomicOr(&masks[e], bit);
+                if (old & bit) bad |= kErrIdRepeat;
+            }
             if (mark && j < tail_from) mark[e] = 1;
         }
+        if (bad && err) atomicOr(err, bad);
     }
 }
 
-__device__ __forceinline__ void write_chunk_positions(const int32_t *__restrict__ ids, int T, int k,
+__device__ __forceinline__ void write_chunk_positions(const int32_t *__restrict__ ids, int T, int E, int k,
                                                       int chunk, const unsigned long long *masks,
                                                       const int32_t *base /* [E] for chunk */,
                                                       int32_t *__restrict__ sorted_pair,
@@ -59,7 +77,7 @@ __device__ __forceinline__ void write_chunk_positions(const int32_t *__restrict_
     for (int j = 0; j < k; ++j) {
         const int e = ids[(size_t)t * k + j];
         const int p = t * k + j;
-        if (keep && !keep[e]) {
+        if (!id_ok(e, E) || (keep && !keep[e])) {
             pair_pos[p] = -1;
             continue;
         }
@@ -71,13 +89,14 @@ __device__ __forceinline__ void write_chunk_positions(const int32_t *__restrict_
 
 // keep[e] = 1 iff some token picks e at a rank below tail_from (keep zeroed
 // before); every writer stores the same value
-__device__ __forceinline__ void mark_kept(const int32_t *__restrict__ ids, int T, int k, int tail_from,
+__device__ __forceinline__ void mark_kept(const int32_t *__restrict__ ids, int T, int E, int k, int tail_from,
                                           int32_t *keep, int i0, int stride) {
     const int n = T * (tail_from < k ? tail_from : k);
     const int kh = tail_from < k ? tail_from : k;
     for (int i = i0; i < n; i += stride) {
         const int t = i / kh, j = i - t * kh;
-        keep[ids[(size_t)t * k + j]] = 1;
+        const int e = ids[(size_t)t * k + j];
+        if (id_ok(e, E)) keep[e] = 1;   // a bad id is reported by the count pass
     }
 }
 
@@ -107,7 +126,8 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t *__r
                                                               int E, int k, int tail_from,
                                                               int32_t *__restrict__ offsets,
                                                               int32_t *__restrict__ sorted_pair,
-                                                              int32_t *__restrict__ pair_pos) {
+                                                              int32_t *__restrict__ pair_pos,
+                                                              int32_t *__restrict__ err) {
     __shared__ unsigned long long masks[kSmallMaskEntries];
     __shared__ int32_t cbase[kSmallMaskEntries];
     __shared__ int32_t tot[1024];
@@ -123,7 +143,8 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t *__r
     __syncthreads();
     // masks of every pair; with tail-skip the same pass flags the kept experts
     for (int c = wv; c < n_chunks; c += 16)
-        build_chunk_masks(ids, T, k, c, masks + (size_t)c * E, nullptr, TAIL ? keep_s : nullptr, tail_from);
+        build_chunk_masks(ids, T, E, k, c, masks + (size_t)c * E, nullptr, err, TAIL ? keep_s : nullptr,
+                          tail_from);
     __syncthreads();
     // per expert: prefix over chunks (a dropped expert counts no pairs)
     int run = 0;
@@ -145,14 +166,14 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t *__r
     if (tid == E - 1) offsets[E] = tot[tid] + run;   // all (kept) pairs
     __syncthreads();
     for (int c = wv; c < n_chunks; c += 16)
-        write_chunk_positions(ids, T, k, c, masks + (size_t)c * E, cbase + (size_t)c * E,
+        write_chunk_positions(ids, T, E, k, c, masks + (size_t)c * E, cbase + (size_t)c * E,
                               sorted_pair, pair_pos, keep);
 }
 
 // large batches, tail-skip: keep flags in the workspace (zeroed just before)
-__global__ __launch_bounds__(256) void dispatch_keep_kernel(const int32_t *__restrict__ ids, int T, int k,
-                                                            int tail_from, int32_t *__restrict__ keep) {
-    mark_kept(ids, T, k, tail_from, keep, blockIdx.x * 256 + threadIdx.x, gridDim.x * 256);
+__global__ __launch_bounds__(256) void dispatch_keep_kernel(const int32_t *__restrict__ ids, int T, int E,
+                                                            int k, int tail_from, int32_t *__restrict__ keep) {
+    mark_kept(ids, T, E, k, tail_from, keep, blockIdx.x * 256 + threadIdx.x, gridDim.x * 256);
 }
 
 // ----------------------------------------------------------- three passes
@@ -160,12 +181,12 @@ __global__ __launch_bounds__(256) void dispatch_keep_kernel(const int32_t *__res
 //    64 lanes touch 64 consecutive experts).
 __global__ __launch_bounds__(64) void dispatch_count_kernel(const int32_t *__restrict__ ids, int T,
                                                             int E, int k, const int32_t *keep,
-                                                            int32_t *__restrict__ cnt) {
+                                                            int32_t *__restrict__ cnt, int32_t *__restrict__ err) {
     __shared__ unsigned long long masks[1024];
     const int c = blockIdx.x;
     for (int i = threadIdx.x; i < E; i += 64) masks[i] = 0ull;
     __syncthreads();
-    build_chunk_masks(ids, T, k, c, masks, keep);
+    build_chunk_masks(ids, T, E, k, c, masks, keep, err);
     __syncthreads();
     for (int i = threadIdx.x; i < E; i += 64) cnt[(size_t)c * E + i] = __popcll(masks[i]);
 }
@@ -262,7 +283,8 @@ __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *__res
     }
     if (c == 0 && lane == 63) offsets[E] = run;
     __syncthreads();
-    build_chunk_masks(ids, T, k, c, masks, keep);
+    // errors were reported by the count pass over the same ids
+    build_chunk_masks(ids, T, E, k, c, masks, keep, nullptr);
     __syncthreads();
     const int t = c * 64 + lane;
     if (t >= T) return;
@@ -270,7 +292,7 @@ __global__ __launch_bounds__(64) void dispatch_place_kernel(const int32_t *__res
     for (int j = 0; j < k; ++j) {
         const int e = ids[(size_t)t * k + j];
         const int p = t * k + j;
-        if (keep && !keep[e]) {
+        if (!id_ok(e, E) || (keep && !keep[e])) {
             pair_pos[p] = -1;
             continue;
         }
@@ -294,13 +316,14 @@ size_t dispatch_ws_bytes(int E, int T, int k) {
 hipError_t launch_dispatch(const int32_t *ids, int T, int E, int k, int tail_from, int32_t *offsets,
                            int32_t *sorted_pair, int32_t *pair_pos, void *ws, hipStream_t s) {
     const bool tail = tail_from < k;
+    int32_t *err = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + kWsErrorWord);
     if (dispatch_fits_small(E, T)) {
         if (tail)
             hipLaunchKernelGGL(dispatch_small_kernel<true>, dim3(1), dim3(1024), 0, s, ids, T, E, k,
-                               tail_from, offsets, sorted_pair, pair_pos);
+                               tail_from, offsets, sorted_pair, pair_pos, err);
         else
             hipLaunchKernelGGL(dispatch_small_kernel<false>, dim3(1), dim3(1024), 0, s, ids, T, E, k,
-                               tail_from, offsets, sorted_pair, pair_pos);
+                               tail_from, offsets, sorted_pair, pair_pos, err);
         return hipGetLastError();
     }
     const int n_chunks = (T + 63) / 64;
@@ -314,9 +337,9 @@ hipError_t launch_dispatch(const int32_t *ids, int T, int E, int k, int tail_fro
         const int n = T * (tail_from > 0 ? tail_from : 1);
         int blocks = (n + 255) / 256;
         blocks = blocks < 1024 ? blocks : 1024;
-        hipLaunchKernelGGL(dispatch_keep_kernel, dim3(blocks), dim3(256), 0, s, ids, T, k, tail_from, keep);
+        hipLaunchKernelGGL(dispatch_keep_kernel, dim3(blocks), dim3(256), 0, s, ids, T, E, k, tail_from, keep);
     }
-    hipLaunchKernelGGL(dispatch_count_kernel, dim3(n_chunks), dim3(64), 0, s, ids, T, E, k, keep, cnt);
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(n_chunks), dim3(64), 0, s, ids, T, E, k, keep, cnt, err);
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3((E + 63) / 64), dim3(1024), 0, s, cnt, n_chunks, E,
                        tot);
     hipLaunchKernelGGL(dispatch_place_kernel, dim3(n_chunks), dim3(64), 0, s, ids, T, E, k, keep, cnt, tot,

@@ -159,3 +159,41 @@ def test_workspace_size_monotone(q):
     s4 = q.moe_workspace_size(2048, 768, 512, 4, 10)
     s8k = q.moe_workspace_size(2048, 768, 512, 8192, 10)
     assert 0 < s1 <= s4 <= s8k and s1 % 256 == 0
+
+
+def test_validate_ids_host(q):
+    """moe_validate_ids: the preconditions moe_dispatch states on its ids
+    (range [0, E), distinct within a token), checked on a host array."""
+    import numpy as np
+    v = lambda ids, T, E, k: q.moe_validate_ids(ids, T, E, k, check=False)
+    ok = np.array([[3, 1], [0, 15], [15, 14]], np.int32)
+    assert v(ok, 3, 16, 2) == q.MOE_OK
+    assert v(np.array([[3, 16]], np.int32), 1, 16, 2) == q.MOE_ERR_INVALID_ARGUMENT     # id = E
+    assert v(np.array([[-1, 2]], np.int32), 1, 16, 2) == q.MOE_ERR_INVALID_ARGUMENT     # negative id
+    assert v(np.array([[5, 5]], np.int32), 1, 16, 2) == q.MOE_ERR_INVALID_ARGUMENT      # repeated
+    # the same expert in different tokens is fine
+    assert v(np.array([[5, 6], [6, 5]], np.int32), 2, 16, 2) == q.MOE_OK
+    assert v(None, 0, 16, 2) == q.MOE_OK                                                # T = 0
+    assert v(None, 2, 16, 2) == q.MOE_ERR_INVALID_ARGUMENT
+    assert v(ok, 3, 16, 17) == q.MOE_ERR_INVALID_ARGUMENT                                # k > E
+    assert v(ok, 3, 1025, 2) == q.MOE_ERR_INVALID_ARGUMENT                               # E > 1024
+    # every generated routing of the workloads' shapes passes; k = E is a permutation
+    rng = np.random.default_rng(3)
+    for E, k, T in ((512, 10, 64), (16, 16, 5), (1024, 1024, 2), (1, 1, 7)):
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        assert v(ids, T, E, k) == q.MOE_OK
+        bad = ids.copy()
+        bad[T - 1, k - 1] = E
+        assert v(bad, T, E, k) == q.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_error_word_layout_matches_header(q):
+    """The error word sits inside the router's 4 KiB counter block, past the
+    token-tile counters (16 tiles x 128 bytes), and the binding agrees with
+    the header."""
+    src = open(HEADER).read()
+    off = int(re.search(r"#define MOE_WS_ERROR_OFFSET (\d+)", src).group(1))
+    assert off == q.MOE_WS_ERROR_OFFSET
+    assert 2048 <= off and off + 4 <= 4096 and off % 4 == 0
+    assert int(re.search(r"#define MOE_WS_ERR_ID_RANGE (\d+)", src).group(1)) == q.MOE_WS_ERR_ID_RANGE
+    assert int(re.search(r"#define MOE_WS_ERR_ID_REPEAT (\d+)", src).group(1)) == q.MOE_WS_ERR_ID_REPEAT
