@@ -285,6 +285,29 @@ moe_status moe_expert_ffn_combine(const moe_layer *layer, const uint16_t *x_bf16
                                   size_t ws_bytes, void *stream);
 
 /*
+ * moe_expert_ffn_noalloc -- moe_expert_ffn without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The call allocates
+ * nothing; its scratch is a fixed 8 MiB device array inside the library
+ * (each GPU the library runs on holds one copy until the process ends),
+ * located on the current device, which must be the device of `stream`.
+ *
+ * Same arguments (minus ws, ws_bytes), results and validation as
+ * moe_expert_ffn, bit-identical to it, for decode-sized batches only: T <= 16
+ * and moe_workspace_size(d_model, d_ff, E, T, k) <= 8 MiB (e.g. d_model=2048,
+ * d_ff=768, E=512, k=10 at every T <= 16).  Larger sizes return
+ * MOE_ERR_UNSUPPORTED and enqueue nothing.  All calls on one GPU share the
+ * array: calls that overlap in time on one GPU (different streams, or
+ * concurrent host threads whose work runs at once) race and must not be
+ * issued; calls ordered on one stream are fine.  Nothing in the array has to
+ * start at zero (each call writes what it reads).  MOE_ERR_HIP if the array's
+ * device address cannot be found.
+ */
+moe_status moe_expert_ffn_noalloc(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, int32_t k,
+                                  const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
+                                  float *y_shared, void *stream);
+
+/*
  * moe_combine -- merge the expert outputs of each token.
  * [forum] "Strata의 동작 원리": the GPU merges every expert's result, then the
  * next layer starts.

@@ -20,6 +20,7 @@ MOE_FMT_Q2_B32, MOE_FMT_Q3_B32 = 1, 2
 ENTRY_POINTS = ("moe_route", "moe_dispatch", "moe_dispatch_tail_skip", "moe_route_dispatch",
                 "moe_route_dispatch_tail_skip",
                 "moe_expert_ffn", "moe_routed_ffn", "moe_shared_ffn", "moe_expert_ffn_combine",
+                "moe_expert_ffn_noalloc",
                 "moe_combine", "moe_validate_ids", "moe_workspace_size", "moe_workspace_init",
                 "moe_status_string", "moe_abi_version")
 MOE_WS_ERROR_OFFSET = 3968                          # byte offset of the workspace's error word
@@ -59,6 +60,7 @@ def _load():
     lib.moe_shared_ffn.argtypes = [C.POINTER(moe_layer), vp, i32, vp, vp, sz, vp]
     lib.moe_expert_ffn_combine.argtypes = [C.POINTER(moe_layer), vp, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                            vp, sz, vp]
+    lib.moe_expert_ffn_noalloc.argtypes = [C.POINTER(moe_layer), vp, i32, i32, vp, vp, vp, vp, vp]
     lib.moe_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
     lib.moe_validate_ids.argtypes = [vp, i32, i32, i32]
     lib.moe_validate_ids.restype = C.c_int
@@ -69,7 +71,7 @@ def _load():
     lib.moe_status_string.restype = C.c_char_p
     lib.moe_abi_version.restype = i32
     for f in ("moe_route", "moe_dispatch", "moe_dispatch_tail_skip", "moe_route_dispatch", "moe_expert_ffn",
-              "moe_combine", "moe_workspace_init"):
+              "moe_expert_ffn_noalloc", "moe_combine", "moe_workspace_init"):
         getattr(lib, f).restype = C.c_int
     return lib
 
@@ -171,6 +173,13 @@ def moe_expert_ffn(layer, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared,
     st = lib.moe_expert_ffn(C.byref(layer), _ptr(x_bf16), T, k, _ptr(offsets), _ptr(sorted_pair),
                             _ptr(y_pairs), _ptr(y_shared), _ptr(ws), ws_bytes, _stream(stream))
     return _check(st, "moe_expert_ffn") if check else st
+
+
+def moe_expert_ffn_noalloc(layer, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, stream=None,
+                           check=True):
+    st = lib.moe_expert_ffn_noalloc(C.byref(layer), _ptr(x_bf16), T, k, _ptr(offsets), _ptr(sorted_pair),
+                                    _ptr(y_pairs), _ptr(y_shared), _stream(stream))
+    return _check(st, "moe_expert_ffn_noalloc") if check else st
 
 
 def moe_routed_ffn(layer, x_bf16, T, k, offsets, sorted_pair, y_pairs, ws, ws_bytes, stream=None,

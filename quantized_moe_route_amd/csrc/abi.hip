@@ -2,11 +2,45 @@
 // the kernel launches.  Declarations and contracts: include/moe.h.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "common.h"
 
 using namespace moe;
 
 namespace {
+
+// Scratch of moe_expert_ffn_noalloc: a fixed device array instead of a
+// caller workspace.  Each GPU the library runs on holds its own copy for the
+// life of the process.  Host code never uses the array's name as an address
+// (on the host it is only a stand-in symbol): the device address is looked up
+// once per device with hipGetSymbolAddress and kept in g_scratch_ptr.
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+void *g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch` (looked up on first use).
+moe_status scratch_of_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return MOE_ERR_HIP;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return MOE_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
 
 constexpr int kMaxE = 1024;
 constexpr int kMaxDim = 16384;
@@ -256,6 +290,28 @@ moe_status moe_shared_ffn(const moe_layer *layer, const uint16_t *x_bf16, int32_
     // k = 0: the workspace holds the shared expert's rows only
     return ffn_checked(layer, x_bf16, T, 0, nullptr, nullptr, nullptr, y_shared, kFfnShared, ws, ws_bytes,
                        stream);
+}
+
+moe_status moe_expert_ffn_noalloc(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, int32_t k,
+                                  const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
+                                  float *y_shared, void *stream) {
+    // every check of moe_expert_ffn except the workspace's (a stand-in
+    // address that passes the alignment test and an unbounded size)
+    const moe_status st = ffn_checked(layer, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, kFfnBoth,
+                                      reinterpret_cast<void *>((uintptr_t)256), SIZE_MAX, stream,
+                                      /*validate_only=*/true);
+    if (st != MOE_OK) return st;
+    if (T > kSmallTMax) return MOE_ERR_UNSUPPORTED;
+    if (ffn_need(layer->d_model, layer->d_ff, layer->n_experts, T, k) > kStaticScratchBytes)
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    void *ws = nullptr;
+    const moe_status sst = scratch_of_current_device(&ws);
+    if (sst != MOE_OK) return sst;
+    // the small-batch kernels write every scratch byte they read (h rows,
+    // group table) earlier in the same call: nothing must start at zero
+    return launched(launch_ffn_small(*layer, x_bf16, T, k, offsets, sorted_pair, y_pairs, y_shared, ws, kFfnBoth,
+                                     as_stream(stream)));
 }
 
 moe_status moe_expert_ffn_combine(const moe_layer *layer, const uint16_t *x_bf16, int32_t T, int32_t k,
