@@ -13,7 +13,12 @@ HIP events on the launch stream.  Per-call GPU durations come from one more
 graph per call (back-to-back launches of that call over consecutive steps'
 inputs), timed with HIP events on the same stream.
 
-Workloads (default 1):
+With no --workload the run covers the metric's three regimes: workload 1
+(the headline line: value, roofline, cpu_baseline) and, under "regimes",
+workloads 2 and 3, each with its own tokens/s, roofline and cpu_baseline,
+timed the same way with the same --steps / --warmup.
+
+Workloads:
   1  decode, T=1, d=2048, f=768, E=512, top-10 + shared, Q2 block-32, 1 layer
      (16 copies of the layer at distinct HBM addresses, cycled per step, and a
      fresh x per step, so the selected experts are not cache-resident)
@@ -108,7 +113,7 @@ def cpu_model():
 
 
 def cpu_baseline(w, host_layer, router, bias, xs_host, seconds):
-    """The oracle, as is, on a bounded sample of the same workload."""
+    """The oracle, as is, timed on a bounded sample of the same workload."""
     import oracle
     n = 0
     t0 = time.perf_counter()
@@ -122,12 +127,45 @@ def cpu_baseline(w, host_layer, router, bias, xs_host, seconds):
     return n, el
 
 
-def main():
+def oracle_spot_check(w, host_layer, x0, lg, ids_gpu, offsets_gpu, sp_gpu, w_gpu, out_gpu, rows, tf):
+    """The CPU-baseline leg's parity sample: the oracle on the step's tokens
+    `rows`, routed on the GPU's own logits; ids and the permutation checked
+    in full.  Returns (ids_exact, max|err|/rms)."""
+    import oracle
+    ids_ref, _ = oracle.topk_softmax(lg, w.k)
+    if tf is None:
+        off_ref, sp_ref, _ = oracle.dispatch(ids_ref, w.n_experts)
+    else:
+        off_ref, sp_ref, _ = oracle.dispatch_tail_skip(ids_ref, w.n_experts, tf)
+    n_kept = int(off_ref[w.n_experts])
+    ids_ok = bool(np.array_equal(ids_gpu, ids_ref) and np.array_equal(offsets_gpu, off_ref)
+                  and np.array_equal(sp_gpu[:n_kept], sp_ref[:n_kept]))
+    if tf is None:
+        _, _, out_ref = oracle.layer(host_layer, w.fmt, w.d_model, w.d_ff, w.n_experts, w.k,
+                                     x0[rows], logits=lg[rows])
+    else:
+        # the kept set belongs to the whole batch: the sampled tokens' output
+        # from their kept rows
+        keep = oracle.tail_keep(ids_ref, w.n_experts, tf)
+        idr = ids_ref[rows]
+        re = np.concatenate([idr.ravel(), -np.ones(len(rows), np.int32)]).astype(np.int32)
+        rt = np.concatenate([np.repeat(rows, w.k), rows]).astype(np.int32)
+        yr = oracle.expert_rows(host_layer, w.fmt, w.d_model, w.d_ff, w.n_experts, x0, re, rt, f64=True)
+        wk = w_gpu[rows].astype(np.float64) * keep[idr]
+        out_ref = yr[len(rows) * w.k:] + np.einsum(
+            "tj,tjd->td", wk, yr[:len(rows) * w.k].reshape(len(rows), w.k, w.d_model))
+    rms = float(np.sqrt(np.mean(out_ref.astype(np.float64) ** 2)))
+    err = float(np.max(np.abs(out_gpu[rows].astype(np.float64) - out_ref)) / rms)
+    return ids_ok, err
+
+
+def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=None, choices=[1, 2, 3, 4, 5, 6],
+                    help="one workload only (default: workload 1, plus 2 and 3 under \"regimes\")")
     ap.add_argument("--tokens", type=int, default=None,
                     help="override the workload's T (tokens per layer), e.g. the mid-size batches")
     ap.add_argument("--tail-skip", type=int, default=None, metavar="RANK",
@@ -140,32 +178,18 @@ def main():
                          "routed experts after it (moe_routed_ffn)")
     ap.add_argument("--copies", type=int, default=None,
                     help="layer copies cycled, single-layer workloads (default 16 decode, 1 prefill)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference kernel "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
-    args = ap.parse_args()
+    return ap.parse_args()
 
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the library has "
-              "no multi-GPU path (the expert-parallel sharding it would use is not implemented).",
-              file=sys.stderr)
-        sys.exit(2)
 
+def run_workload(wid, args):
+    """Bench one workload; returns (result dict, ok)."""
     import torch
-
-    if args.calibrate_copy:
-        n = args.calibrate_copy << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
-        return
 
     import synth
     import synth.device as sdev
@@ -173,7 +197,7 @@ def main():
     from quantized_moe_route_amd import hip
     from quantized_moe_route_amd.layer import DeviceLayer, SideStream, alloc_buffers, run_layer
 
-    w = synth.WORKLOADS[args.workload]
+    w = synth.WORKLOADS[wid]
     if args.tokens is not None:
         import dataclasses
         import re
@@ -222,11 +246,6 @@ def main():
     def layer_of(step, li):
         return layers[li] if n_lay > 1 else layers[step % len(layers)]
 
-    # ------------------------------------------------- parity spot check (oracle)
-    # decode: every token; prefill: a seeded sample of tokens (the oracle
-    # evaluates them one by one from the GPU's logits).  ids and the
-    # permutation are checked in full either way.
-    import oracle
     tf = args.tail_skip
     if tf is not None and not 0 <= tf <= w.k:
         log(f"--tail-skip must lie in [0, {w.k}]")
@@ -238,41 +257,14 @@ def main():
         sys.exit(2)
     side = SideStream(device=dev) if ov else None
     fuse_cmb = not args.separate_calls and not ov and w.T <= FUSE_COMBINE_TMAX
+    # step 0 once, eagerly: its outputs are the CPU-baseline leg's parity sample
     run_layer(layer_of(0, 0), xs[0][0], buf, stream=sh, tail_from=tf, fused=fused, side=side,
               fuse_combine=fuse_cmb)
     hip.stream_synchronize(sh)
-    x0 = xs[0][0].cpu().numpy().view(np.uint16)
-    lg = buf.logits[:w.T].cpu().numpy()
-    ids_ref, _ = oracle.topk_softmax(lg, w.k)
-    if tf is None:
-        off_ref, sp_ref, _ = oracle.dispatch(ids_ref, w.n_experts)
-    else:
-        off_ref, sp_ref, _ = oracle.dispatch_tail_skip(ids_ref, w.n_experts, tf)
-    n_kept = int(off_ref[w.n_experts])
-    ids_ok = bool(np.array_equal(buf.ids[:w.T].cpu().numpy(), ids_ref)
-                  and np.array_equal(buf.offsets.cpu().numpy(), off_ref)
-                  and np.array_equal(buf.sorted_pair[:n_kept].cpu().numpy(), sp_ref[:n_kept]))
-    rows = (np.sort(np.random.default_rng(7).choice(w.T, size=16, replace=False))
-            if prefill else np.arange(w.T))
-    if tf is None:
-        _, _, out_ref = oracle.layer(host_layer, w.fmt, w.d_model, w.d_ff, w.n_experts, w.k,
-                                     x0[rows], logits=lg[rows])
-    else:
-        # the kept set belongs to the whole batch: the sampled tokens' output
-        # from their kept rows
-        keep = oracle.tail_keep(ids_ref, w.n_experts, tf)
-        idr = ids_ref[rows]
-        re = np.concatenate([idr.ravel(), -np.ones(len(rows), np.int32)]).astype(np.int32)
-        rt = np.concatenate([np.repeat(rows, w.k), rows]).astype(np.int32)
-        yr = oracle.expert_rows(host_layer, w.fmt, w.d_model, w.d_ff, w.n_experts, x0, re, rt, f64=True)
-        wk = buf.w[:w.T].cpu().numpy()[rows].astype(np.float64) * keep[idr]
-        out_ref = yr[len(rows) * w.k:] + np.einsum(
-            "tj,tjd->td", wk, yr[:len(rows) * w.k].reshape(len(rows), w.k, w.d_model))
-    rms = float(np.sqrt(np.mean(out_ref.astype(np.float64) ** 2)))
-    err = float(np.max(np.abs(buf.out[:w.T].cpu().numpy()[rows].astype(np.float64) - out_ref))
-                / rms)
-    log(f"parity step 0 ({len(rows)} tokens): ids/permutation exact={ids_ok} "
-        f"max|err|/rms={err:.3e}")
+    step0 = {"x": xs[0][0].cpu().numpy().view(np.uint16), "lg": buf.logits[:w.T].cpu().numpy(),
+             "ids": buf.ids[:w.T].cpu().numpy(), "offsets": buf.offsets.cpu().numpy(),
+             "sp": buf.sorted_pair[:w.T * w.k].cpu().numpy(), "w": buf.w[:w.T].cpu().numpy(),
+             "out": buf.out[:w.T].cpu().numpy()}
 
     # deviation of the lossy tail-skip layer from the full layer (same input)
     tail_info = None
@@ -281,9 +273,8 @@ def main():
         run_layer(layer_of(0, 0), xs[0][0], buf, stream=sh)
         hip.stream_synchronize(sh)
         full = buf.out[:w.T].double()
-        dev = float((out_skip.double() - full).abs().max() / full.pow(2).mean().sqrt())
-        tail_info = {"tail_from": tf, "pairs": w.T * w.k, "kept_pairs_step0": n_kept,
-                     "max_dev_from_full_layer_over_rms": dev}
+        dv = float((out_skip.double() - full).abs().max() / full.pow(2).mean().sqrt())
+        tail_info = {"tail_from": tf, "pairs": w.T * w.k, "max_dev_from_full_layer_over_rms": dv}
 
     def dispatch():
         if tf is None:
@@ -335,8 +326,8 @@ def main():
     else:
         calls = (["route_dispatch"] if fused else ["route", "dispatch"]) + ["expert_ffn", "combine"]
 
-    def enqueue(step0, nsteps):
-        for s in range(step0, step0 + nsteps):
+    def enqueue(step0_, nsteps):
+        for s in range(step0_, step0_ + nsteps):
             for li in range(n_lay):
                 if ov:
                     # fork: the shared expert beside routing; join before the combine
@@ -396,6 +387,7 @@ def main():
         pr = np.array(per_run)
         step_us = {"median": float(np.median(pr)), "p10": float(np.percentile(pr, 10)),
                    "p90": float(np.percentile(pr, 90)), "replays": len(per_run), "steps_each": K}
+        del g_warm, g_timed
 
     # replay check: the last timed step again, eagerly; deterministic kernels
     enqueue(K - 1, 1)
@@ -418,6 +410,7 @@ def main():
         e1.record(sh)
         hip.stream_synchronize(sh)
         avg_us[c] = 1e3 * e0.elapsed_ms(e1) / G
+        del gc
     side = side_saved
 
     # algorithmic work of one moe_expert_ffn launch.
@@ -443,8 +436,8 @@ def main():
         # + the merge: every y row read back, out written, pair positions and weights
         ffn_bytes += (rows_ffn * 4 + w.T * 4) * w.d_model + w.T * w.k * 8
     t_ffn = avg_us[ffn_call] * 1e-6
-    # counters were taken at the workload's own T only
-    traffic = traffic_for(args.workload) if args.tokens is None else None
+    # counters were taken at the workload's own T and calls only
+    traffic = (traffic_for(wid) if args.tokens is None and tf is None and not ov and fused else None)
     if prefill:
         achieved = ffn_flops / t_ffn / 1e12
         roof = {"bound": "mfma", "kernel": "moe_expert_ffn (pf_gemm gate/up + down, "
@@ -468,14 +461,25 @@ def main():
     tokens_per_s = w.T * K / (wall_ms / 1e3)
 
     # ------------------------------------------------------------ CPU oracle
+    # The only oracle calls of the run: the parity sample of step 0 (decode:
+    # every token; prefill: 16 seeded tokens, routed on the GPU's logits;
+    # ids and the permutation in full), then the oracle's own throughput on
+    # a bounded sample of the same workload.
     cpu = None
+    parity = {"ids_exact": None, "max_err_over_rms": None, "tokens_checked": 0,
+              "graph_replay_bitwise": replay_ok}
     if not args.no_cpu_baseline:
         import oracle as orc
+        rows = (np.sort(np.random.default_rng(7).choice(w.T, size=16, replace=False))
+                if prefill else np.arange(w.T))
+        ids_ok, err = oracle_spot_check(w, host_layer, step0["x"], step0["lg"], step0["ids"],
+                                        step0["offsets"], step0["sp"], step0["w"], step0["out"], rows, tf)
+        parity.update(ids_exact=ids_ok, max_err_over_rms=err, tokens_checked=int(len(rows)))
+        log(f"parity step 0 ({len(rows)} tokens): ids/permutation exact={ids_ok} max|err|/rms={err:.3e}")
         if prefill:
             # 256-token slices of the chunk, layer 0, until the time is up
             chunk = 256
-            x_full = xs[0][0].cpu().numpy().view(np.uint16)
-            xs_host = [x_full[i:i + chunk] for i in range(0, w.T, chunk)]
+            xs_host = [step0["x"][i:i + chunk] for i in range(0, w.T, chunk)]
         else:
             chunk = w.T
             xs_host = [xs[s][0].cpu().numpy().view(np.uint16) for s in range(min(S, 64))]
@@ -514,12 +518,56 @@ def main():
         ("layer_mfma_frac" if prefill else "layer_hbm_frac"):
             (ffn_flops * n_lay / (gpu_ms / K * 1e-3) / 1e12 / BF16_PEAK_TFLOPS) if prefill else
             (layer_bytes * n_lay / (gpu_ms / K * 1e-3) / 1e9 / HBM_PEAK_GBS),
-        "parity": {"ids_exact": ids_ok, "max_err_over_rms": err, "tokens_checked": int(len(rows)),
-                   "graph_replay_bitwise": replay_ok},
+        "parity": parity,
         **({} if tail_info is None else {"tail_skip": tail_info}),
     }
-    print(json.dumps(res))
-    if not (ids_ok and err <= 2e-3 and replay_ok):
+    ok = replay_ok and (parity["ids_exact"] is None or (parity["ids_exact"] and parity["max_err_over_rms"] <= 2e-3))
+    # release this workload's device memory before the next one
+    del layers, xs, buf
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, ok
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the library has "
+              "no multi-GPU path (the expert-parallel sharding it would use is not implemented).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
+        return
+
+    single = (args.workload is not None or args.tokens is not None or args.tail_skip is not None
+              or args.separate_calls or args.overlap_shared or args.copies is not None)
+    wids = [args.workload or 1] if single else [1, 2, 3]
+    results = []
+    all_ok = True
+    for wid in wids:
+        log(f"--- workload {wid}")
+        res, ok = run_workload(wid, args)
+        results.append(res)
+        all_ok = all_ok and ok
+    head = results[0]
+    if len(results) > 1:
+        keep = ("value", "unit", "steps", "warmup", "ms_per_step", "dtype", "config", "roofline",
+                "cpu_baseline", "gpu_ms_per_step", "step_us", "per_call_us", "layer_mfma_frac",
+                "layer_hbm_frac", "parity")
+        head["regimes"] = {r["config"]["workload"]: {k: r[k] for k in keep if k in r} for r in results[1:]}
+    print(json.dumps(head))
+    if not all_ok:
         sys.exit(1)
 
 

@@ -23,11 +23,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // user restores them), then the scratch regions.  A counter that many
 // workgroups hit sits on a 128-byte line of its own: device-scope atomics on
 // one line are served one after another.  Header: 4 KiB for the router's
-// tiles, then one line per 16-column output tile (d_model <= 16,384) for the
-// down kernel's fused combine.
+// token tiles (and the error word), one line per 16-column output tile
+// (d_model <= 16,384) for the down kernel's fused combine, then one line per
+// (token tile, 32-expert column slice) for the router's column slices.
 constexpr int kCntLine = 32;        // int32 counters per 128-byte line
 constexpr size_t kCombineCnt = 4096;                       // byte offset of the combine counters
-constexpr size_t kWsHeader = kCombineCnt + (16384 / 16) * 128;
+constexpr size_t kRouteSliceCnt = kCombineCnt + (16384 / 16) * 128;   // router slice counters
+constexpr int kRouteSliceCntLines = 16 * 32;                          // 16 tiles x 32 slices
+constexpr size_t kWsHeader = kRouteSliceCnt + (size_t)kRouteSliceCntLines * 128;
 constexpr int kRouteTile = 8;       // tokens per tile of the one-launch router
 // the one-launch router's tile tt counts its arrivals at counters[kCntLine * tt]
 // (tiles 0..15: bytes 0..2047)
@@ -286,8 +289,12 @@ __device__ inline bool find_group(const int32_t *__restrict__ offsets, int E, in
     return true;
 }
 
-// silu(g) * u in fp32
-__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u * 2^-2a in fp32, as (g 2^-a) / (1 + e^-g) * (u 2^-a): the
+// power-of-two scalings are exact, so this is silu(g) * u scaled, and it
+// stays finite for any g, u whose scaled product fits
+__device__ __forceinline__ float swiglu(float g, float u, int a) {
+    return ldexpf(g, -a) / (1.0f + __expf(-g)) * ldexpf(u, -a);
+}
 
 // ---------------------------------------------------------------- launchers
 // (defined in the .hip files; return hipError_t of the launch)

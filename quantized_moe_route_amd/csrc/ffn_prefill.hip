@@ -22,8 +22,13 @@
 // router costs no idle tail beyond one unit.
 //
 // Operands:
-//   A (activations): x converted once to fp16 (exact for bf16 values in fp16
-//     range), or h.  Each 192-row x 128-column stage is copied global -> LDS
+//   A (activations): x converted once to fp16 after an exact power-of-two
+//     scaling per token row (x * 2^-a, 2^a <= max|x_row| < 2^(a+1)), so any
+//     bf16 row fits fp16's range; or h, stored as h * 2^-2a.  The gate/up
+//     epilogue takes the true gate value back (2^a times its accumulator)
+//     for the sigmoid, and the down epilogue multiplies y by 2^2a: both
+//     exact, so the scaling changes no result beyond fp16's subnormal range.
+//     Each 192-row x 128-column stage is copied global -> LDS
 //     by the direct-to-LDS loads (no registers), two stages in flight; the
 //     16-byte chunks of a row are XOR-swizzled by the row index so the
 //     fragment reads are free of bank conflicts.
@@ -195,28 +200,55 @@ __device__ __forceinline__ void build_items_block(const int32_t *__restrict__ of
 }
 
 // The two prepasses in one launch: block 0 builds the work items, the other
-// blocks convert x to fp16 (exact for bf16 values in fp16 range).
+// blocks convert x to fp16, one wave per token row: a = the exponent of the
+// row's largest magnitude (0 for a zero row) goes to xexp[t], and the row is
+// stored as fp16(x * 2^-a), so its largest value lies in [1, 2).
 __global__ __launch_bounds__(1024) void pf_prep_kernel(const int32_t *__restrict__ offsets, int E, int T,
                                                        int P, int parts, PfItem *__restrict__ items,
                                                        PfSched *__restrict__ sched,
                                                        const uint16_t *__restrict__ x,
-                                                       uint16_t *__restrict__ x16, size_t n8) {
+                                                       uint16_t *__restrict__ x16, int32_t *__restrict__ xexp,
+                                                       int d) {
     if (blockIdx.x == 0) {
         build_items_block(offsets, E, T, P, parts, items, sched);
         return;
     }
-    const size_t stride = (size_t)(gridDim.x - 1) * 1024;
-    for (size_t i = (size_t)(blockIdx.x - 1) * 1024 + threadIdx.x; i < n8; i += stride) {
-        const u32x4 v = reinterpret_cast<const u32x4 *>(x)[i];
-        u32x4 o;
+    const int wv = threadIdx.x >> 6, lane = __lane_id();
+    const int cpr = d / 8;   // 16-byte chunks per row
+    for (int t = (blockIdx.x - 1) * 16 + wv; t < T; t += (gridDim.x - 1) * 16) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (size_t)t * d);
+        u32x4 *dst = reinterpret_cast<u32x4 *>(x16 + (size_t)t * d);
+        uint32_t mx = 0u;   // largest magnitude, as bf16 bits without the sign
+        for (int c = lane; c < cpr; c += 64) {
+            const u32x4 v = src[c];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float a = __uint_as_float(v[q] << 16), b = __uint_as_float(v[q] & 0xffff0000u);
-            const _Float16 ha = static_cast<_Float16>(a), hb = static_cast<_Float16>(b);
-            o[q] = (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-                   ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t lo = v[q] & 0x7fffu, hi = (v[q] >> 16) & 0x7fffu;
+                mx = lo > mx ? lo : mx;
+                mx = hi > mx ? hi : mx;
+            }
         }
-        reinterpret_cast<u32x4 *>(x16)[i] = o;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t u = (uint32_t)__shfl_xor((int)mx, o, 64);
+            mx = u > mx ? u : mx;
+        }
+        // exponent field of the largest magnitude (0: zero or subnormal)
+        const int ef = (int)(mx >> 7);
+        const int a = mx == 0u ? 0 : (ef == 0 ? -126 : ef - 127);
+        if (lane == 0) xexp[t] = a;
+        for (int c = lane; c < cpr; c += 64) {
+            const u32x4 v = src[c];   // the row's second read: cached
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float lo = ldexpf(__uint_as_float(v[q] << 16), -a);
+                const float hi = ldexpf(__uint_as_float(v[q] & 0xffff0000u), -a);
+                const _Float16 hl = static_cast<_Float16>(lo), hh = static_cast<_Float16>(hi);
+                o[q] = (uint32_t)__builtin_bit_cast(uint16_t, hl) | ((uint32_t)__builtin_bit_cast(uint16_t, hh) << 16);
+            }
+            dst[c] = o;
+        }
     }
 }
 
@@ -358,6 +390,7 @@ struct PfGemmArgs {
     QMatDev s0, s1;            // shared expert, same roles
     const PfItem *items;
     PfSched *sched;
+    const int32_t *xexp;       // per token: x row scaled by 2^-xexp, h rows by 2^-2xexp
     const uint16_t *a_hi;      // gate/up: x as fp16 [T][d]; down: h [(P + T)][f]
     const uint16_t *a_lo;      // down: h_lo [T][f] (shared rows)
     const int32_t *sorted_pair;
@@ -393,10 +426,11 @@ struct PfGeom {
 };
 constexpr int kPfNtw = MOE_PF_NTW;
 
-// silu(g) * u with the hardware reciprocal (about 1 ulp): h is rounded to
-// fp16 right after
-__device__ __forceinline__ float swiglu_fast(float g, float u) {
-    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+// silu(g) * u * 2^-2a from the accumulators g_a = g * 2^-a, u_a = u * 2^-a:
+// g_a * sigmoid(g) * u_a, the sigmoid taken at the true g = g_a * 2^a, with
+// the hardware reciprocal (about 1 ulp); h is rounded to fp16 right after
+__device__ __forceinline__ float swiglu_scaled(float ga, float ua, int a) {
+    return ga * __builtin_amdgcn_rcpf(1.0f + __expf(-ldexpf(ga, a))) * ua;
 }
 
 // One unit: the rows of one item x one column tile, all of K.
@@ -411,8 +445,8 @@ __device__ __forceinline__ float swiglu_fast(float g, float u) {
 // MT: 32-row m-tiles that hold rows of the item (1..4).
 template <int FMT, int MODE, bool SH, int MT, int NTW>
 __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item, int tile,
-                                        uint8_t *As, int *s_row, const PfItem *pf_items, int pf_t, int pf_n,
-                                        PfItem *pf_dst) {
+                                        uint8_t *As, int *s_row, int *s_exp, const PfItem *pf_items, int pf_t,
+                                        int pf_n, PfItem *pf_dst) {
     using G = PfGeom<NTW>;
     const int tid = threadIdx.x, l = __lane_id();
     const int wv = wave_uniform(tid >> 6);
@@ -479,17 +513,21 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
     // end repeat its last row and are never stored.  The first step's
     // weights are loaded right after the pair lookup and before its use, so
     // their latency runs under the lookup, the barrier and the A copies.
-    int src = 0;
+    int src = 0, tok = 0;
     if (tid < PF_MT) {
         const int r = tid < nrows ? tid : nrows - 1;
+        tok = SH ? item.row0 + r : a.sorted_pair[item.row0 + r] / a.k;
         if constexpr (MODE == 0)
-            src = SH ? item.row0 + r : a.sorted_pair[item.row0 + r];
+            src = tok;
         else
             src = item.hrow0 + r;
     }
 #pragma unroll
     for (int n = 0; n < NTW; ++n) load_b_tile(bcur, 0, n);
-    if (tid < PF_MT) s_row[tid] = (MODE == 0 && !SH) ? src / a.k : src;
+    if (tid < PF_MT) s_row[tid] = src;
+    // the row's power-of-two exponent, used in the epilogue (loaded now, its
+    // latency runs under the K loop)
+    const int rexp = tid < PF_MT ? a.xexp[tok] : 0;
     // LDS only: the previous unit's output stores may still be in flight
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     wg_barrier();
@@ -623,6 +661,8 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
     // outside the branch so the compiler knows it and does not make each LDS
     // read of the epilogue wait for the stores before it
     wait_vm<0>();
+    if (tid < PF_MT) s_exp[tid] = rexp;
+    __syncthreads();
     // the next unit's item (thread 0), loaded while the epilogue runs
     // (thread 0: pf_t is the next ticket of this queue, pf_items its items,
     // pf_n its unit count)
@@ -648,12 +688,15 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
                 // read back along rows for 16-byte stores
                 uint16_t *eh = reinterpret_cast<uint16_t *>(ep);
                 uint16_t *el = eh + 32 * G::EP0H_PITCH;
+                int rx[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) rx[r] = s_exp[m * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
 #pragma unroll
                 for (int n = 0; n < NTW / 2; ++n)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int row = 8 * (r >> 2) + 4 * h + (r & 3);
-                        const float hv = swiglu_fast(acc[m][n][r], acc[m][n + NTW / 2][r]);
+                        const float hv = swiglu_scaled(acc[m][n][r], acc[m][n + NTW / 2][r], rx[r]);
                         const _Float16 hh = static_cast<_Float16>(hv);
                         eh[row * G::EP0H_PITCH + n * 32 + (l & 31)] = __builtin_bit_cast(uint16_t, hh);
                         if constexpr (SH)
@@ -693,7 +736,11 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
                 for (int it = 0; it < 32 * LPR / 64; ++it) {
                     const int row = it * (64 / LPR) + l / LPR;
                     const int grow = m * 32 + row;
-                    const f32x4 v = *reinterpret_cast<const f32x4 *>(ep + row * G::EP1_PITCH + (l % LPR) * 4);
+                    f32x4 v = *reinterpret_cast<const f32x4 *>(ep + row * G::EP1_PITCH + (l % LPR) * 4);
+                    // y = (h * 2^-2a) . W * 2^2a
+                    const int ya = 2 * s_exp[grow];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) v[c] = ldexpf(v[c], ya);
                     // y is read once, by the merge: nontemporal stores
                     if (grow < nrows)
                         __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(out + (size_t)(item.row0 + grow) * a.d + c0));
@@ -715,6 +762,7 @@ template <int FMT, int MODE, int NTW>
 __global__ __launch_bounds__(256, MOE_PF_OCC) void pf_gemm_kernel(PfGemmArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t As[PF_NSTAGE * PF_STAGE];
     __shared__ int s_row[PF_MT];
+    __shared__ int s_exp[PF_MT];
     __shared__ int s_ticket;
     __shared__ int s_xq[PF_NXCD + 1];   // queue bounds (fixed for the launch)
     __shared__ __attribute__((aligned(16))) PfItem s_next;   // item of ticket s_next_t in queue s_next_x
@@ -757,15 +805,15 @@ __global__ __launch_bounds__(256, MOE_PF_OCC) void pf_gemm_kernel(PfGemmArgs a) 
         const int tile = t % a.nt;
         constexpr int MTX = PF_MT / 32;
         if (item.expert < 0) {
-            pf_unit<FMT, MODE, true, MTX, NTW>(a, item, tile, As, s_row, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next);
+            pf_unit<FMT, MODE, true, MTX, NTW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next);
         } else {
             switch ((item.nrows + 31) >> 5) {
-                case 1: pf_unit<FMT, MODE, false, 1, NTW>(a, item, tile, As, s_row, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
-                case 2: pf_unit<FMT, MODE, false, 2, NTW>(a, item, tile, As, s_row, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
-                case 3: pf_unit<FMT, MODE, false, 3, NTW>(a, item, tile, As, s_row, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
-                case 4: pf_unit<FMT, MODE, false, 4 < MTX ? 4 : MTX, NTW>(a, item, tile, As, s_row, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
-                case 5: pf_unit<FMT, MODE, false, 5 < MTX ? 5 : MTX, NTW>(a, item, tile, As, s_row, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
-                default: pf_unit<FMT, MODE, false, MTX, NTW>(a, item, tile, As, s_row, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                case 1: pf_unit<FMT, MODE, false, 1, NTW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                case 2: pf_unit<FMT, MODE, false, 2, NTW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                case 3: pf_unit<FMT, MODE, false, 3, NTW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                case 4: pf_unit<FMT, MODE, false, 4 < MTX ? 4 : MTX, NTW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                case 5: pf_unit<FMT, MODE, false, 5 < MTX ? 5 : MTX, NTW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                default: pf_unit<FMT, MODE, false, MTX, NTW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
             }
         }
         // pf_unit ended with a barrier: every thread has read s_ticket
@@ -782,6 +830,7 @@ __global__ __launch_bounds__(256, MOE_PF_OCC) void pf_gemm_kernel(PfGemmArgs a) 
 struct PfWs {
     PfSched *sched;
     PfItem *items;
+    int32_t *xexp;
     uint16_t *x16;
     uint16_t *h;
     uint16_t *h_lo;
@@ -801,6 +850,8 @@ static PfWs pf_carve(void *ws, int d, int f, int E, int T, int k) {
     p += 256;
     w.items = reinterpret_cast<PfItem *>(p);
     p += align256(pf_max_items(E, T, k) * sizeof(PfItem));
+    w.xexp = reinterpret_cast<int32_t *>(p);
+    p += align256((size_t)T * sizeof(int32_t));
     w.x16 = reinterpret_cast<uint16_t *>(p);
     p += align256((size_t)T * d * 2);
     w.h = reinterpret_cast<uint16_t *>(p);
@@ -810,7 +861,8 @@ static PfWs pf_carve(void *ws, int d, int f, int E, int T, int k) {
 }
 
 static size_t ws_bytes(int d, int f, int E, int T, int k) {
-    return 256 + align256(pf_max_items(E, T, k) * sizeof(PfItem)) + align256((size_t)T * d * 2) +
+    return 256 + align256(pf_max_items(E, T, k) * sizeof(PfItem)) + align256((size_t)T * sizeof(int32_t)) +
+           align256((size_t)T * d * 2) +
            align256(((size_t)T * k + T) * f * 2) + align256((size_t)T * f * 2);
 }
 
@@ -835,14 +887,15 @@ static void pf_launch_fmt(const moe_layer &L, const uint16_t *x, int T, int k, c
                           int parts, hipStream_t s) {
     const int d = L.d_model, f = L.d_ff, E = L.n_experts;
     const int P = T * k;
-    const size_t n8 = (size_t)T * d / 8;
-    size_t blocks = (n8 + 1023) / 1024;
+    // x conversion: one wave per token row, 16 rows per block
+    size_t blocks = ((size_t)T + 15) / 16;
     if (blocks > 2048) blocks = 2048;
     hipLaunchKernelGGL(pf_prep_kernel, dim3((unsigned)(1 + blocks)), dim3(1024), 0, s, offsets, E, T, P,
-                       parts, w.items, w.sched, x, w.x16, n8);
+                       parts, w.items, w.sched, x, w.x16, w.xexp, d);
     PfGemmArgs a{};
     a.items = w.items;
     a.sched = w.sched;
+    a.xexp = w.xexp;
     a.sorted_pair = sorted_pair;
     a.h_out = w.h;
     a.h_lo_out = w.h_lo;

@@ -23,7 +23,10 @@
 //   are fp32.
 //   - gate/up: A = the batch's x rows (bf16, exact; each group row then takes
 //     its token's sums); h = silu(g)*u in fp32 is written as fp16 hi + fp16
-//     lo (22 significant bits).
+//     lo (22 significant bits) of h * 2^-2a, where 2^a <= max|x_t| < 2^(a+1)
+//     for the row's token t (an exact power-of-two scaling, so h fits fp16's
+//     range for any bf16 x); a goes to hx[row] and the down projection
+//     multiplies y by 2^2a.
 //   - down: A stacks the group's h_hi rows over its h_lo rows in one 16-row
 //     tile, so one fp16 matrix-core step covers both halves.
 //   - four waves of a workgroup split K; partial sums meet in LDS in a fixed
@@ -139,48 +142,6 @@ constexpr int kBatch = MOE_DECODE_BATCH;   // units prefetched per wave per batc
 constexpr int kDownBatch = 3;
 
 constexpr size_t kXsMaxBytes = 32768;   // x staged in LDS by the gate/up kernel (up to 8 tokens)
-constexpr int kPfPieces = 4;   // 16-byte pieces per thread (covers 3 down tiles)
-
-// The down-projection weights of output tiles ot = nt, nt + G, nt + 2G, ...
-// (G gate/up tiles per group: with G and the down grid's width multiples of
-// 8, each such tile's down workgroup runs on the XCD of this one), read while
-// the gate/up work runs so that the down kernel finds them in the caches
-// instead of paying a full memory latency after its group lookup.  The
-// values are only held until the caller consumes them.  Used for single-token
-// batches (11 groups): there the FFN gains ~0.6 us; with 4 or 16 tokens (22
-// to 140 groups) the extra loads slowed gate/up by more than down gained.
-template <int FMT>
-__device__ __forceinline__ void down_prefetch(u32x4 (&pf)[kPfPieces], const QMatDev &down,
-                                              const QMatDev &sdown, int d, int f, const Group &grp,
-                                              int nt, int G) {
-    const QMatDev W = grp.expert < 0 ? sdown : down;
-    const int e = grp.expert < 0 ? 0 : grp.expert;
-    const int KC = f / 128, OT = d / 16;
-    // pieces of one tile: codes (32 per unit), Q3 third bits (16), scales (8), Q2 minimums (8)
-    const int n_lo = KC * 32, n_hi = FMT == MOE_FMT_Q3_B32 ? KC * 16 : 0, n_sc = KC * 8;
-    const int P = n_lo + n_hi + 2 * n_sc - (FMT == MOE_FMT_Q3_B32 ? n_sc : 0);
-    const int ntile = (OT - nt + G - 1) / G;   // tiles nt + G m < OT
-#pragma unroll
-    for (int i = 0; i < kPfPieces; ++i) {
-        int q = (int)threadIdx.x + (int)blockDim.x * i;
-        q = q < ntile * P ? q : 0;   // unconditional loads: spare threads re-read piece 0
-        const int tq = q / P, pp = q - tq * P;
-        int ot = nt + G * tq;
-        ot = ot < OT ? ot : OT - 1;   // (only when no tile is left: f > d)
-        const size_t ub = ((size_t)e * OT + ot) * KC;
-        const uint8_t *src;
-        if (pp < n_lo)
-            src = W.lo + ub * 512 + (size_t)pp * 16;
-        else if (pp < n_lo + n_hi)
-            src = W.hi + ub * 256 + (size_t)(pp - n_lo) * 16;
-        else if (pp < n_lo + n_hi + n_sc)
-            src = reinterpret_cast<const uint8_t *>(W.scale) + ub * 128 + (size_t)(pp - n_lo - n_hi) * 16;
-        else
-            src = reinterpret_cast<const uint8_t *>(W.min) + ub * 128 + (size_t)(pp - n_lo - n_hi - n_sc) * 16;
-        pf[i] = *reinterpret_cast<const u32x4 *>(src);
-    }
-}
-
 // One gate/up task: 16 h columns (row tile nt) of one expert group, for all
 // of the group's rows.  The NW waves of the workgroup split K and meet in LDS
 // (red); wave 0 applies SwiGLU and writes h as fp16 hi + lo.
@@ -193,22 +154,38 @@ __device__ __forceinline__ void down_prefetch(u32x4 (&pf)[kPfPieces], const QMat
 // workgroup (global-to-LDS, no registers held) and the activation operands
 // are read from there; TPW > 1: one workgroup of TPW x NW waves serves TPW
 // column tiles with that one copy.
+// The exponent a of the largest magnitude of x_t (0 for a zero row), from the
+// largest bf16 magnitude bits (sign cleared): 2^a <= max|x_t| < 2^(a+1).
+__device__ __forceinline__ int exp_of_max_bits(uint32_t mx) {
+    const int ef = (int)(mx >> 7);
+    return mx == 0u ? 0 : (ef == 0 ? -126 : ef - 127);
+}
+__device__ __forceinline__ uint32_t max_mag_bf16x8(const u32x4 &v, uint32_t mx) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = v[q] & 0x7fffu, hi = (v[q] >> 16) & 0x7fffu;
+        mx = lo > mx ? lo : mx;
+        mx = hi > mx ? hi : mx;
+    }
+    return mx;
+}
+
 template <int FMT, int IMAX, int NW, bool XL, int TPW>
 __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &up, const QMatDev &sgate,
                                             const QMatDev &sup, const uint16_t *__restrict__ x, int T, int k, int d,
                                             int f, const int32_t *__restrict__ sorted_pair, const Group &grp,
-                                            int nt, float (*red)[2][IMAX][64], uint16_t *__restrict__ h_hi,
-                                            uint16_t *__restrict__ h_lo, const QMatDev &down,
-                                            const QMatDev &sdown, uint16_t *xs) {
+                                            int nt, float (*red)[2][IMAX][64], uint32_t (*redx)[16],
+                                            uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo,
+                                            int32_t *__restrict__ hx, uint16_t *xs) {
     static_assert(NW > 1, "token rows: K split over waves");
     static_assert(TPW == 1 || XL, "several tiles per workgroup share the staged x");
-    constexpr bool kPrefetch = IMAX == 1 && TPW == 1;   // single-token batch
     const int lane = __lane_id();
     // TPW tiles per workgroup: waves [NW g, NW g + NW) take tile nt + g
     const int wall = wave_uniform(threadIdx.x >> 6);
     const int wv = wall % NW, tg = wall / NW;
     nt += tg;
     red += tg * NW;
+    redx += tg * NW;
     const int gq = lane >> 4, rr = lane & 15;
     const bool shared = grp.expert < 0;
     const QMatDev Wg = shared ? sgate : gate;
@@ -234,7 +211,7 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
     const int xr = rr < T ? rr : T - 1;   // the token row of this lane's matrix row
     const uint16_t *xrow[1] = {x + (size_t)xr * d};
     const int cpr = d / 8;                // 16-byte chunks per x row
-    u32x4 pf[kPfPieces];
+    uint32_t xmax = 0u;                   // largest |x| bits of this lane's row over its K slices
     GateUpUnit<FMT, 1> U[kBatch];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
@@ -272,10 +249,6 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
                 if (u < KC) gateup_load_x(U[b], u, gq, xrow);
             }
         }
-        if (kPrefetch && u0 == wv) {
-            __asm__ volatile("" ::: "memory");
-            down_prefetch<FMT>(pf, down, sdown, d, f, grp, nt, f / 16);
-        }
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
             if (u0 + NW * b < KC) {
@@ -288,6 +261,8 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
                             xs + ((size_t)xr * cpr + (c ^ (xr & 7))) * 8);
                     }
                 }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) xmax = max_mag_bf16x8(U[b].A[0][j], xmax);
                 gateup_block<FMT, 1, IMAX, 0>(U[b], ag, au);
                 gateup_block<FMT, 1, IMAX, 1>(U[b], ag, au);
                 gateup_block<FMT, 1, IMAX, 2>(U[b], ag, au);
@@ -300,13 +275,16 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
         red[wv][0][i][lane] = ag[0][i];
         red[wv][1][i][lane] = au[0][i];
     }
-    __syncthreads();
-    if (wv != 0) {
-        if constexpr (kPrefetch)
-#pragma unroll
-            for (int i = 0; i < kPfPieces; ++i) __asm__ volatile("" ::"v"(pf[i]));
-        return;
+    // the row's (lane rr's token) largest |x| over the four lane groups
+    {
+        uint32_t o = (uint32_t)__shfl_xor((int)xmax, 16, 64);
+        xmax = o > xmax ? o : xmax;
+        o = (uint32_t)__shfl_xor((int)xmax, 32, 64);
+        xmax = o > xmax ? o : xmax;
+        if (lane < 16) redx[wv][lane] = xmax;
     }
+    __syncthreads();
+    if (wv != 0) return;
     // output row r = 4 gq + i takes the sums of its token's matrix row
     const int n = nt * 16 + rr;
 #pragma unroll
@@ -316,21 +294,23 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
         const int t = shared ? otok[i] : otok[i] / k;
         const int sl = (t >> 2) * 16 + rr, si = t & 3;
         float gs = red[0][0][si][sl], us = red[0][1][si][sl];
+        uint32_t mx = redx[0][t];
 #pragma unroll
         for (int w2 = 1; w2 < NW; ++w2) {
             gs += red[w2][0][si][sl];
             us += red[w2][1][si][sl];
+            mx = redx[w2][t] > mx ? redx[w2][t] : mx;
         }
-        const float h = swiglu(gs, us);
+        // h * 2^-2a = (g 2^-a) sigmoid(g) (u 2^-a): exact scalings
+        const int a = exp_of_max_bits(mx);
+        const float h = swiglu(gs, us, a);
         const _Float16 hh = static_cast<_Float16>(h);
         const float rem = h - static_cast<float>(hh);
         const size_t off = (size_t)(grp.hrow0 + r) * f + n;
         h_hi[off] = __builtin_bit_cast(uint16_t, hh);
         h_lo[off] = f32_to_f16_bits(rem);
+        if (nt == 0) hx[grp.hrow0 + r] = a;
     }
-    if constexpr (kPrefetch)
-#pragma unroll
-        for (int i = 0; i < kPfPieces; ++i) __asm__ volatile("" ::"v"(pf[i]));
 }
 
 template <int FMT, int MT>
@@ -406,14 +386,25 @@ __device__ __forceinline__ void down_load_w(DownW<FMT, MT, NW> &Wt, const QMatDe
 template <int FMT, int MT, int IMAX, int NW, bool DEV, bool HL>
 __device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev &down, const QMatDev &sdown,
                                           const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
-                                          int d, int f, const Group &grp, int ot, int wq,
-                                          float (*red)[MT][IMAX][64], float *__restrict__ y_pairs,
+                                          const int32_t *__restrict__ hx, int d, int f, const Group &grp, int ot,
+                                          int wq, float (*red)[MT][IMAX][64], float *__restrict__ y_pairs,
                                           float *__restrict__ y_shared, uint16_t *hs) {
     static_assert(!HL || MT == 1, "staged h: groups of at most 8 rows");
     const int lane = __lane_id();
     const int gq = lane >> 4, rr = lane & 15;
     const int KC = f / 128;
     const int nrows = grp.nrows;
+    // the exponents of this lane's output rows (y = acc * 2^2a), loaded
+    // early: their latency runs under the weights'
+    int ya[MT][IMAX];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < IMAX; ++i) {
+            int r = mt * 8 + gq * 4 + i;
+            r = r < nrows ? r : nrows - 1;
+            ya[mt][i] = wq == 0 ? 2 * hx[grp.hrow0 + r] : 0;
+        }
     const int cpr = f / 8;
     const uint16_t *hrow[MT];
 #pragma unroll
@@ -505,7 +496,7 @@ __device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev 
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < IMAX; ++i) {
-            const float y = acc[mt][i] + __shfl_xor(acc[mt][i], 32, 64);
+            const float y = ldexpf(acc[mt][i] + __shfl_xor(acc[mt][i], 32, 64), ya[mt][i]);
             const int r = mt * 8 + gq * 4 + i;
             if (gq >= 2 || r >= nrows) continue;
             float *dst = grp.expert < 0 ? y_shared + (size_t)r * d + o
@@ -574,8 +565,9 @@ __global__ __launch_bounds__(64 * NW * TPW) void gateup_small_kernel(
     QMatDev gate, QMatDev up, QMatDev sgate, QMatDev sup, const uint16_t *__restrict__ x, int T,
     int k, int d, int f, int E, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ sorted_pair, uint16_t *__restrict__ h_hi,
-    uint16_t *__restrict__ h_lo, Group *__restrict__ table, QMatDev down, QMatDev sdown, int slot0) {
+    uint16_t *__restrict__ h_lo, int32_t *__restrict__ hx, Group *__restrict__ table, int slot0) {
     __shared__ float red[NW * TPW][2][IMAX][64];
+    __shared__ uint32_t redx[NW * TPW][16];
     extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];   // XL: x, T * d halves
     Group grp;
     const bool found = find_group(offsets, E, T, T * k, slot0 + (int)blockIdx.y, grp);
@@ -585,7 +577,7 @@ __global__ __launch_bounds__(64 * NW * TPW) void gateup_small_kernel(
     }
     if (!found) return;
     gateup_task<FMT, IMAX, NW, XL, TPW>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp,
-                                        (int)blockIdx.x * TPW, red, h_hi, h_lo, down, sdown, xs_dyn);
+                                        (int)blockIdx.x * TPW, red, redx, h_hi, h_lo, hx, xs_dyn);
 }
 
 // grid: (d_model/16 row tiles, group slots); NW waves split K = d_ff.  FUSE:
@@ -593,7 +585,7 @@ __global__ __launch_bounds__(64 * NW * TPW) void gateup_small_kernel(
 template <int FMT, int MT, int IMAX, int NW, bool FUSE, bool HL>
 __global__ __launch_bounds__(64 * NW) void down_small_kernel(
     QMatDev down, QMatDev sdown, const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
-    int d, int f, const Group *__restrict__ table, float *__restrict__ y_pairs,
+    const int32_t *__restrict__ hx, int d, int f, const Group *__restrict__ table, float *__restrict__ y_pairs,
     float *__restrict__ y_shared, CombineArgs cb) {
     __shared__ float red[NW][MT][IMAX][64];
     extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];   // HL: the group's h rows
@@ -602,7 +594,7 @@ __global__ __launch_bounds__(64 * NW) void down_small_kernel(
         const int wq = wave_uniform(threadIdx.x >> 6);
         DownW<FMT, MT, NW> Wt;
         down_load_w<FMT, MT, NW>(Wt, down, sdown, d, f, grp, blockIdx.x, wq);
-        down_task<FMT, MT, IMAX, NW, FUSE, HL>(Wt, down, sdown, h_hi, h_lo, d, f, grp, blockIdx.x, wq, red,
+        down_task<FMT, MT, IMAX, NW, FUSE, HL>(Wt, down, sdown, h_hi, h_lo, hx, d, f, grp, blockIdx.x, wq, red,
                                                y_pairs, y_shared, xs_dyn);
     }
     if constexpr (FUSE) combine_tile(cb, y_pairs, y_shared, d, blockIdx.x, gridDim.y);
@@ -610,20 +602,22 @@ __global__ __launch_bounds__(64 * NW) void down_small_kernel(
 
 static QMatDev qm(const moe_qmat &m) { return QMatDev{m.lo, m.hi, m.scale, m.min}; }
 
-// h_hi, h_lo [rows][f] (each padded to 128 elements), then the group table
+// h_hi, h_lo [rows][f] (each padded to 128 elements), the group table, then
+// the rows' exponents hx [rows]
 size_t ffn_small_ws_bytes(int d, int f, int E, int T, int k) {
     (void)d;
     const size_t rows = (size_t)T * k + T;
     const size_t P = (size_t)T * k;
     const size_t slots = 1 + ((size_t)E < P ? (size_t)E : P);
-    return 2 * (((rows * f + 127) / 128) * 128) * sizeof(uint16_t) + slots * sizeof(Group) + 256;
+    return 2 * (((rows * f + 127) / 128) * 128) * sizeof(uint16_t) + ((slots * sizeof(Group) + 255) / 256) * 256 +
+           rows * sizeof(int32_t) + 256;
 }
 
 template <int FMT, int MTD, int IMAX>
 static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k,
                              const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
-                             float *y_shared, uint16_t *h_hi, uint16_t *h_lo, Group *table, int parts,
-                             const CombineArgs &cb, hipStream_t s) {
+                             float *y_shared, uint16_t *h_hi, uint16_t *h_lo, int32_t *hx, Group *table,
+                             int parts, const CombineArgs &cb, hipStream_t s) {
     const int d = L.d_model, f = L.d_ff, E = L.n_experts;
     const int P = T * k;
     const int slot0 = (parts & kFfnShared) ? 0 : 1;
@@ -644,20 +638,17 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
     if (T <= 8 && xbytes <= kXsMaxBytes)
         hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, true, 1>), dim3(f / 16, slots),
                            dim3(64 * NWG), (unsigned)xbytes, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up),
-                           x, T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, table, qm(L.down), qm(L.sh_down),
-                           slot0);
+                           x, T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, hx, table, slot0);
     else if (IMAX >= 2 && T <= 16 && xbytes <= 2 * kXsMaxBytes && (f / 16) % 2 == 0)
         // 9 to 16 tokens: x takes up to 64 KiB, so one workgroup of eight
         // waves serves two column tiles with one copy
         hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, IMAX >= 2, IMAX >= 2 ? 2 : 1>), dim3(f / 32, slots),
                            dim3(2 * 64 * NWG), (unsigned)xbytes, s, qm(L.gate), qm(L.up), qm(L.sh_gate),
-                           qm(L.sh_up), x, T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, table, qm(L.down),
-                           qm(L.sh_down), slot0);
+                           qm(L.sh_up), x, T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, hx, table, slot0);
     else
         hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, false, 1>), dim3(f / 16, slots),
                            dim3(64 * NWG), 0, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up), x,
-                           T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, table, qm(L.down), qm(L.sh_down),
-                           slot0);
+                           T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, hx, table, slot0);
     // up to four tokens: the group's h rows (at most T of hi and of lo)
     // staged in LDS (measured: T = 1 +0.7%, T = 2 +9%, T = 4 +3% on Q2,
     // neutral on Q3; at T = 8 it lost 1.5%)
@@ -666,39 +657,39 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
     const bool hl = HLOK && T <= 4 && hbytes <= kXsMaxBytes;
     if (cb.out && hl)
         hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, true, HLOK>), dim3(d / 16, slots),
-                           dim3(64 * NWD), (unsigned)hbytes, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, d, f,
+                           dim3(64 * NWD), (unsigned)hbytes, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f,
                            table, y_pairs, y_shared, cb);
     else if (cb.out)
         hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, true, false>), dim3(d / 16, slots),
-                           dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, d, f, table,
+                           dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f, table,
                            y_pairs, y_shared, cb);
     else if (hl)
         hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, false, HLOK>), dim3(d / 16, slots),
-                           dim3(64 * NWD), (unsigned)hbytes, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, d, f,
+                           dim3(64 * NWD), (unsigned)hbytes, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f,
                            table, y_pairs, y_shared, cb);
     else
         hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, false, false>), dim3(d / 16, slots),
-                           dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, d, f, table,
+                           dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f, table,
                            y_pairs, y_shared, cb);
 }
 
 template <int FMT>
 static void launch_small_t(const moe_layer &L, const uint16_t *x, int T, int k,
                            const int32_t *offsets, const int32_t *sorted_pair, float *y_pairs,
-                           float *y_shared, uint16_t *h_hi, uint16_t *h_lo, Group *table, int parts,
-                           const CombineArgs &cb, hipStream_t s) {
+                           float *y_shared, uint16_t *h_hi, uint16_t *h_lo, int32_t *hx, Group *table,
+                           int parts, const CombineArgs &cb, hipStream_t s) {
     // down M tiles: 8 rows (hi over lo) per tile; gate/up: one 16-token tile
     if (T == 1)
-        launch_small_fmt<FMT, 1, 1>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table,
+        launch_small_fmt<FMT, 1, 1>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, hx, table,
                                     parts, cb, s);
     else if (T == 2)
-        launch_small_fmt<FMT, 1, 2>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table,
+        launch_small_fmt<FMT, 1, 2>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, hx, table,
                                     parts, cb, s);
     else if (T <= 8)
-        launch_small_fmt<FMT, 1, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table,
+        launch_small_fmt<FMT, 1, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, hx, table,
                                     parts, cb, s);
     else   // T <= 16
-        launch_small_fmt<FMT, 2, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table,
+        launch_small_fmt<FMT, 2, 4>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, hx, table,
                                     parts, cb, s);
 }
 
@@ -710,13 +701,16 @@ hipError_t launch_ffn_small(const moe_layer &L, const uint16_t *x, int T, int k,
     uint16_t *h_hi = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + kWsHeader);
     uint16_t *h_lo = h_hi + ((rows * L.d_ff + 127) / 128) * 128;
     Group *table = reinterpret_cast<Group *>(h_lo + ((rows * L.d_ff + 127) / 128) * 128);
+    const size_t slots = 1 + ((size_t)L.n_experts < (size_t)T * k ? (size_t)L.n_experts : (size_t)T * k);
+    int32_t *hx = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(table) +
+                                              ((slots * sizeof(Group) + 255) / 256) * 256);
     const CombineArgs cb{pair_pos, topk_w, out,
                          reinterpret_cast<int32_t *>(static_cast<char *>(ws) + kCombineCnt), T, k};
     if (L.format == MOE_FMT_Q2_B32)
-        launch_small_t<MOE_FMT_Q2_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table,
+        launch_small_t<MOE_FMT_Q2_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, hx, table,
                                         parts, cb, s);
     else
-        launch_small_t<MOE_FMT_Q3_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, table,
+        launch_small_t<MOE_FMT_Q3_B32>(L, x, T, k, offsets, sorted_pair, y_pairs, y_shared, h_hi, h_lo, hx, table,
                                         parts, cb, s);
     return hipGetLastError();
 }

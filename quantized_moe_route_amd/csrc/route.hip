@@ -7,10 +7,12 @@
 //
 // Small T (decode, MTP verify): one launch.  The d x E router matrix (4 MiB
 // fp32 at d=2048, E=512) is the only large read, so it is split over
-// (E/64 column slices) x (d/128 row chunks) workgroups -- 128 of them at the
-// full shape -- each reading 128 rows x 64 columns once.  Partial sums are
-// reduced in a fixed order by the last workgroup to arrive, which also runs
-// the top-k, so the result is deterministic and needs no second launch.
+// (E/32 column slices) x (d/128 row chunks) workgroups -- 256 of them at the
+// full shape, one per compute unit -- each reading 128 rows x 32 columns
+// (whole 128-byte lines) once.  Each column slice's last workgroup adds its
+// partial sums in a fixed order and ranks the slice; the last slice merges
+// the slices' candidate lists into the top-k.  The result is deterministic
+// and needs no second launch.
 //
 // Large T (prefill): a matrix-core GEMM.  fp32 router weights are split
 // exactly into three bf16 terms (truncation: hi + mid + lo == w), x is already
@@ -282,198 +284,487 @@ __device__ __forceinline__ void wave_topk_ord_any(const float *lg, int E, int k,
 }
 
 // ------------------------------------------------------- small T: one launch
-// grid: (ceil(E/64) column slices, d/128 row chunks, ceil(T/8) token tiles),
-// 512 threads: wave w of a workgroup owns 16 router rows, lane = one expert
-// column, for the tile's (up to) 8 tokens.  Partial sums go out at device
-// scope; the last workgroup of a tile to arrive adds the d/128 partials of
-// every (token, expert) of the tile in chunk order, writes the logits and
-// runs the top-k from LDS.  Tiles are independent (a counter line each).
-constexpr int kMaxSmallT = kRouteTile;
+// Three phases in one launch, for tiles of up to 8 tokens:
+//   A. grid (ceil(E/32) column slices x d/128 row chunks, token tiles), 256
+//      threads.  A workgroup reads its 128 rows x 32 columns of the router
+//      matrix -- whole 128-byte lines, 16 bytes per lane, all loads in
+//      flight at once -- multiplies them with the tile's x rows, sums its 32
+//      row groups in a fixed order and publishes the 32 x Tt partial sums at
+//      device scope, then arrives on its column slice's counter.
+//   B. The last workgroup of a column slice to arrive adds the slice's d/128
+//      partial sums in row-chunk order (fixed), adds the bias, writes the
+//      logits and ranks each token's 32 keys; for k <= 32 it publishes the
+//      slice's top k in rank order and arrives on the tile's counter.
+//   C. The last slice of the tile to arrive merges each token's sorted slice
+//      lists, one wave per token.  Two lower bounds on the k-th largest key
+//      prune the lists: the largest k-th entry of a list holding k, and the
+//      k-th largest of the lists' first ceil(k / lists) entries (k keys are at
+//      least either); the few keys at or above both are ranked exactly.  Keys are (order-preserving logit bits, inverted
+//      expert index), unique, so equal logits rank the lower expert first.
+//      For k > 32 it runs the serial wave top-k on the logits instead.  With
+//      offsets given (one tile, k <= 64) it also lists the pairs by expert,
+//      as moe_dispatch does.
+// Every sum runs in a fixed order and the selection is exact, so the result
+// does not depend on arrival order.  Counters each sit on a line of their own
+// (16 arrivals per slice, one per slice per tile).
+constexpr int kRS = 32;                  // router columns per workgroup (one 128-byte line)
+constexpr int kRK = 128;                 // router rows per workgroup
+constexpr int kRT = kRouteTile;          // tokens per tile
+constexpr int kRSMax = 1024 / kRS;       // column slices at E = 1024
+constexpr int kRSurv = kRSMax * kRS;     // phase C: survivors per token (at most every list entry)
+constexpr int kRWaveScr = kRSurv + 64 + 32;   // phase C scratch per wave (u64): survivors, heads, picks
+static_assert(kRouteSliceCntLines == kRouteSmallTMax / kRouteTile * kRSMax, "one counter line per tile and slice");
 
-// With offsets given (a batch of one tile, k <= 64), the last workgroup also
-// lists the pairs by expert, as moe_dispatch does, from the ids it has just
-// picked: one launch instead of two.
-__global__ __launch_bounds__(512) void route_small_kernel(
-    const uint16_t *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
-    float *__restrict__ logits, int T, int d, int E, int k, int32_t *__restrict__ ids,
-    float *__restrict__ w, int32_t *__restrict__ counters, float *__restrict__ partial,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pair_pos,
-    int tail_from) {
-    __shared__ float red[8][kMaxSmallT][64];
-    __shared__ int32_t sel_ids[kMaxSmallT * kWaveTopkMaxK];   // the batch's picks, for the listing
-    __shared__ uint32_t emask[1024];                          // listing: tokens (bits) per expert
-    __shared__ int32_t eoff[1024];                            // listing: first position per expert
-    __shared__ int32_t wtot[8];
-    // one LDS pool: the logits [T][E] for the register top-k (k <= 64), or
-    // the serial top-k's per-wave scratch (k > 64)
-    constexpr int kPoolBytes = 2 * 8 * 1024 * 4;
-    static_assert(kMaxSmallT * 1024 * 4 <= kPoolBytes, "pool too small for the logits");
-    __shared__ __attribute__((aligned(16))) unsigned char pool[kPoolBytes];
-    __shared__ int last_flag;
-    float *lgs = reinterpret_cast<float *>(pool);                       // [T][E], k <= 64
-    float *sel = reinterpret_cast<float *>(pool);                       // [8][1024], k > 64
-    int *seli = reinterpret_cast<int *>(pool + 8 * 1024 * 4);           // [8][1024], k > 64
-    const int cs = blockIdx.x;
-    const int kc = blockIdx.y;
-    const int n_kc = gridDim.y;
-    // this workgroup's token tile: tokens [t0, t0 + T)
-    const int t0 = blockIdx.z * kRouteTile;
-    T = T - t0 < kRouteTile ? T - t0 : kRouteTile;
-    x += (size_t)t0 * d;
-    logits += (size_t)t0 * E;
-    ids += (size_t)t0 * k;
-    w += (size_t)t0 * k;
-    partial += (size_t)blockIdx.z * n_kc * kRouteTile * E;
-    int32_t *const counter = counters + kCntLine * blockIdx.z;
-    const int tid = threadIdx.x;
-    const int col = tid & 63;
-    const int wv = wave_uniform(tid >> 6);
-    const int e = cs * 64 + col;
+__device__ __forceinline__ unsigned long long route_key(float v, int e) {
+    return ((unsigned long long)ord_key(v) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ __forceinline__ float key_value(unsigned long long key) { return ord_value((uint32_t)(key >> 32)); }
+__device__ __forceinline__ int key_expert(unsigned long long key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+__device__ __forceinline__ unsigned long long load_dev_u64(const unsigned long long *p) {
+    return __hip_atomic_load(const_cast<unsigned long long *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev_u64(unsigned long long *p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long max_u64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
 
-    // 16 router rows per thread, all loads in flight together
-    const int c0 = kc * 128 + wv * 16;
-    // unconditional loads at clamped indices (columns past E and tokens past T
-    // are computed and discarded), so they are all in flight at once
-    const int ec = e < E ? e : E - 1;
-    float wrv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) wrv[r] = wr[(size_t)(c0 + r) * E + ec];
-    u32x4 xv[kMaxSmallT][2];
-#pragma unroll
-    for (int t = 0; t < kMaxSmallT; ++t) {
-        const int tc = t < T ? t : 0;
-        xv[t][0] = *reinterpret_cast<const u32x4 *>(x + (size_t)tc * d + c0);
-        xv[t][1] = *reinterpret_cast<const u32x4 *>(x + (size_t)tc * d + c0 + 8);
-    }
-#pragma unroll
-    for (int t = 0; t < kMaxSmallT; ++t) {
-        float a_ = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const uint32_t word = xv[t][r >> 3][(r >> 1) & 3];
-            const float xf = __uint_as_float((r & 1) ? (word & 0xffff0000u) : (word << 16));
-            a_ += xf * wrv[r];
-        }
-        red[wv][t][col] = a_;
-    }
+// Inclusive prefix sum over the wave in registers: four row shifts, then the
+// row broadcasts carry each row's total into the rows above.
+__device__ __forceinline__ int wave_scan_dpp(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
+    return v;
+}
+
+// The listing of moe_dispatch from the batch's picks (ids_s [T][k] in LDS):
+// a token picks an expert at most once, so the pairs of expert e are the
+// tokens in emask[e]; pair p = t k + j goes to (pairs of lower experts) +
+// (tokens before t in emask[e]), the position a stable sort by expert gives.
+// Bit 31 marks an expert some token picked at a rank below tail_from (route
+// tail-skip; with tail_from = k every picked expert): the others list no
+// pairs.  Called by all 256 threads; T <= 8, k <= 64.
+__device__ void list_pairs(const int32_t *ids_s, int T, int E, int k, int tail_from, uint32_t *emask,
+                           int32_t *eoff, int32_t *wtot, int32_t *__restrict__ offsets,
+                           int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pair_pos) {
+    constexpr uint32_t KEEP = 1u << 31;
+    const int tid = threadIdx.x, wv = tid >> 6;
+    for (int e = tid; e < 1024; e += 256) emask[e] = 0u;
     __syncthreads();
-    if (wv == 0 && e < E) {
-        for (int t = 0; t < T; ++t) {
-            float s_ = red[0][t][col];
+    const int P = T * k;
+    for (int p = tid; p < P; p += 256)
+        atomicOr(&emask[ids_s[p]], (1u << (p / k)) | (p % k < tail_from ? KEEP : 0u));
+    __syncthreads();
+    // exclusive scan of the per-expert counts, four experts per thread
+    auto kept_count = [](uint32_t m) { return (m & KEEP) ? __popc(m & ~KEEP) : 0; };
+    const int e0 = 4 * tid;
+    int c[4], sum = 0;
 #pragma unroll
-            for (int w2 = 1; w2 < 8; ++w2) s_ += red[w2][t][col];
-            store_dev(&partial[((size_t)kc * T + t) * E + e], s_);
+    for (int i = 0; i < 4; ++i) {
+        c[i] = kept_count(emask[e0 + i]);
+        sum += c[i];
+    }
+    const int incl = wave_scan_dpp(sum);
+    if (__lane_id() == 63) wtot[wv] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int w2 = 0; w2 < wv; ++w2) run += wtot[w2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        eoff[e0 + i] = run;
+        if (e0 + i < E) offsets[e0 + i] = run;
+        run += c[i];
+    }
+    if (tid == 255) offsets[E] = run;   // all (kept) pairs; slots past E count none
+    __syncthreads();
+    for (int p = tid; p < P; p += 256) {
+        const int e = ids_s[p], t = p / k;
+        const uint32_t m = emask[e];
+        if (m & KEEP) {
+            const int pos = eoff[e] + __popc(m & ((1u << t) - 1u));
+            sorted_pair[pos] = p;
+            pair_pos[p] = pos;
+        } else {
+            pair_pos[p] = -1;
         }
     }
-    publish_then_count(counter, gridDim.x * gridDim.y, last_flag);
+}
+
+// The listing for a single token (pairs p = j): the kept picks (ranks j <
+// tail_from) sorted by expert; pair j's position is the number of kept picks
+// with a lower expert (a token picks an expert once) and offsets[e] counts
+// the kept picks below e.  All 256 threads; ids_s [k] in LDS, k <= 64.
+__device__ void list_pairs_one(const int32_t *ids_s, int E, int k, int tail_from, int32_t *__restrict__ offsets,
+                               int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pair_pos) {
+    const int tid = threadIdx.x;
+    const int kk = tail_from < k ? tail_from : k;   // picks 0 .. kk-1 are kept
+    int id[16];
+    for (int j0 = 0; j0 < kk; j0 += 16) {
+        // 16 picks at a time, all LDS reads in flight
+#pragma unroll
+        for (int j = 0; j < 16; ++j) id[j] = j0 + j < kk ? ids_s[j0 + j] : 0x7fffffff;
+        for (int e = tid; e <= E; e += 256) {
+            int n = j0 == 0 ? 0 : offsets[e];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) n += id[j] < e ? 1 : 0;
+            offsets[e] = n;
+        }
+        if (tid < kk) {
+            const int me = ids_s[tid];
+            int pos = j0 == 0 ? 0 : pair_pos[tid];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) pos += id[j] < me ? 1 : 0;
+            pair_pos[tid] = pos;
+        }
+    }
+    if (tid < kk) sorted_pair[pair_pos[tid]] = tid;
+    else if (tid < k) pair_pos[tid] = -1;
+}
+
+// TT: token slots (1, 2, 4 or 8; >= the tile's token count)
+template <bool VEC, int TT>
+__global__ __launch_bounds__(256) void route_small_kernel(
+    const uint16_t *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
+    float *__restrict__ logits, int T, int d, int E, int k, int32_t *__restrict__ ids, float *__restrict__ w,
+    int32_t *__restrict__ tile_cnt, int32_t *__restrict__ slice_cnt, float *__restrict__ partial,
+    unsigned long long *__restrict__ cand, int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_pair,
+    int32_t *__restrict__ pair_pos, int tail_from) {
+    // one LDS pool, reused by the phases: A 4 KiB, B 2 KiB, C per-wave
+    // scratch (35 KiB), or the serial selection's per-wave scratch (32 KiB)
+    constexpr int kPool = 4 * kRWaveScr * 8;
+    static_assert(4 * 2048 * 4 <= kPool && 4 * TT * kRS * 4 <= kPool, "the pool serves every phase");
+    __shared__ __attribute__((aligned(16))) unsigned char pool[kPool];
+    __shared__ __attribute__((aligned(16))) uint16_t xT[kRK][TT];   // A: x, rows x tokens
+    __shared__ int32_t sel_ids[kRT * kWaveTopkMaxK];                 // C: the picks, for the listing
+    __shared__ uint32_t emask[1024];
+    __shared__ int32_t eoff[1024];
+    __shared__ int32_t wtot[4];
+    __shared__ int last_flag;
+
+    const int ES = (E + kRS - 1) / kRS, KC = d / kRK;
+    const int slice = blockIdx.x % ES, kc = blockIdx.x / ES, tt = blockIdx.y;
+    const int t0 = tt * kRT;
+    const int Tt = T - t0 < kRT ? T - t0 : kRT;
+    const int tid = threadIdx.x, l = __lane_id();
+    const int wv = wave_uniform(tid >> 6);
+    // partial sums of this slice: [KC][kRT][kRS]
+    float *const pslice = partial + ((size_t)tt * ES + slice) * KC * (kRT * kRS);
+
+    // ------------------------------------------------------------- phase A
+    {
+        const int eq = l & 7, rs = l >> 3;
+        const int e0 = slice * kRS + eq * 4;
+        float wv4[4][4];
+        // unconditional loads at clamped addresses (columns past E are
+        // computed and dropped), all in flight together
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = kc * kRK + wv * 32 + i * 8 + rs;
+            const float *src = wr + (size_t)row * E;
+            if constexpr (VEC) {
+                const int ec = e0 < E ? e0 : E - 4;
+                const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src + ec));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) wv4[i][c] = v[c];
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) wv4[i][c] = src[e0 + c < E ? e0 + c : E - 1];
+            }
+        }
+        // x: 16 chunks of 8 rows per token, transposed into xT (token slots
+        // past the tile's end are zero)
+        if (tid < 16 * TT) {
+            const int t = tid >> 4, ch = tid & 15;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (t < Tt) v = *reinterpret_cast<const u32x4 *>(x + (size_t)(t0 + t) * d + kc * kRK + ch * 8);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xT[ch * 8 + j][t] = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
+        }
+        __syncthreads();
+        float acc[TT][4];
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[t][c] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = wv * 32 + i * 8 + rs;
+            uint32_t xw[(TT + 1) / 2];
+#pragma unroll
+            for (int q = 0; q < (TT + 1) / 2; ++q)
+                xw[q] = TT == 1 ? (uint32_t)xT[row][0] : reinterpret_cast<const uint32_t *>(&xT[row][0])[q];
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                const uint32_t word = xw[t >> 1];
+                const float xf = __uint_as_float((t & 1) ? (word & 0xffff0000u) : (word << 16));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[t][c] = fmaf(xf, wv4[i][c], acc[t][c]);
+            }
+        }
+        // the 8 row lanes of a wave (same eq) by butterfly, in a fixed order;
+        // then the 4 waves through LDS
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float v = acc[t][c];
+                v += __shfl_xor(v, 8, 64);
+                v += __shfl_xor(v, 16, 64);
+                v += __shfl_xor(v, 32, 64);
+                acc[t][c] = v;
+            }
+        float *red = reinterpret_cast<float *>(pool);   // [4 waves][TT][32]
+        if (rs == 0) {
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) red[(wv * TT + t) * kRS + eq * 4 + c] = acc[t][c];
+        }
+        __syncthreads();
+        if (tid < TT * kRS) {
+            const int t = tid / kRS, e = tid % kRS;
+            if (t < Tt) {
+                const float s = ((red[(0 * TT + t) * kRS + e] + red[(1 * TT + t) * kRS + e]) +
+                                 red[(2 * TT + t) * kRS + e]) + red[(3 * TT + t) * kRS + e];
+                store_dev(&pslice[(size_t)kc * (kRT * kRS) + t * kRS + e], s);
+            }
+        }
+    }
+    int32_t *const scnt = slice_cnt + (size_t)(tt * kRSMax + slice) * kCntLine;
+    publish_then_count(scnt, KC, last_flag);
     if (!last_flag) return;
-    if (tid == 0) store_dev_int(counter, 0);
-    // last workgroup: sum the partials of every (token, expert) in chunk
-    // order.  A thread takes up to four (token, expert) entries per pass, with
-    // all their partial loads in flight together.
-    for (int idx0 = tid; idx0 < T * E; idx0 += 4 * 512) {
-        const int left = (T * E - (idx0 - tid) + 511) / 512;   // uniform over the block
-        const int nu = left < 4 ? left : 4;
-        float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int q0 = 0; q0 < n_kc; q0 += 16) {
-            float v[4][16];
+    if (tid == 0) store_dev_int(scnt, 0);
+
+    // ------------------------------------------------------------- phase B
+    const int kc32 = k < kRS ? k : kRS;   // picks per slice list
+    {
+        unsigned long long *kl = reinterpret_cast<unsigned long long *>(pool);   // [TT][32]
+        const int t = tid / kRS, e = tid % kRS, eg = slice * kRS + e;
+        // the bias, loaded before the partial sums so their waits cover it
+        const float bv = bias ? bias[eg < E ? eg : E - 1] : 0.f;
+        unsigned long long key = 0ull;
+        if (t < Tt) {
+            // the KC partial sums of (t, e) in row-chunk order, 16 loads in
+            // flight at a time (device-coherent: other workgroups wrote them)
+            float s = 0.f;
+            for (int q0 = 0; q0 < KC; q0 += 16) {
+                float v[16];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (u >= nu) break;
-                const int idx = idx0 + u * 512 < T * E ? idx0 + u * 512 : idx0;
-                const int t = idx / E, ee = idx - t * E;
+                for (int j = 0; j < 16; ++j) {
+                    const int q = q0 + j < KC ? q0 + j : KC - 1;
+                    v[j] = load_dev(&pslice[(size_t)q * (kRT * kRS) + t * kRS + e]);
+                }
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int qc = q0 + i < n_kc ? q0 + i : n_kc - 1;
-                    v[u][i] = load_dev(&partial[((size_t)qc * T + t) * E + ee]);
+                for (int j = 0; j < 16; ++j) s += q0 + j < KC ? v[j] : 0.f;
+            }
+            if (eg < E) {
+                if (bias) s += bv;
+                store_dev(&logits[(size_t)(t0 + t) * E + eg], s);
+                key = route_key(s, eg);
+            }
+        }
+        if (tid < TT * kRS) kl[tid] = key;
+        __syncthreads();
+        if (k <= kRS && t < Tt && eg < E) {
+            // rank among the slice's 32 keys (empty slots hold 0)
+            int rank = 0;
+#pragma unroll
+            for (int j = 0; j < kRS; ++j) rank += kl[t * kRS + j] > key ? 1 : 0;
+            if (rank < kc32) store_dev_u64(&cand[(((size_t)tt * kRT + t) * kRSMax + slice) * kRS + rank], key);
+        }
+    }
+    int32_t *const tcnt = tile_cnt + (size_t)tt * kCntLine;
+    publish_then_count(tcnt, ES, last_flag);
+    if (!last_flag) return;
+    if (tid == 0) store_dev_int(tcnt, 0);
+
+    // ------------------------------------------------------------- phase C
+    const bool listing = offsets != nullptr;
+    if (k <= kRS) {
+        unsigned long long *S = reinterpret_cast<unsigned long long *>(pool) + wv * kRWaveScr;
+        unsigned long long *H = S + kRSurv, *sel = H + 64;
+        const int total = ES * kc32;
+        const int m = (k + ES - 1) / ES;   // heads per list: ES * m >= k
+        for (int t = wv; t < Tt; t += 4) {
+            // the token's slice lists, all loads in flight: entry i = (slice
+            // i / kc32, rank i % kc32); a slice of n < 32 experts lists min(k, n)
+            const unsigned long long *cb = cand + ((size_t)tt * kRT + t) * kRSMax * kRS;
+            unsigned long long v[16];
+            bool ok[16];
+            // unconditional loads (clamped to entry 0, which every list has),
+            // all in flight before the first is used
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int i = l + 64 * j;
+                const int sl = i / kc32, r = i - sl * kc32;
+                const int len = E - sl * kRS < kRS ? E - sl * kRS : kRS;   // experts in slice sl
+                ok[j] = i < total && r < len;
+                v[j] = load_dev_u64(&cb[ok[j] ? (size_t)sl * kRS + r : 0]);
+            }
+            unsigned long long tha = 0ull;
+            int nh = 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int i = l + 64 * j;
+                const int r = i % kc32;
+                v[j] = ok[j] ? v[j] : 0ull;
+                // bound a: the largest k-th entry of a list that holds k
+                if (ok[j] && r == k - 1) tha = max_u64(tha, v[j]);
+                nh += (ok[j] && r < m) ? 1 : 0;
+            }
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) tha = max_u64(tha, __shfl_xor(tha, o, 64));
+            // bound b: the k-th largest list head (the first m entries of
+            // every list), when there are at least k heads
+            const int hi = wave_scan_dpp(nh);
+            const int hn = __shfl(hi, 63, 64);
+            {
+                int pos = hi - nh;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int i = l + 64 * j;
+                    const int r = i % kc32;
+                    if (v[j] != 0ull && r < m) H[pos++] = v[j];
                 }
             }
+            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            unsigned long long thb = 0ull;
+            if (hn >= k) {
+                const unsigned long long hk = l < hn ? H[l] : 0ull;
+                int hr = 0;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (u >= nu) break;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sum[u] += q0 + i < n_kc ? v[u][i] : 0.0f;
+                for (int j = 0; j < 64; ++j) hr += (j < hn && H[j] > hk) ? 1 : 0;
+                const unsigned long long hit = __ballot(l < hn && hr == k - 1);
+                thb = hit ? __shfl(hk, __builtin_ctzll(hit), 64) : 0ull;
             }
-        }
+            // survivors: entries >= theta (every key of the top k is one;
+            // k keys are at least either bound)
+            const unsigned long long th = max_u64(tha, thb);
+            int c = 0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int idx = idx0 + u * 512;
-            if (u >= nu || idx >= T * E) continue;
-            const int ee = idx % E;
-            const float s_ = bias ? sum[u] + bias[ee] : sum[u];
-            logits[idx] = s_;
-            if (k <= kWaveTopkMaxK) lgs[idx] = s_;
+            for (int j = 0; j < 16; ++j) c += (v[j] != 0ull && v[j] >= th) ? 1 : 0;
+            const int incl = wave_scan_dpp(c);
+            const int n = __shfl(incl, 63, 64);
+            {
+                int pos = incl - c;
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (v[j] != 0ull && v[j] >= th) S[pos++] = v[j];
+            }
+            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            // exact ranks among the survivors, 16 LDS reads in flight
+            for (int i = l; i < ((n + 63) & ~63); i += 64) {
+                const unsigned long long key = i < n ? S[i] : 0ull;
+                int rank = 0;
+                for (int j0 = 0; j0 < n; j0 += 16) {
+                    unsigned long long o[16];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) o[j] = S[j0 + j < n ? j0 + j : 0];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) rank += (j0 + j < n && o[j] > key) ? 1 : 0;
+                }
+                if (i < n && rank < k) sel[rank] = key;
+            }
+            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const unsigned long long key = l < k ? sel[l] : 0ull;
+            const float lv = key_value(key);
+            const float l0 = __shfl(lv, 0, 64);
+            const float ev = l < k ? expf(lv - l0) : 0.0f;
+            const float inv = 1.0f / wave_sum(ev);
+            if (l < k) {
+                const int e = key_expert(key);
+                ids[(size_t)(t0 + t) * k + l] = e;
+                w[(size_t)(t0 + t) * k + l] = ev * inv;
+                if (listing) sel_ids[t * k + l] = e;
+            }
+            // the next token of this wave reuses S, H and sel
+            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
-    }
-    __syncthreads();
-    // one wave per token
-    if (k <= kWaveTopkMaxK) {
-        for (int t = wv; t < T; t += 8)
-            wave_topk_ord_any(lgs + t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k,
-                              offsets ? sel_ids + t * k : nullptr);
-        if (!offsets) return;
-        // The listing: a token picks an expert at most once, so the pairs of
-        // expert e are the tokens in emask[e]; pair p = t k + j goes to
-        // (pairs of lower experts) + (tokens before t in emask[e]), the
-        // position a stable sort by expert gives.  Bit 31 marks an expert
-        // some token picked at a rank below tail_from (route tail-skip; with
-        // tail_from = k every picked expert): the others list no pairs.
-        constexpr uint32_t KEEP = 1u << 31;
-        for (int e = tid; e < 1024; e += 512) emask[e] = 0u;
-        __syncthreads();
-        const int P = T * k;
-        if (tid < P) atomicOr(&emask[sel_ids[tid]], (1u << (tid / k)) | (tid % k < tail_from ? KEEP : 0u));
-        __syncthreads();
-        // exclusive scan of the per-expert counts, two experts per thread
-        const int e0 = 2 * tid;
-        auto kept_count = [](uint32_t m) { return (m & KEEP) ? __popc(m & ~KEEP) : 0; };
-        const int c0 = kept_count(emask[e0]), c1 = kept_count(emask[e0 + 1]);
-        const int incl = wave_incl_scan(c0 + c1);
-        if (__lane_id() == 63) wtot[wv] = incl;
-        __syncthreads();
-        int base = 0;
-        for (int w2 = 0; w2 < wv; ++w2) base += wtot[w2];
-        const int ex = base + incl - (c0 + c1);
-        eoff[e0] = ex;
-        eoff[e0 + 1] = ex + c0;
-        if (e0 < E) offsets[e0] = ex;
-        if (e0 + 1 < E) offsets[e0 + 1] = ex + c0;
-        if (tid == 511) offsets[E] = base + incl;   // all pairs (slots past E count none)
-        __syncthreads();
-        if (tid < P) {
-            const int e = sel_ids[tid], t = tid / k;
-            const uint32_t m = emask[e];
-            if (m & KEEP) {
-                const int pos = eoff[e] + __popc(m & ((1u << t) - 1u));
-                sorted_pair[pos] = tid;
-                pair_pos[tid] = pos;
+    } else {
+        // large k: per-token wave top-k on the logits (device-scope loads:
+        // other workgroups wrote them)
+        float *selv = reinterpret_cast<float *>(pool) + wv * 2048;
+        int *seli = reinterpret_cast<int *>(selv + 1024);
+        for (int t = wv; t < Tt; t += 4) {
+            const float *lg = logits + (size_t)(t0 + t) * E;
+            if (k <= kWaveTopkMaxK) {
+                // ordered keys in registers; picks into sel_ids for the listing
+                float *lgs = selv;   // this wave's scratch: the token's logits
+                for (int e = l; e < E; e += 64) lgs[e] = load_dev(&lg[e]);
+                __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                wave_topk_ord_any(lgs, E, k, ids + (size_t)(t0 + t) * k, w + (size_t)(t0 + t) * k,
+                                  listing ? sel_ids + t * k : nullptr);
             } else {
-                pair_pos[tid] = -1;
+                wave_topk_any<true>(lg, E, k, ids + (size_t)(t0 + t) * k, w + (size_t)(t0 + t) * k, selv, seli);
             }
+            // the next token of this wave reuses the scratch
+            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
-        return;
     }
-    // large k: serial selection per token from the logits just written
-    for (int t = wv; t < T; t += 8)
-        wave_topk_any<false>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k,
-                             sel + wv * 1024, seli + wv * 1024);
+    if (!listing) return;
+    __syncthreads();
+    if (Tt == 1)
+        list_pairs_one(sel_ids, E, k, tail_from, offsets, sorted_pair, pair_pos);
+    else
+        list_pairs(sel_ids, Tt, E, k, tail_from, emask, eoff, wtot, offsets, sorted_pair, pair_pos);
+}
+
+// workspace after the header: the partial sums [tiles][ES][d/128][kRT][kRS],
+// then the candidate lists [tiles][kRT][kRSMax][kRS]
+static size_t route_partial_bytes(int d, int E, int T) {
+    const size_t tiles = (size_t)(T + kRT - 1) / kRT, ES = (size_t)(E + kRS - 1) / kRS;
+    return tiles * ES * (size_t)(d / kRK) * kRT * kRS * sizeof(float);
 }
 
 size_t route_ws_bytes(int d, int E, int T) {
     if (T > kRouteSmallTMax) return router_gemm_ws_bytes(d, E);
-    const size_t tiles = (size_t)(T + kRouteTile - 1) / kRouteTile;
-    return (size_t)(d / 128) * tiles * kRouteTile * E * sizeof(float);
+    const size_t tiles = (size_t)(T + kRT - 1) / kRT;
+    return route_partial_bytes(d, E, T) + tiles * kRT * kRSMax * kRS * sizeof(unsigned long long);
+}
+
+template <bool VEC>
+static void launch_route_small_v(dim3 grid, int TT, hipStream_t s, const uint16_t *x, const float *wr,
+                                 const float *bias, float *logits, int T, int d, int E, int k, int32_t *ids, float *w,
+                                 int32_t *tile_cnt, int32_t *slice_cnt, float *partial, unsigned long long *cand,
+                                 int32_t *offsets, int32_t *sorted_pair, int32_t *pair_pos, int tail_from) {
+#define MOE_ROUTE_LAUNCH(TTV)                                                                                        \
+    hipLaunchKernelGGL((route_small_kernel<VEC, TTV>), grid, dim3(256), 0, s, x, wr, bias, logits, T, d, E, k, ids, \
+                       w, tile_cnt, slice_cnt, partial, cand, offsets, sorted_pair, pair_pos, tail_from)
+    if (TT == 1)
+        MOE_ROUTE_LAUNCH(1);
+    else if (TT == 2)
+        MOE_ROUTE_LAUNCH(2);
+    else if (TT == 4)
+        MOE_ROUTE_LAUNCH(4);
+    else
+        MOE_ROUTE_LAUNCH(8);
+#undef MOE_ROUTE_LAUNCH
 }
 
 hipError_t launch_route_small(const uint16_t *x, const float *wr, const float *bias, float *logits,
                               int T, int d, int E, int k, int32_t *ids, float *w, void *ws,
                               hipStream_t s, int32_t *offsets, int32_t *sorted_pair, int32_t *pair_pos,
                               int tail_from) {
-    int32_t *counters = reinterpret_cast<int32_t *>(ws);
-    float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + kWsHeader);
-    dim3 grid((E + 63) / 64, d / 128, (T + kRouteTile - 1) / kRouteTile);
-    hipLaunchKernelGGL(route_small_kernel, grid, dim3(512), 0, s, x, wr, bias, logits, T, d, E, k,
-                       ids, w, counters, partial, offsets, sorted_pair, pair_pos, tail_from < 0 ? k : tail_from);
+    char *base = static_cast<char *>(ws);
+    int32_t *tile_cnt = reinterpret_cast<int32_t *>(base);
+    int32_t *slice_cnt = reinterpret_cast<int32_t *>(base + kRouteSliceCnt);
+    float *partial = reinterpret_cast<float *>(base + kWsHeader);
+    unsigned long long *cand =
+        reinterpret_cast<unsigned long long *>(base + kWsHeader + route_partial_bytes(d, E, T));
+    const int ES = (E + kRS - 1) / kRS, KC = d / kRK;
+    const dim3 grid(ES * KC, (T + kRT - 1) / kRT);
+    // token slots: the batch itself up to one tile, else full tiles
+    const int TT = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
+    const int tf = tail_from < 0 ? k : tail_from;
+    if (E % 4 == 0)
+        launch_route_small_v<true>(grid, TT, s, x, wr, bias, logits, T, d, E, k, ids, w, tile_cnt, slice_cnt, partial,
+                                   cand, offsets, sorted_pair, pair_pos, tf);
+    else
+        launch_route_small_v<false>(grid, TT, s, x, wr, bias, logits, T, d, E, k, ids, w, tile_cnt, slice_cnt,
+                                    partial, cand, offsets, sorted_pair, pair_pos, tf);
     return hipGetLastError();
 }
 

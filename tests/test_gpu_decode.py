@@ -12,9 +12,11 @@ import oracle
 import synth
 from tests import packing
 
-# the workspace's counter header: 4 KiB for the router, one 128-byte line
-# per 16-column output tile (up to d = 16,384) for the fused combine
-WS_HEADER = 4096 + 1024 * 128
+# the workspace's counter header: 4 KiB for the router's token tiles (and
+# the error word), one 128-byte line per 16-column output tile (d <= 16,384)
+# for the fused combine, one line per (token tile, 32-expert slice) for the
+# router
+WS_HEADER = 4096 + 1024 * 128 + 16 * 32 * 128
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
