@@ -9,10 +9,9 @@
 // fp32 at d=2048, E=512) is the only large read, so it is split over
 // (E/32 column slices) x (d/128 row chunks) workgroups -- 256 of them at the
 // full shape, one per compute unit -- each reading 128 rows x 32 columns
-// (whole 128-byte lines) once.  Each column slice's last workgroup adds its
-// partial sums in a fixed order and ranks the slice; the last slice merges
-// the slices' candidate lists into the top-k.  The result is deterministic
-// and needs no second launch.
+// (whole 128-byte lines) once.  The tile's last workgroup to finish adds
+// the partial sums in a fixed order and selects the top k, one wave per
+// token.  The result is deterministic and needs no second launch.
 //
 // Large T (prefill): a matrix-core GEMM.  fp32 router weights are split
 // exactly into three bf16 terms (truncation: hi + mid + lo == w), x is already
@@ -284,35 +283,29 @@ __device__ __forceinline__ void wave_topk_ord_any(const float *lg, int E, int k,
 }
 
 // ------------------------------------------------------- small T: one launch
-// Three phases in one launch, for tiles of up to 8 tokens:
+// Two phases in one launch, for tiles of up to 8 tokens:
 //   A. grid (ceil(E/32) column slices x d/128 row chunks, token tiles), 256
 //      threads.  A workgroup reads its 128 rows x 32 columns of the router
 //      matrix -- whole 128-byte lines, 16 bytes per lane, all loads in
 //      flight at once -- multiplies them with the tile's x rows, sums its 32
 //      row groups in a fixed order and publishes the 32 x Tt partial sums at
-//      device scope, then arrives on its column slice's counter.
-//   B. The last workgroup of a column slice to arrive adds the slice's d/128
-//      partial sums in row-chunk order (fixed), adds the bias, writes the
-//      logits and ranks each token's 32 keys; for k <= 32 it publishes the
-//      slice's top k in rank order and arrives on the tile's counter.
-//   C. The last slice of the tile to arrive merges each token's sorted slice
-//      lists, one wave per token.  Two lower bounds on the k-th largest key
-//      prune the lists: the largest k-th entry of a list holding k, and the
-//      k-th largest of the lists' first ceil(k / lists) entries (k keys are at
-//      least either); the few keys at or above both are ranked exactly.  Keys are (order-preserving logit bits, inverted
-//      expert index), unique, so equal logits rank the lower expert first.
-//      For k > 32 it runs the serial wave top-k on the logits instead.  With
-//      offsets given (one tile, k <= 64) it also lists the pairs by expert,
-//      as moe_dispatch does.
+//      device scope.  It arrives on its column slice's counter; the slice's
+//      last workgroup arrives on the tile's counter (two levels of 16
+//      arrivals instead of one of 256: arrivals on one line are served one
+//      after another).
+//   B. The tile's last workgroup adds each logit's d/128 partial sums in
+//      row-chunk order (fixed), adds the bias and writes the logits; then,
+//      one wave per token, selects the top k (wave_select) and writes ids and
+//      weights.  With offsets given (one tile, k <= 64) it also lists the
+//      pairs by expert, as moe_dispatch does.
 // Every sum runs in a fixed order and the selection is exact, so the result
-// does not depend on arrival order.  Counters each sit on a line of their own
-// (16 arrivals per slice, one per slice per tile).
+// does not depend on arrival order.
 constexpr int kRS = 32;                  // router columns per workgroup (one 128-byte line)
 constexpr int kRK = 128;                 // router rows per workgroup
 constexpr int kRT = kRouteTile;          // tokens per tile
 constexpr int kRSMax = 1024 / kRS;       // column slices at E = 1024
-constexpr int kRSurv = kRSMax * kRS;     // phase C: survivors per token (at most every list entry)
-constexpr int kRWaveScr = kRSurv + 64 + 32;   // phase C scratch per wave (u64): survivors, heads, picks
+constexpr int kRGroup = 4;               // tokens per selection round (one wave each)
+constexpr int kRRow = 1024 + 64;         // LDS key row per token: 64 P keys, then the survivors' zero pad
 static_assert(kRouteSliceCntLines == kRouteSmallTMax / kRouteTile * kRSMax, "one counter line per tile and slice");
 
 __device__ __forceinline__ unsigned long long route_key(float v, int e) {
@@ -320,12 +313,6 @@ __device__ __forceinline__ unsigned long long route_key(float v, int e) {
 }
 __device__ __forceinline__ float key_value(unsigned long long key) { return ord_value((uint32_t)(key >> 32)); }
 __device__ __forceinline__ int key_expert(unsigned long long key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
-__device__ __forceinline__ unsigned long long load_dev_u64(const unsigned long long *p) {
-    return __hip_atomic_load(const_cast<unsigned long long *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_dev_u64(unsigned long long *p, unsigned long long v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ unsigned long long max_u64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
 
 // Inclusive prefix sum over the wave in registers: four row shifts, then the
@@ -338,6 +325,115 @@ __device__ __forceinline__ int wave_scan_dpp(int v) {
     v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
     v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
     return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_max_u64(unsigned long long v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    return max_u64(v, ((unsigned long long)hi << 32) | lo);
+}
+// The maximum over each aligned group of L lanes (L a power of two <= 64).
+__device__ __forceinline__ unsigned long long group_max_u64(unsigned long long v, int L) {
+    if (L > 1) v = dpp_max_u64<0xB1>(v);    // quad_perm [1,0,3,2]
+    if (L > 2) v = dpp_max_u64<0x4E>(v);    // quad_perm [2,3,0,1]
+    if (L > 4) v = dpp_max_u64<0x141>(v);   // row_half_mirror: the two quads of each 8
+    if (L > 8) v = dpp_max_u64<0x140>(v);   // row_mirror: the two halves of each 16
+    if (L > 16) v = max_u64(v, __shfl_xor(v, 16, 64));
+    if (L > 32) v = max_u64(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int lane) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// The k (<= 64) largest keys of a wave; lane j returns the j-th (0 in lanes
+// >= k).  Lane l holds v[i], the key of item l + 64 i (0 = no item; keys are
+// unique and nonzero) and the wave holds at least k items.  A lower bound
+// prunes first: the lanes form G >= k groups of L = 64 / G; the k-th largest
+// of the G group maxima is reached by at least k keys (those maxima), so
+// every key of the top k reaches it.  The keys at or above the bound -- a few
+// more than k for typical logits -- are compacted into LDS and ranked
+// exactly against each other.  Per-wave LDS scratch: M and sel of 64 keys
+// each, S of 64 P + 16 keys.
+template <int P>
+__device__ unsigned long long wave_select(const unsigned long long (&v)[P], int k, unsigned long long *M,
+                                          unsigned long long *sel, unsigned long long *S) {
+    const int l = __lane_id();
+    int G = 1;
+    while (G < k) G <<= 1;
+    const int lg = 6 - __builtin_ctz(G);    // log2 of L = 64 / G
+    unsigned long long gm = v[0];
+#pragma unroll
+    for (int i = 1; i < P; ++i) gm = max_u64(gm, v[i]);
+    gm = group_max_u64(gm, 1 << lg);
+    // the group maxima, padded with zeros to whole reads of 16
+    const int Gp = (G + 15) & ~15;
+    if (l < Gp) M[l] = 0ull;
+    if ((l & ((1 << lg) - 1)) == 0) M[l >> lg] = gm;
+    int rk = 0;
+    for (int j0 = 0; j0 < Gp; j0 += 16) {
+        unsigned long long o[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[j] = M[j0 + j];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) rk += o[j] > gm ? 1 : 0;
+    }
+    // the bound: the group maximum of rank k - 1 (with fewer than k nonzero
+    // maxima every key stays)
+    const unsigned long long hit = __ballot(rk == k - 1 && gm != 0ull);
+    const unsigned long long th = hit ? readlane_u64(gm, __builtin_ctzll(hit)) : 1ull;
+    // survivors, compacted in lane order
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i) c += v[i] >= th ? 1 : 0;
+    const int incl = wave_scan_dpp(c);
+    const int n = __builtin_amdgcn_readlane(incl, 63);
+    int pos = incl - c;
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+        if (v[i] >= th) S[pos++] = v[i];
+    if (l < 16) S[n + l] = 0ull;   // zero keys rank below every key
+    // exact ranks: 16 LDS reads in flight per step
+    for (int i0 = 0; i0 < n; i0 += 64) {
+        const int i = i0 + l;
+        const unsigned long long key = S[i < n ? i : n];
+        int rank = 0;
+        for (int j0 = 0; j0 < n; j0 += 16) {
+            unsigned long long o[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[j] = S[j0 + j];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) rank += o[j] > key ? 1 : 0;
+        }
+        if (i < n && rank < k) sel[rank] = key;
+    }
+    return l < k ? sel[l] : 0ull;
+}
+
+// One token's selection from its LDS key row (row[e] for e < 64 P, zero past
+// E): ids, weights (softmax over the k picks) and, if asked, the picks in
+// ids_lds for the listing.  The row is reused as the survivors' scratch.
+template <int P>
+__device__ void select_token(unsigned long long *row, int k, unsigned long long *M, unsigned long long *sel,
+                             int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_lds) {
+    const int l = __lane_id();
+    unsigned long long v[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) v[i] = row[l + 64 * i];
+    const unsigned long long my = wave_select<P>(v, k, M, sel, row);
+    const float lv = key_value(my);
+    const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), 0));
+    const float ev = l < k ? expf(lv - l0) : 0.0f;
+    const float inv = 1.0f / wave_sum(ev);
+    if (l < k) {
+        const int e = key_expert(my);
+        ids[l] = e;
+        w[l] = ev * inv;
+        if (ids_lds) ids_lds[l] = e;
+    }
 }
 
 // The listing of moe_dispatch from the batch's picks (ids_s [T][k] in LDS):
@@ -396,32 +492,51 @@ __device__ void list_pairs(const int32_t *ids_s, int T, int E, int k, int tail_f
 // The listing for a single token (pairs p = j): the kept picks (ranks j <
 // tail_from) sorted by expert; pair j's position is the number of kept picks
 // with a lower expert (a token picks an expert once) and offsets[e] counts
-// the kept picks below e.  All 256 threads; ids_s [k] in LDS, k <= 64.
+// the kept picks below e.  All 256 threads; ids_s [>= 64] in LDS, k <= 64,
+// E <= 1024.  Counts stay in registers until the end.
 __device__ void list_pairs_one(const int32_t *ids_s, int E, int k, int tail_from, int32_t *__restrict__ offsets,
                                int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pair_pos) {
     const int tid = threadIdx.x;
     const int kk = tail_from < k ? tail_from : k;   // picks 0 .. kk-1 are kept
-    int id[16];
+    const int R = E / 256 + 1;                      // offsets slots per thread: e = tid + 256 r <= E
+    const int me = ids_s[tid & 63];
+    int n[5] = {0, 0, 0, 0, 0};
+    int pos = 0;
     for (int j0 = 0; j0 < kk; j0 += 16) {
-        // 16 picks at a time, all LDS reads in flight
+        // 16 picks at a time: unconditional LDS reads (ids_s holds 64),
+        // picks past kk count as no expert
+        int id[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) id[j] = j0 + j < kk ? ids_s[j0 + j] : 0x7fffffff;
-        for (int e = tid; e <= E; e += 256) {
-            int n = j0 == 0 ? 0 : offsets[e];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) n += id[j] < e ? 1 : 0;
-            offsets[e] = n;
+        for (int j = 0; j < 16; ++j) {
+            const int r = ids_s[j0 + j];
+            id[j] = j0 + j < kk ? r : 0x7fffffff;
         }
-        if (tid < kk) {
-            const int me = ids_s[tid];
-            int pos = j0 == 0 ? 0 : pair_pos[tid];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) pos += id[j] < me ? 1 : 0;
-            pair_pos[tid] = pos;
+        for (int r = 0; r < 5; ++r) {
+            if (r < R) {
+                const int e = tid + 256 * r;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) n[r] += id[j] < e ? 1 : 0;
+            }
         }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) pos += id[j] < me ? 1 : 0;
     }
-    if (tid < kk) sorted_pair[pair_pos[tid]] = tid;
-    else if (tid < k) pair_pos[tid] = -1;
+#pragma unroll
+    for (int r = 0; r < 5; ++r)
+        if (r < R && tid + 256 * r <= E) offsets[tid + 256 * r] = n[r];
+    if (tid < kk) {
+        pair_pos[tid] = pos;
+        sorted_pair[pos] = tid;
+    } else if (tid < k) {
+        pair_pos[tid] = -1;
+    }
+}
+
+// Device-coherent 16-byte load (sc1: served by the level all XCDs share)
+// through a buffer resource; byte offsets past `bytes` read zero.
+__device__ __forceinline__ f32x4 load_dev_f4(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 16));
 }
 
 // TT: token slots (1, 2, 4 or 8; >= the tile's token count)
@@ -430,19 +545,19 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
     float *__restrict__ logits, int T, int d, int E, int k, int32_t *__restrict__ ids, float *__restrict__ w,
     int32_t *__restrict__ tile_cnt, int32_t *__restrict__ slice_cnt, float *__restrict__ partial,
-    unsigned long long *__restrict__ cand, int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_pair,
-    int32_t *__restrict__ pair_pos, int tail_from) {
-    // one LDS pool, reused by the phases: A 4 KiB, B 2 KiB, C per-wave
-    // scratch (35 KiB), or the serial selection's per-wave scratch (32 KiB)
-    constexpr int kPool = 4 * kRWaveScr * 8;
-    static_assert(4 * 2048 * 4 <= kPool && 4 * TT * kRS * 4 <= kPool, "the pool serves every phase");
-    __shared__ __attribute__((aligned(16))) unsigned char pool[kPool];
-    __shared__ __attribute__((aligned(16))) uint16_t xT[kRK][TT];   // A: x, rows x tokens
-    __shared__ int32_t sel_ids[kRT * kWaveTopkMaxK];                 // C: the picks, for the listing
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pair_pos,
+    int tail_from) {
+    // key rows of kRGroup tokens (B); phase A's cross-wave sums and the
+    // serial selection's scratch (k > 64) live in the same memory
+    __shared__ __attribute__((aligned(16))) unsigned long long keys[kRGroup][kRRow];
+    __shared__ __attribute__((aligned(16))) unsigned long long wscr[4][128];   // per wave: M, sel
+    __shared__ __attribute__((aligned(16))) uint16_t xT[kRK][TT];             // A: x, rows x tokens
+    __shared__ int32_t sel_ids[kRT * kWaveTopkMaxK];                          // B: the picks, for the listing
     __shared__ uint32_t emask[1024];
     __shared__ int32_t eoff[1024];
     __shared__ int32_t wtot[4];
-    __shared__ int last_flag;
+    __shared__ int last_flag, tile_flag;
+    static_assert(4 * TT * kRS * 4 <= sizeof(keys), "phase A's sums fit the key rows");
 
     const int ES = (E + kRS - 1) / kRS, KC = d / kRK;
     const int slice = blockIdx.x % ES, kc = blockIdx.x / ES, tt = blockIdx.y;
@@ -450,13 +565,19 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     const int Tt = T - t0 < kRT ? T - t0 : kRT;
     const int tid = threadIdx.x, l = __lane_id();
     const int wv = wave_uniform(tid >> 6);
-    // partial sums of this slice: [KC][kRT][kRS]
-    float *const pslice = partial + ((size_t)tt * ES + slice) * KC * (kRT * kRS);
+    // partial sums of the tile: [ES][KC][kRT][kRS]
+    float *const ptile = partial + (size_t)tt * ES * KC * (kRT * kRS);
 
     // ------------------------------------------------------------- phase A
     {
         const int eq = l & 7, rs = l >> 3;
         const int e0 = slice * kRS + eq * 4;
+        // row chunk 0 adds the bias to its partial sums (a 0-byte resource
+        // elsewhere reads zeros); loaded with the router rows
+        const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(bias), 0, (bias && kc == 0) ? E * (int)sizeof(float) : 0, 0x00020000);
+        const float bias_e = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(brs, 4 * (slice * kRS + (tid & (kRS - 1))), 0, 0));
         float wv4[4][4];
         // unconditional loads at clamped addresses (columns past E are
         // computed and dropped), all in flight together
@@ -516,7 +637,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
                 v += __shfl_xor(v, 32, 64);
                 acc[t][c] = v;
             }
-        float *red = reinterpret_cast<float *>(pool);   // [4 waves][TT][32]
+        float *red = reinterpret_cast<float *>(&keys[0][0]);   // [4 waves][TT][32]
         if (rs == 0) {
 #pragma unroll
             for (int t = 0; t < TT; ++t)
@@ -527,212 +648,168 @@ __global__ __launch_bounds__(256) void route_small_kernel(
         if (tid < TT * kRS) {
             const int t = tid / kRS, e = tid % kRS;
             if (t < Tt) {
-                const float s = ((red[(0 * TT + t) * kRS + e] + red[(1 * TT + t) * kRS + e]) +
-                                 red[(2 * TT + t) * kRS + e]) + red[(3 * TT + t) * kRS + e];
-                store_dev(&pslice[(size_t)kc * (kRT * kRS) + t * kRS + e], s);
+                const float s = (((red[(0 * TT + t) * kRS + e] + red[(1 * TT + t) * kRS + e]) +
+                                  red[(2 * TT + t) * kRS + e]) + red[(3 * TT + t) * kRS + e]) + bias_e;
+                store_dev(&ptile[(((size_t)slice * KC + kc) * kRT + t) * kRS + e], s);
             }
         }
     }
+    // two-level arrival: the slice's counter, then (its last chunk) the tile's
     int32_t *const scnt = slice_cnt + (size_t)(tt * kRSMax + slice) * kCntLine;
     publish_then_count(scnt, KC, last_flag);
     if (!last_flag) return;
-    if (tid == 0) store_dev_int(scnt, 0);
+    int32_t *const tcnt = tile_cnt + (size_t)tt * kCntLine;
+    if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(tcnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        tile_flag = old == ES - 1;
+    }
+    __syncthreads();
+    if (!tile_flag) return;
+    // The tile's last workgroup resets the tile's counters at its very end: a
+    // store issued before its loads would delay them (the memory counter
+    // retires in order).
 
     // ------------------------------------------------------------- phase B
-    const int kc32 = k < kRS ? k : kRS;   // picks per slice list
-    {
-        unsigned long long *kl = reinterpret_cast<unsigned long long *>(pool);   // [TT][32]
-        const int t = tid / kRS, e = tid % kRS, eg = slice * kRS + e;
-        // the bias, loaded before the partial sums so their waits cover it
-        const float bv = bias ? bias[eg < E ? eg : E - 1] : 0.f;
-        unsigned long long key = 0ull;
-        if (t < Tt) {
-            // the KC partial sums of (t, e) in row-chunk order, 16 loads in
-            // flight at a time (device-coherent: other workgroups wrote them)
-            float s = 0.f;
-            for (int q0 = 0; q0 < KC; q0 += 16) {
-                float v[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int q = q0 + j < KC ? q0 + j : KC - 1;
-                    v[j] = load_dev(&pslice[(size_t)q * (kRT * kRS) + t * kRS + e]);
-                }
-#pragma unroll
-                for (int j = 0; j < 16; ++j) s += q0 + j < KC ? v[j] : 0.f;
-            }
-            if (eg < E) {
-                if (bias) s += bv;
-                store_dev(&logits[(size_t)(t0 + t) * E + eg], s);
-                key = route_key(s, eg);
-            }
-        }
-        if (tid < TT * kRS) kl[tid] = key;
-        __syncthreads();
-        if (k <= kRS && t < Tt && eg < E) {
-            // rank among the slice's 32 keys (empty slots hold 0)
-            int rank = 0;
-#pragma unroll
-            for (int j = 0; j < kRS; ++j) rank += kl[t * kRS + j] > key ? 1 : 0;
-            if (rank < kc32) store_dev_u64(&cand[(((size_t)tt * kRT + t) * kRSMax + slice) * kRS + rank], key);
-        }
-    }
-    int32_t *const tcnt = tile_cnt + (size_t)tt * kCntLine;
-    publish_then_count(tcnt, ES, last_flag);
-    if (!last_flag) return;
-    if (tid == 0) store_dev_int(tcnt, 0);
-
-    // ------------------------------------------------------------- phase C
     const bool listing = offsets != nullptr;
-    if (k <= kRS) {
-        unsigned long long *S = reinterpret_cast<unsigned long long *>(pool) + wv * kRWaveScr;
-        unsigned long long *H = S + kRSurv, *sel = H + 64;
-        const int total = ES * kc32;
-        const int m = (k + ES - 1) / ES;   // heads per list: ES * m >= k
-        for (int t = wv; t < Tt; t += 4) {
-            // the token's slice lists, all loads in flight: entry i = (slice
-            // i / kc32, rank i % kc32); a slice of n < 32 experts lists min(k, n)
-            const unsigned long long *cb = cand + ((size_t)tt * kRT + t) * kRSMax * kRS;
-            unsigned long long v[16];
-            bool ok[16];
-            // unconditional loads (clamped to entry 0, which every list has),
-            // all in flight before the first is used
+    const int E4 = (E + 3) >> 2;
+    const int Pk = E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16;   // keys per lane
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc(ptile, 0, ES * KC * (kRT * kRS) * (int)sizeof(float), 0x00020000);
+    const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(logits, 0, T * E * (int)sizeof(float), 0x00020000);
+    for (int g0 = 0; g0 < Tt; g0 += kRGroup) {
+        const int nt = Tt - g0 < kRGroup ? Tt - g0 : kRGroup;
+        const int items = nt * E4;   // (token, 4 experts)
+        // logits and keys, two items per thread per round; each item's d/128
+        // partial sums are added in row-chunk order, all loads in flight
+        for (int it0 = 0; it0 < items; it0 += 512) {
+            const int nh = it0 + 256 < items ? 2 : 1;   // items per thread this round
+            int itm[2];
+            f32x4 s[2];
+            uint32_t off0[2];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int i = l + 64 * j;
-                const int sl = i / kc32, r = i - sl * kc32;
-                const int len = E - sl * kRS < kRS ? E - sl * kRS : kRS;   // experts in slice sl
-                ok[j] = i < total && r < len;
-                v[j] = load_dev_u64(&cb[ok[j] ? (size_t)sl * kRS + r : 0]);
+            for (int h = 0; h < 2; ++h) {
+                const int it = it0 + h * 256 + tid;
+                itm[h] = it;
+                const int itc = it < items ? it : 0;
+                const int t = itc / E4, e4 = itc - t * E4;
+                const int sl = e4 >> 3, q = e4 & 7;
+                // byte offset of (slice, chunk 0, token, quad); chunks 1 KiB apart
+                off0[h] = (uint32_t)((((sl * KC) * kRT + g0 + t) * kRS + q * 4) * 4);
+                s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            unsigned long long tha = 0ull;
-            int nh = 0;
+            int q0 = 0;
+            constexpr uint32_t kChunkBytes = kRT * kRS * 4;
+            if (nh == 2) {
+                // both items' loads in flight before the first add
+                for (; q0 + 16 <= KC; q0 += 16) {
+                    f32x4 pa[16], pb[16];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int i = l + 64 * j;
-                const int r = i % kc32;
-                v[j] = ok[j] ? v[j] : 0ull;
-                // bound a: the largest k-th entry of a list that holds k
-                if (ok[j] && r == k - 1) tha = max_u64(tha, v[j]);
-                nh += (ok[j] && r < m) ? 1 : 0;
-            }
+                    for (int j = 0; j < 16; ++j) pa[j] = load_dev_f4(prs, off0[0] + (uint32_t)(q0 + j) * kChunkBytes);
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) tha = max_u64(tha, __shfl_xor(tha, o, 64));
-            // bound b: the k-th largest list head (the first m entries of
-            // every list), when there are at least k heads
-            const int hi = wave_scan_dpp(nh);
-            const int hn = __shfl(hi, 63, 64);
-            {
-                int pos = hi - nh;
+                    for (int j = 0; j < 16; ++j) pb[j] = load_dev_f4(prs, off0[1] + (uint32_t)(q0 + j) * kChunkBytes);
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int i = l + 64 * j;
-                    const int r = i % kc32;
-                    if (v[j] != 0ull && r < m) H[pos++] = v[j];
+                    for (int j = 0; j < 16; ++j) s[0] += pa[j];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) s[1] += pb[j];
                 }
-            }
-            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            unsigned long long thb = 0ull;
-            if (hn >= k) {
-                const unsigned long long hk = l < hn ? H[l] : 0ull;
-                int hr = 0;
-#pragma unroll
-                for (int j = 0; j < 64; ++j) hr += (j < hn && H[j] > hk) ? 1 : 0;
-                const unsigned long long hit = __ballot(l < hn && hr == k - 1);
-                thb = hit ? __shfl(hk, __builtin_ctzll(hit), 64) : 0ull;
-            }
-            // survivors: entries >= theta (every key of the top k is one;
-            // k keys are at least either bound)
-            const unsigned long long th = max_u64(tha, thb);
-            int c = 0;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) c += (v[j] != 0ull && v[j] >= th) ? 1 : 0;
-            const int incl = wave_scan_dpp(c);
-            const int n = __shfl(incl, 63, 64);
-            {
-                int pos = incl - c;
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    if (v[j] != 0ull && v[j] >= th) S[pos++] = v[j];
-            }
-            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            // exact ranks among the survivors, 16 LDS reads in flight
-            for (int i = l; i < ((n + 63) & ~63); i += 64) {
-                const unsigned long long key = i < n ? S[i] : 0ull;
-                int rank = 0;
-                for (int j0 = 0; j0 < n; j0 += 16) {
-                    unsigned long long o[16];
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) o[j] = S[j0 + j < n ? j0 + j : 0];
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) rank += (j0 + j < n && o[j] > key) ? 1 : 0;
+                for (; q0 < KC; ++q0) {
+                    s[0] += load_dev_f4(prs, off0[0] + (uint32_t)q0 * kChunkBytes);
+                    s[1] += load_dev_f4(prs, off0[1] + (uint32_t)q0 * kChunkBytes);
                 }
-                if (i < n && rank < k) sel[rank] = key;
-            }
-            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            const unsigned long long key = l < k ? sel[l] : 0ull;
-            const float lv = key_value(key);
-            const float l0 = __shfl(lv, 0, 64);
-            const float ev = l < k ? expf(lv - l0) : 0.0f;
-            const float inv = 1.0f / wave_sum(ev);
-            if (l < k) {
-                const int e = key_expert(key);
-                ids[(size_t)(t0 + t) * k + l] = e;
-                w[(size_t)(t0 + t) * k + l] = ev * inv;
-                if (listing) sel_ids[t * k + l] = e;
-            }
-            // the next token of this wave reuses S, H and sel
-            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        }
-    } else {
-        // large k: per-token wave top-k on the logits (device-scope loads:
-        // other workgroups wrote them)
-        float *selv = reinterpret_cast<float *>(pool) + wv * 2048;
-        int *seli = reinterpret_cast<int *>(selv + 1024);
-        for (int t = wv; t < Tt; t += 4) {
-            const float *lg = logits + (size_t)(t0 + t) * E;
-            if (k <= kWaveTopkMaxK) {
-                // ordered keys in registers; picks into sel_ids for the listing
-                float *lgs = selv;   // this wave's scratch: the token's logits
-                for (int e = l; e < E; e += 64) lgs[e] = load_dev(&lg[e]);
-                __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                wave_topk_ord_any(lgs, E, k, ids + (size_t)(t0 + t) * k, w + (size_t)(t0 + t) * k,
-                                  listing ? sel_ids + t * k : nullptr);
             } else {
-                wave_topk_any<true>(lg, E, k, ids + (size_t)(t0 + t) * k, w + (size_t)(t0 + t) * k, selv, seli);
+                for (; q0 + 16 <= KC; q0 += 16) {
+                    f32x4 pa[16];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) pa[j] = load_dev_f4(prs, off0[0] + (uint32_t)(q0 + j) * kChunkBytes);
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) s[0] += pa[j];
+                }
+                for (; q0 < KC; ++q0) s[0] += load_dev_f4(prs, off0[0] + (uint32_t)q0 * kChunkBytes);
             }
-            // the next token of this wave reuses the scratch
-            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (itm[h] < items) {
+                    const int t = itm[h] / E4, e4 = itm[h] - t * E4;
+                    unsigned long long kq[4];
+                    float *const lrow = logits + (size_t)(t0 + g0 + t) * E;
+                    if constexpr (VEC) {
+                        // one 16-byte device-coherent store (the large-k
+                        // selection below re-reads the logits)
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[h]), lrs,
+                                                               (int)(((size_t)(lrow - logits) + 4 * e4) * 4), 0, 16);
+                    }
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int e = 4 * e4 + c;
+                        kq[c] = 0ull;
+                        if (e < E) {
+                            if constexpr (!VEC) store_dev(&lrow[e], s[h][c]);
+                            kq[c] = route_key(s[h][c], e);
+                        }
+                    }
+                    u32x4 lo, hi;
+                    lo = u32x4{(uint32_t)kq[0], (uint32_t)(kq[0] >> 32), (uint32_t)kq[1], (uint32_t)(kq[1] >> 32)};
+                    hi = u32x4{(uint32_t)kq[2], (uint32_t)(kq[2] >> 32), (uint32_t)kq[3], (uint32_t)(kq[3] >> 32)};
+                    *reinterpret_cast<u32x4 *>(&keys[t][4 * e4]) = lo;
+                    *reinterpret_cast<u32x4 *>(&keys[t][4 * e4 + 2]) = hi;
+                }
+            }
         }
+        // zero keys from 4 ceil(E/4) to the row's 64 Pk
+        const int pad0 = 4 * E4, padn = 64 * Pk - pad0;
+        for (int i = tid; i < nt * padn; i += 256) keys[i / padn][pad0 + i % padn] = 0ull;
+        if (k > kWaveTopkMaxK) __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // logits re-read below
+        __syncthreads();
+        if (wv < nt) {
+            const int t = g0 + wv;
+            int32_t *const id_t = ids + (size_t)(t0 + t) * k;
+            float *const w_t = w + (size_t)(t0 + t) * k;
+            if (k <= kWaveTopkMaxK) {
+                unsigned long long *M = wscr[wv], *sel = wscr[wv] + 64;
+                int32_t *il = listing ? sel_ids + t * k : nullptr;
+                switch (Pk) {
+                case 1: select_token<1>(keys[wv], k, M, sel, id_t, w_t, il); break;
+                case 2: select_token<2>(keys[wv], k, M, sel, id_t, w_t, il); break;
+                case 4: select_token<4>(keys[wv], k, M, sel, id_t, w_t, il); break;
+                case 8: select_token<8>(keys[wv], k, M, sel, id_t, w_t, il); break;
+                default: select_token<16>(keys[wv], k, M, sel, id_t, w_t, il); break;
+                }
+            } else {
+                // large k: the serial wave top-k on the logits just written
+                // (device-scope loads), scratch in this wave's key row
+                float *selv = reinterpret_cast<float *>(keys[wv]);
+                int *seli = reinterpret_cast<int *>(selv + 1024);
+                wave_topk_any<true>(logits + (size_t)(t0 + t) * E, E, k, id_t, w_t, selv, seli);
+            }
+        }
+        __syncthreads();   // the key rows serve the next group
     }
-    if (!listing) return;
-    __syncthreads();
-    if (Tt == 1)
-        list_pairs_one(sel_ids, E, k, tail_from, offsets, sorted_pair, pair_pos);
-    else
-        list_pairs(sel_ids, Tt, E, k, tail_from, emask, eoff, wtot, offsets, sorted_pair, pair_pos);
+    if (listing) {
+        if (Tt == 1)
+            list_pairs_one(sel_ids, E, k, tail_from, offsets, sorted_pair, pair_pos);
+        else
+            list_pairs(sel_ids, Tt, E, k, tail_from, emask, eoff, wtot, offsets, sorted_pair, pair_pos);
+    }
+    // zero the tile's counters for the next call (every arrival is in)
+    if (tid < ES) store_dev_int(slice_cnt + (size_t)(tt * kRSMax + tid) * kCntLine, 0);
+    if (tid == 0) store_dev_int(tcnt, 0);
 }
 
-// workspace after the header: the partial sums [tiles][ES][d/128][kRT][kRS],
-// then the candidate lists [tiles][kRT][kRSMax][kRS]
-static size_t route_partial_bytes(int d, int E, int T) {
-    const size_t tiles = (size_t)(T + kRT - 1) / kRT, ES = (size_t)(E + kRS - 1) / kRS;
-    return tiles * ES * (size_t)(d / kRK) * kRT * kRS * sizeof(float);
-}
-
+// workspace after the header: the partial sums [tiles][ES][d/128][kRT][kRS]
 size_t route_ws_bytes(int d, int E, int T) {
     if (T > kRouteSmallTMax) return router_gemm_ws_bytes(d, E);
-    const size_t tiles = (size_t)(T + kRT - 1) / kRT;
-    return route_partial_bytes(d, E, T) + tiles * kRT * kRSMax * kRS * sizeof(unsigned long long);
+    const size_t tiles = (size_t)(T + kRT - 1) / kRT, ES = (size_t)(E + kRS - 1) / kRS;
+    return tiles * ES * (size_t)(d / kRK) * kRT * kRS * sizeof(float);
 }
 
 template <bool VEC>
 static void launch_route_small_v(dim3 grid, int TT, hipStream_t s, const uint16_t *x, const float *wr,
                                  const float *bias, float *logits, int T, int d, int E, int k, int32_t *ids, float *w,
-                                 int32_t *tile_cnt, int32_t *slice_cnt, float *partial, unsigned long long *cand,
-                                 int32_t *offsets, int32_t *sorted_pair, int32_t *pair_pos, int tail_from) {
+                                 int32_t *tile_cnt, int32_t *slice_cnt, float *partial, int32_t *offsets,
+                                 int32_t *sorted_pair, int32_t *pair_pos, int tail_from) {
 #define MOE_ROUTE_LAUNCH(TTV)                                                                                        \
     hipLaunchKernelGGL((route_small_kernel<VEC, TTV>), grid, dim3(256), 0, s, x, wr, bias, logits, T, d, E, k, ids, \
-                       w, tile_cnt, slice_cnt, partial, cand, offsets, sorted_pair, pair_pos, tail_from)
+                       w, tile_cnt, slice_cnt, partial, offsets, sorted_pair, pair_pos, tail_from)
     if (TT == 1)
         MOE_ROUTE_LAUNCH(1);
     else if (TT == 2)
@@ -752,8 +829,6 @@ hipError_t launch_route_small(const uint16_t *x, const float *wr, const float *b
     int32_t *tile_cnt = reinterpret_cast<int32_t *>(base);
     int32_t *slice_cnt = reinterpret_cast<int32_t *>(base + kRouteSliceCnt);
     float *partial = reinterpret_cast<float *>(base + kWsHeader);
-    unsigned long long *cand =
-        reinterpret_cast<unsigned long long *>(base + kWsHeader + route_partial_bytes(d, E, T));
     const int ES = (E + kRS - 1) / kRS, KC = d / kRK;
     const dim3 grid(ES * KC, (T + kRT - 1) / kRT);
     // token slots: the batch itself up to one tile, else full tiles
@@ -761,10 +836,10 @@ hipError_t launch_route_small(const uint16_t *x, const float *wr, const float *b
     const int tf = tail_from < 0 ? k : tail_from;
     if (E % 4 == 0)
         launch_route_small_v<true>(grid, TT, s, x, wr, bias, logits, T, d, E, k, ids, w, tile_cnt, slice_cnt, partial,
-                                   cand, offsets, sorted_pair, pair_pos, tf);
+                                   offsets, sorted_pair, pair_pos, tf);
     else
         launch_route_small_v<false>(grid, TT, s, x, wr, bias, logits, T, d, E, k, ids, w, tile_cnt, slice_cnt,
-                                    partial, cand, offsets, sorted_pair, pair_pos, tf);
+                                    partial, offsets, sorted_pair, pair_pos, tf);
     return hipGetLastError();
 }
 
