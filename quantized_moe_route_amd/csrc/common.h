@@ -240,27 +240,24 @@ __device__ inline bool find_group(const int32_t *__restrict__ offsets, int E, in
     const int target = slot - 1;  // index among non-empty experts
     const int l = __lane_id();
     const int per = (E + 63) / 64;  // <= 16
-    // One round trip: lane l loads the start offsets of experts l + 64 i
-    // (unconditional loads at clamped indices: a predicated load would be
-    // waited for inside its own branch); each end offset is the next
-    // expert's start, taken from the neighbouring lane.
-    int lo[16];
+    // One round trip: lane l loads the start and end offsets of experts
+    // l + 64 i (unconditional loads at clamped indices: a predicated load
+    // would be waited for inside its own branch; past E both read offsets[E],
+    // an empty range).  Plain loads: every workgroup of a launch reads the
+    // same offsets, so all but the first on each XCD hit its L2.
+    int lo[16], hi[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int e = l + 64 * i;
         lo[i] = offsets[e < E ? e : E];
+        hi[i] = offsets[e < E ? e + 1 : E];
     }
-    const int last = offsets[E < 1024 ? E : 1024];
     int cum = 0, sel_row = -1, sel_n = 0;
     unsigned long long sel_m = 0ull;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         if (i < per) {
-            const int nxt = i + 1 < 16 ? __shfl(lo[i + 1], 0) : last;
-            int hi = __shfl(lo[i], (l + 1) & 63);
-            hi = l == 63 ? nxt : hi;
-            const bool valid = l + 64 * i < E;
-            const unsigned long long m = __ballot(valid && hi > lo[i]);
+            const unsigned long long m = __ballot(hi[i] > lo[i]);
             const int c = __popcll(m);
             const bool hit = sel_row < 0 && target < cum + c;
             sel_m = hit ? m : sel_m;
@@ -271,18 +268,17 @@ __device__ inline bool find_group(const int32_t *__restrict__ offsets, int E, in
     }
     if (sel_row < 0) return false;
     const int bit = nth_set_bit(sel_m, sel_n);
-    const int found = 64 * sel_row + bit;
-    // start and end of the found expert: lane bit (and its successor) hold them
-    int a = lo[0], b = lo[0];
+    // start and end of the found expert: lane `bit` of row sel_row holds them
+    int a = lo[0], b = hi[0];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 1; i < 16; ++i)
         if (i == sel_row) {
             a = lo[i];
-            b = i + 1 < 16 ? lo[i + 1] : last;
+            b = hi[i];
         }
-    const int row0 = __shfl(a, bit);
-    const int end = bit < 63 ? __shfl(a, bit + 1) : __shfl(b, 0);
-    g.expert = found;
+    const int row0 = __builtin_amdgcn_readlane(a, bit);
+    const int end = __builtin_amdgcn_readlane(b, bit);
+    g.expert = 64 * sel_row + bit;
     g.row0 = row0;
     g.nrows = end - row0;
     g.hrow0 = row0;

@@ -137,6 +137,8 @@ __device__ __forceinline__ void gateup_block(const GateUpUnit<FMT, MT> &U, f32x4
 #define MOE_DECODE_BATCH 4
 #endif
 constexpr int kBatch = MOE_DECODE_BATCH;   // units prefetched per wave per batch
+// gate/up: units per wave per batch, NB = 16 / NW (K = d_model = 2048 is 16
+// units: one batch per wave)
 // down: K = d_ff = 768 is 6 units, 3 per wave of two; a batch of 4 held a
 // fourth, unused unit's registers (166 -> 128 VGPRs at 16 tokens)
 constexpr int kDownBatch = 3;
@@ -170,7 +172,7 @@ __device__ __forceinline__ uint32_t max_mag_bf16x8(const u32x4 &v, uint32_t mx) 
     return mx;
 }
 
-template <int FMT, int IMAX, int NW, bool XL, int TPW>
+template <int FMT, int IMAX, int NW, bool XL, int TPW, int NB = 16 / NW>
 __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &up, const QMatDev &sgate,
                                             const QMatDev &sup, const uint16_t *__restrict__ x, int T, int k, int d,
                                             int f, const int32_t *__restrict__ sorted_pair, const Group &grp,
@@ -212,31 +214,18 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
     const uint16_t *xrow[1] = {x + (size_t)xr * d};
     const int cpr = d / 8;                // 16-byte chunks per x row
     uint32_t xmax = 0u;                   // largest |x| bits of this lane's row over its K slices
-    GateUpUnit<FMT, 1> U[kBatch];
+    GateUpUnit<FMT, 1> U[NB];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
+    for (int b = 0; b < NB; ++b) {
         const int u = wv + NW * b;
         if (u < KC) gateup_load_w(U[b], Wg, Wu, ubase + u, lane, rr);
     }
-    if constexpr (XL) {
-        // x [T][d] into LDS once per workgroup by global-to-LDS copies (no
-        // registers held): chunk c of row r goes to r * cpr + (c ^ (r & 7)),
-        // so the T rows read at one column fall in different banks
-        const int nch = T * cpr;
-        for (int q = wall; q * 64 < nch; q += NW * TPW) {
-            const int L = q * 64 + lane;
-            if (L < nch) {
-                const int r = L / cpr, cs = L - r * cpr;
-                copy_to_lds16(x + (size_t)r * d + (size_t)(cs ^ (r & 7)) * 8, xs + (size_t)q * 512);
-            }
-        }
-        wait_vm<0>();   // the copies and the first weights
-        __syncthreads();
-    }
-    for (int u0 = wv; u0 < KC; u0 += NW * kBatch) {
+    // XL: x was staged and waited for by every wave before the barrier that
+    // published the group
+    for (int u0 = wv; u0 < KC; u0 += NW * NB) {
         if (u0 != wv) {
 #pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
+            for (int b = 0; b < NB; ++b) {
                 const int u = u0 + NW * b;
                 if (u < KC) gateup_load_w(U[b], Wg, Wu, ubase + u, lane, rr);
             }
@@ -244,13 +233,13 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
         __asm__ volatile("" ::: "memory");
         if constexpr (!XL) {
 #pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
+            for (int b = 0; b < NB; ++b) {
                 const int u = u0 + NW * b;
                 if (u < KC) gateup_load_x(U[b], u, gq, xrow);
             }
         }
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
+        for (int b = 0; b < NB; ++b) {
             if (u0 + NW * b < KC) {
                 if constexpr (XL) {
                     const int u = u0 + NW * b;
@@ -508,6 +497,9 @@ __device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev 
         }
 }
 
+constexpr int kTileMaxT = 4;    // down_tile_kernel: T <= 4, k <= 16 (pairs and merge in LDS)
+constexpr int kTileMaxK = 16;
+
 // The fused combine (moe_combine's sum for one 16-column output tile).  Every
 // workgroup of the tile (one per group slot, empty slots included) arrives
 // after its y stores have completed at device scope; the last to arrive
@@ -569,15 +561,48 @@ __global__ __launch_bounds__(64 * NW * TPW) void gateup_small_kernel(
     __shared__ float red[NW * TPW][2][IMAX][64];
     __shared__ uint32_t redx[NW * TPW][16];
     extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];   // XL: x, T * d halves
-    Group grp;
-    const bool found = find_group(offsets, E, T, T * k, slot0 + (int)blockIdx.y, grp);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        const Group none{0, 0, 0, 0};
-        *reinterpret_cast<u32x4 *>(&table[blockIdx.y]) = __builtin_bit_cast(u32x4, found ? grp : none);
+    if constexpr (XL) {
+        // x [T][d] into LDS once per workgroup by global-to-LDS copies (no
+        // registers held), issued first: x does not depend on the group.
+        // Chunk c of row r goes to r * cpr + (c ^ (r & 7)), so the T rows
+        // read at one column fall in different banks.
+        const int cpr = d / 8, nch = T * cpr, lane = __lane_id();
+        const int wall = wave_uniform(threadIdx.x >> 6);
+        for (int q = wall; q * 64 < nch; q += NW * TPW) {
+            const int L = q * 64 + lane;
+            if (L < nch) {
+                const int r = L / cpr, cs = L - r * cpr;
+                copy_to_lds16(x + (size_t)r * d + (size_t)(cs ^ (r & 7)) * 8, xs_dyn + (size_t)q * 512);
+            }
+        }
     }
-    if (!found) return;
+    // one wave looks the group up; the others take it from LDS
+    __shared__ Group grp_s;
+    __shared__ int found_s;
+    if (threadIdx.x < 64) {
+        Group g;
+        const bool f0 = find_group(offsets, E, T, T * k, slot0 + (int)blockIdx.y, g);
+        if (threadIdx.x == 0) {
+            grp_s = g;
+            found_s = f0;
+        }
+    }
+    // meet: every wave's x copies are in LDS and the group is known to all
+    // (nothing else is in flight yet, so the full drain costs nothing)
+    __syncthreads();
+    const Group grp = grp_s;
+    const bool found = found_s != 0;
+    // the first tile of each slot records the slot's group for the down
+    // kernel, after its own loads (a store issued before them would delay
+    // them: the memory counter retires in order)
+    const bool rec = blockIdx.x == 0 && threadIdx.x == 0;
+    if (!found) {
+        if (rec) *reinterpret_cast<u32x4 *>(&table[blockIdx.y]) = u32x4{0u, 0u, 0u, 0u};
+        return;
+    }
     gateup_task<FMT, IMAX, NW, XL, TPW>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp,
                                         (int)blockIdx.x * TPW, red, redx, h_hi, h_lo, hx, xs_dyn);
+    if (rec) *reinterpret_cast<u32x4 *>(&table[blockIdx.y]) = __builtin_bit_cast(u32x4, grp);
 }
 
 // grid: (d_model/16 row tiles, group slots); NW waves split K = d_ff.  FUSE:
@@ -598,6 +623,153 @@ __global__ __launch_bounds__(64 * NW) void down_small_kernel(
                                                y_pairs, y_shared, xs_dyn);
     }
     if constexpr (FUSE) combine_tile(cb, y_pairs, y_shared, d, blockIdx.x, gridDim.y);
+}
+
+
+// Down projection for batches of at most 4 tokens and d_ff <= 768: one
+// workgroup per 16-row output tile and chunk of up to 16 group slots, one
+// wave per slot over all of K = d_ff, so no partial sums cross waves.  Each
+// wave copies its group's h rows (hi, then lo) into an LDS region of its own
+// and waits for nothing but its own copies.  FUSE with a single chunk (T = 1
+// at top-10: 11 slots) also merges each token's outputs for the tile in the
+// workgroup -- shared term first, then the pairs in j order, one fma each,
+// moe_combine's order -- with no counter and no re-read; with several
+// chunks each arrives on the tile's counter after its y stores and the last
+// one merges from memory (combine_tile).
+constexpr int kTileUnits = 6;   // d_ff / 128 <= 6
+template <int FMT, int RMAX, bool FUSE>
+__global__ __launch_bounds__(64 * 16) void down_tile_kernel(
+    QMatDev down, QMatDev sdown, const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
+    const int32_t *__restrict__ hx, int d, int f, const Group *__restrict__ table, int slots, int nchunks,
+    float *__restrict__ y_pairs, float *__restrict__ y_shared, CombineArgs cb) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t hs_dyn[];   // per wave: 2 RMAX rows of f halves
+    __shared__ float ylds[(kTileMaxT * kTileMaxK + kTileMaxT) * 16];   // y by row (pairs, then shared)
+    __shared__ int32_t pp_s[kTileMaxT * kTileMaxK];
+    __shared__ float w_s[kTileMaxT * kTileMaxK];
+    const int lane = __lane_id(), gq = lane >> 4, rr = lane & 15;
+    const int wv = wave_uniform(threadIdx.x >> 6), CH = blockDim.x >> 6;
+    const int ot = blockIdx.x, slot = blockIdx.y * CH + wv;
+    const int T = cb.T, k = cb.k, P = T * k;
+    const bool merge_here = FUSE && nchunks == 1;
+    if (merge_here) {
+        // the routing of the batch, for the merge (written by earlier kernels)
+        for (int i = threadIdx.x; i < P; i += blockDim.x) {
+            pp_s[i] = cb.pair_pos[i];
+            w_s[i] = cb.w[i];
+        }
+    }
+    Group grp{0, 0, 0, 0};
+    if (slot < slots) grp = table[slot];
+    const int n = grp.nrows;
+    float yv[RMAX];
+    if (n > 0) {
+        const int KC = f / 128, cpr = f / 8;
+        uint16_t *hs = hs_dyn + (size_t)wv * (2 * RMAX * f);
+        // 1. the group's h rows, loaded into registers first and written to
+        //    this wave's LDS once they land (register loads, not global-to-LDS
+        //    copies: the compiler then waits for exactly these and leaves the
+        //    weights in flight; every tile's workgroup reads the same rows, so
+        //    they are plain loads that stay in L2).  Stored row S < n is h_hi row S, S >= n h_lo
+        //    row S - n; chunk c of row S at S * cpr + (c ^ (S & 7)) (the rows
+        //    read at one column fall in different banks).
+        constexpr int QMAX = 3 * RMAX;   // 16-byte chunks per lane: 2 RMAX rows of <= 96
+        const int nch = 2 * n * cpr;
+        u32x4 hv[QMAX];
+#pragma unroll
+        for (int q = 0; q < QMAX; ++q) {
+            const int L = q * 64 + lane < nch ? q * 64 + lane : 0;   // unconditional, clamped
+            const int S = L / cpr, cs = L - S * cpr;
+            const int hr = S < n ? S : S - n;
+            const uint16_t *src = (S < n ? h_hi : h_lo) + (size_t)(grp.hrow0 + hr) * f;
+            hv[q] = *reinterpret_cast<const u32x4 *>(src + (size_t)(cs ^ (S & 7)) * 8);
+        }
+        // 2. the rows' exponents (y = acc 2^2a)
+        int ya[RMAX];
+#pragma unroll
+        for (int i = 0; i < RMAX; ++i) {
+            const int r = 4 * gq + i < n ? 4 * gq + i : n - 1;
+            ya[i] = 2 * hx[grp.hrow0 + r];
+        }
+        // 3. all of the wave's weights (unconditional, clamped past KC)
+        const bool shared = grp.expert < 0;
+        const QMatDev W = shared ? sdown : down;
+        const size_t ubase = ((size_t)(shared ? 0 : grp.expert) * (d / 16) + ot) * KC;
+        DownUnit<FMT, 1> U[kTileUnits];
+#pragma unroll
+        for (int b = 0; b < kTileUnits; ++b) {
+            const size_t unit = ubase + (b < KC ? b : KC - 1);
+            auto ld = [](const auto *p) { return __builtin_nontemporal_load(p); };
+            U[b].lw = ld(reinterpret_cast<const u32x2 *>(W.lo + unit * 512 + lane * 8));
+            if constexpr (FMT == MOE_FMT_Q3_B32) U[b].hw = ld(reinterpret_cast<const uint32_t *>(W.hi + unit * 256 + lane * 4));
+            U[b].sw = ld(reinterpret_cast<const u32x2 *>(W.scale + unit * 64 + rr * 4));
+            if constexpr (FMT == MOE_FMT_Q2_B32) U[b].mw = ld(reinterpret_cast<const u32x2 *>(W.min + unit * 64 + rr * 4));
+            __asm__ volatile("" ::: "memory");   // issue in unit order: unit 0 lands first
+        }
+#pragma unroll
+        for (int q = 0; q < QMAX; ++q)
+            if (q * 64 + lane < nch) *reinterpret_cast<u32x4 *>(hs + (size_t)(q * 64 + lane) * 8) = hv[q];
+        const int srow = (rr < 8 ? 0 : n) + ((rr & 7) < n ? (rr & 7) : n - 1);
+        f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int b = 0; b < kTileUnits; ++b) {
+            if (b < KC) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = b * 16 + j * 4 + gq;
+                    U[b].A[0][j] = *reinterpret_cast<const u32x4 *>(hs + ((size_t)srow * cpr + (c ^ (srow & 7))) * 8);
+                }
+                down_block<FMT, 1, RMAX, 0>(U[b], acc);
+                down_block<FMT, 1, RMAX, 1>(U[b], acc);
+                down_block<FMT, 1, RMAX, 2>(U[b], acc);
+                down_block<FMT, 1, RMAX, 3>(U[b], acc);
+            }
+        }
+        // hi rows (lanes gq 0, 1) + lo rows (gq 2, 3)
+#pragma unroll
+        for (int i = 0; i < RMAX; ++i) {
+            yv[i] = ldexpf(acc[0][i] + __shfl_xor(acc[0][i], 32, 64), ya[i]);
+            const int r = 4 * gq + i;
+            if (merge_here && gq < 2 && r < n) ylds[(shared ? P + r : grp.row0 + r) * 16 + rr] = yv[i];
+        }
+    }
+    // y to memory: after the merge's barrier when merging here (a barrier
+    // waits for this workgroup's outstanding stores to complete)
+    auto store_y = [&](bool dev) {
+        if (n == 0) return;
+        const int o = ot * 16 + rr;
+#pragma unroll
+        for (int i = 0; i < RMAX; ++i) {
+            const int r = 4 * gq + i;
+            if (gq >= 2 || r >= n) continue;
+            float *dst = grp.expert < 0 ? y_shared + (size_t)r * d + o : y_pairs + (size_t)(grp.row0 + r) * d + o;
+            if (dev)
+                store_dev(dst, yv[i]);   // read by another workgroup of this launch
+            else
+                *dst = yv[i];
+        }
+    };
+    if constexpr (!FUSE) {
+        store_y(false);
+    } else {
+        if (!merge_here) {
+            store_y(true);
+            combine_tile(cb, y_pairs, y_shared, d, ot, nchunks);
+            return;
+        }
+        // only LDS traffic to wait for: no global store is outstanding
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        wg_barrier();
+        for (int i = threadIdx.x; i < T * 16; i += blockDim.x) {
+            const int t = i >> 4, c = i & 15;
+            float acc = ylds[(P + t) * 16 + c];
+            for (int j = 0; j < k; ++j) {
+                const int p = pp_s[t * k + j];
+                if (p >= 0) acc = fmaf(w_s[t * k + j], ylds[p * 16 + c], acc);
+            }
+            cb.out[(size_t)t * d + ot * 16 + c] = acc;
+        }
+        store_y(false);
+    }
 }
 
 static QMatDev qm(const moe_qmat &m) { return QMatDev{m.lo, m.hi, m.scale, m.min}; }
@@ -624,12 +796,14 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
     const int slots = ((parts & kFfnShared) ? 1 : 0) + ((parts & kFfnRouted) ? (E < P ? E : P) : 0);
     if (slots == 0) return;
 #ifndef MOE_GU_WAVES
-#define MOE_GU_WAVES 4
+#define MOE_GU_WAVES 8
 #endif
 #ifndef MOE_DN_WAVES
 #define MOE_DN_WAVES 2
 #endif
-    constexpr int NWG = MOE_GU_WAVES, NWD = MOE_DN_WAVES;   // waves per workgroup (split K)
+    // waves per workgroup (split K): eight for one or two tokens; from three
+    // tokens on there are enough groups that four keep more workgroups resident
+    constexpr int NWG = IMAX <= 2 ? MOE_GU_WAVES : 4, NWD = MOE_DN_WAVES;
     // up to eight tokens: x staged in LDS (32 KiB at most), which frees the
     // registers that held it, so more waves keep weight loads in flight, and
     // reads each x byte from L2 once per workgroup instead of once per wave
@@ -642,13 +816,35 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
     else if (IMAX >= 2 && T <= 16 && xbytes <= 2 * kXsMaxBytes && (f / 16) % 2 == 0)
         // 9 to 16 tokens: x takes up to 64 KiB, so one workgroup of eight
         // waves serves two column tiles with one copy
-        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, IMAX >= 2, IMAX >= 2 ? 2 : 1>), dim3(f / 32, slots),
-                           dim3(2 * 64 * NWG), (unsigned)xbytes, s, qm(L.gate), qm(L.up), qm(L.sh_gate),
+        // (four waves per tile: the LDS of x and of eight waves' sums would
+        // pass 64 KiB)
+        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, 4, IMAX >= 2, IMAX >= 2 ? 2 : 1>), dim3(f / 32, slots),
+                           dim3(2 * 64 * 4), (unsigned)xbytes, s, qm(L.gate), qm(L.up), qm(L.sh_gate),
                            qm(L.sh_up), x, T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, hx, table, slot0);
     else
         hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, false, 1>), dim3(f / 16, slots),
                            dim3(64 * NWG), 0, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up), x,
                            T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, hx, table, slot0);
+    // one token (and k <= 16, d_ff <= 768): all groups of an output tile in
+    // one workgroup, one wave per group (measured at T = 4 with 41 groups in
+    // chunks of 4 it lost to one workgroup per group and tile)
+    if (MTD == 1 && T == 1 && k <= kTileMaxK && f <= 128 * kTileUnits && f % 128 == 0) {
+        constexpr int RMAX = IMAX;
+        int CH = slots < 16 ? slots : 16;
+        const int lds_ch = 49152 / (2 * RMAX * f * 2);   // waves whose h rows fit 48 KiB
+        CH = CH < lds_ch ? CH : lds_ch;
+        const int nchunks = (slots + CH - 1) / CH;
+        const unsigned lds = (unsigned)(CH * 2 * RMAX * f * 2);
+        if (cb.out)
+            hipLaunchKernelGGL((down_tile_kernel<FMT, RMAX, true>), dim3(d / 16, nchunks), dim3(64 * CH), lds, s,
+                               qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f, table, slots, nchunks, y_pairs,
+                               y_shared, cb);
+        else
+            hipLaunchKernelGGL((down_tile_kernel<FMT, RMAX, false>), dim3(d / 16, nchunks), dim3(64 * CH), lds, s,
+                               qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f, table, slots, nchunks, y_pairs,
+                               y_shared, cb);
+        return;
+    }
     // up to four tokens: the group's h rows (at most T of hi and of lo)
     // staged in LDS (measured: T = 1 +0.7%, T = 2 +9%, T = 4 +3% on Q2,
     // neutral on Q3; at T = 8 it lost 1.5%)
