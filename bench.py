@@ -59,13 +59,16 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix
 METRIC = "MoE-layer tokens/s (decode T=1/4, prefill 8192); % HBM BW or % MFMA peak"
 
 # HBM bytes per expert-FFN call of the step (moe_expert_ffn_combine for
-# workload 1, moe_expert_ffn for workload 3), from two rocprofv3 --pmc runs
-# (FETCH_SIZE, WRITE_SIZE; each scaled by what it reads for a plain 1 GiB
-# copy), keyed by workload.  Each figure is tied to a hash of the kernel
-# sources it was taken on and is reported as null once those sources change.
+# workloads 1 and 2, moe_expert_ffn for workloads 3 and 4), from two rocprofv3
+# --pmc runs (FETCH_SIZE, WRITE_SIZE; each scaled by what it reads for a plain
+# 1 GiB copy: 2.0 and 1.0), keyed by workload.  Each figure is tied to a hash of
+# the kernel sources it was taken on and is reported as null once those
+# sources change.
 TRAFFIC = {
-    1: (("common.h", "ffn_small.hip"), "0b364f5fdd57a6c7", 26941583),
-    3: (("common.h", "ffn_prefill.hip"), "ce333fe783ae8f6a", 2532121274),
+    1: (("common.h", "ffn_small.hip"), "6c8ab70c15c43e43", 20203520),
+    2: (("common.h", "ffn_small.hip"), "6c8ab70c15c43e43", 49151385),
+    3: (("common.h", "ffn_prefill.hip"), "b267e8c39e1bdf1e", 2569451315),
+    4: (("common.h", "ffn_prefill.hip"), "b267e8c39e1bdf1e", 2187057459),
 }
 
 
