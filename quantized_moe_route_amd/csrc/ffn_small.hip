@@ -56,23 +56,55 @@ struct GateUpUnit {
     u32x4 A[MT][4];
 };
 
+// The codes of one unit of gate and up (the block scales and minimums come
+// through piece_gather below).
 template <int FMT, int MT>
-__device__ __forceinline__ void gateup_load_w(GateUpUnit<FMT, MT> &U, const QMatDev &Wg,
-                                              const QMatDev &Wu, size_t unit, int lane, int rr) {
-    // each weight is read once per call: nontemporal
-    auto ld = [](const auto *p) { return __builtin_nontemporal_load(p); };
+__device__ __forceinline__ void gateup_load_codes(GateUpUnit<FMT, MT> &U, const QMatDev &Wg, const QMatDev &Wu,
+                                                  size_t unit, int lane) {
+    auto ld = [](const auto *p) { return __builtin_nontemporal_load(p); };   // read once
     U.lg = ld(reinterpret_cast<const u32x2 *>(Wg.lo + unit * 512 + lane * 8));
     U.lu = ld(reinterpret_cast<const u32x2 *>(Wu.lo + unit * 512 + lane * 8));
     if constexpr (FMT == MOE_FMT_Q3_B32) {
         U.hg = ld(reinterpret_cast<const uint32_t *>(Wg.hi + unit * 256 + lane * 4));
         U.hu = ld(reinterpret_cast<const uint32_t *>(Wu.hi + unit * 256 + lane * 4));
     }
-    U.sg = ld(reinterpret_cast<const u32x2 *>(Wg.scale + unit * 64 + rr * 4));
-    U.su = ld(reinterpret_cast<const u32x2 *>(Wu.scale + unit * 64 + rr * 4));
-    if constexpr (FMT == MOE_FMT_Q2_B32) {
-        U.mg = ld(reinterpret_cast<const u32x2 *>(Wg.min + unit * 64 + rr * 4));
-        U.mu = ld(reinterpret_cast<const u32x2 *>(Wu.min + unit * 64 + rr * 4));
+}
+
+// Block scales (and Q2 minimums) of a wave's batch of units: P pieces of 128
+// bytes (a unit's 16 rows x 4 blocks of fp16), gathered with one 16-byte
+// load per lane per 64 chunks into the wave's own LDS region, from where each
+// lane reads its row's 8 bytes.  (8-byte loads by every lane, four lanes to
+// an address, cost several times the code loads' issue time.)  The loads are
+// unconditional (lanes past the last chunk repeat it).
+template <int P>
+struct PieceGather {
+    static constexpr int N = (8 * P + 63) / 64;
+    u32x4 v[N];
+    // piece_addr(p): the global address of piece p, as an integer (a select
+    // among pointers can become a lookup table in scratch memory)
+    template <typename F>
+    __device__ __forceinline__ void issue(F piece_addr) {
+        typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+        const int lane = __lane_id();
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int c = i * 64 + lane < 8 * P ? i * 64 + lane : 8 * P - 1;
+            const uint64_t a = piece_addr(c >> 3) + (uint64_t)(c & 7) * 16;
+            v[i] = __builtin_nontemporal_load(reinterpret_cast<global_u32x4 *>(a));
+        }
     }
+    // into a region of N x 64 chunks (lanes past the last chunk store their
+    // repeat into the spare slots: no branch, so the compiler's waits stay
+    // exact)
+    __device__ __forceinline__ void store(u32x4 *lds) const {
+        const int lane = __lane_id();
+#pragma unroll
+        for (int i = 0; i < N; ++i) lds[i * 64 + lane] = v[i];
+    }
+};
+// row rr of piece p in a gathered region
+__device__ __forceinline__ u32x2 piece_row(const u32x4 *lds, int p, int rr) {
+    return reinterpret_cast<const u32x2 *>(lds)[p * 16 + rr];
 }
 
 template <int FMT, int MT>
@@ -178,7 +210,7 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
                                             int f, const int32_t *__restrict__ sorted_pair, const Group &grp,
                                             int nt, float (*red)[2][IMAX][64], uint32_t (*redx)[16],
                                             uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo,
-                                            int32_t *__restrict__ hx, uint16_t *xs) {
+                                            int32_t *__restrict__ hx, uint16_t *xs, u32x4 *pieces) {
     static_assert(NW > 1, "token rows: K split over waves");
     static_assert(TPW == 1 || XL, "several tiles per workgroup share the staged x");
     const int lane = __lane_id();
@@ -215,22 +247,59 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
     const int cpr = d / 8;                // 16-byte chunks per x row
     uint32_t xmax = 0u;                   // largest |x| bits of this lane's row over its K slices
     GateUpUnit<FMT, 1> U[NB];
+    // scale pieces of a batch: unit b, matrix m (gate, up), plane (scale, Q2 min)
+    constexpr int NPL = FMT == MOE_FMT_Q2_B32 ? 2 : 1;
+    constexpr int NP = NB * 2 * NPL;
+    u32x4 *const pw = pieces + (size_t)wall * 64 * PieceGather<NP>::N;   // this wave's region
+    // plane base addresses as integers, chosen by selects
+    const uint64_t gs = (uint64_t)Wg.scale, gm = (uint64_t)Wg.min, us = (uint64_t)Wu.scale, um = (uint64_t)Wu.min;
+    auto gather = [=](int u0) {
+        PieceGather<NP> g;
+        g.issue([=](int p) {
+            const int b = p / (2 * NPL), m = (p / NPL) & 1, pl = p % NPL;
+            const int u = u0 + NW * b < KC ? u0 + NW * b : KC - 1;
+            // three selects; the empty asm keeps them selects (folded, they
+            // become a table in scratch memory)
+            uint64_t base = m == 0 && pl == 1 ? gm : gs;
+            __asm__ volatile("" : "+v"(base));
+            base = m == 1 && pl == 0 ? us : base;
+            __asm__ volatile("" : "+v"(base));
+            base = m == 1 && pl == 1 ? um : base;
+            return base + (ubase + u) * 128;
+        });
+        return g;
+    };
+    PieceGather<NP> pg = gather(wv);
+    // unconditional (clamped past KC; those units are not used): a load in a
+    // branch makes the compiler's waits conservative
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int u = wv + NW * b;
-        if (u < KC) gateup_load_w(U[b], Wg, Wu, ubase + u, lane, rr);
+        gateup_load_codes(U[b], Wg, Wu, ubase + (u < KC ? u : KC - 1), lane);
     }
     // XL: x was staged and waited for by every wave before the barrier that
     // published the group
     for (int u0 = wv; u0 < KC; u0 += NW * NB) {
         if (u0 != wv) {
+            pg = gather(u0);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const int u = u0 + NW * b;
-                if (u < KC) gateup_load_w(U[b], Wg, Wu, ubase + u, lane, rr);
+                gateup_load_codes(U[b], Wg, Wu, ubase + (u < KC ? u : KC - 1), lane);
             }
         }
         __asm__ volatile("" ::: "memory");
+        // the scales landed before the codes (issued first): stage and read them
+        pg.store(pw);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            U[b].sg = piece_row(pw, (b * 2 + 0) * NPL, rr);
+            U[b].su = piece_row(pw, (b * 2 + 1) * NPL, rr);
+            if constexpr (FMT == MOE_FMT_Q2_B32) {
+                U[b].mg = piece_row(pw, (b * 2 + 0) * NPL + 1, rr);
+                U[b].mu = piece_row(pw, (b * 2 + 1) * NPL + 1, rr);
+            }
+        }
         if constexpr (!XL) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
@@ -338,8 +407,10 @@ __device__ __forceinline__ void down_block(const DownUnit<FMT, MT> &U, f32x4 *ac
 template <int FMT, int MT, int NW>
 struct DownW {
     static constexpr int NB = kDownBatch;
-    u32x2 lw[NB], sw[NB], mw[NB];
+    static constexpr int NPL = FMT == MOE_FMT_Q2_B32 ? 2 : 1;   // scale (and Q2 min) pieces per unit
+    u32x2 lw[NB];
     uint32_t hw[NB];
+    PieceGather<NB * NPL> pg;
 };
 
 template <int FMT, int MT, int NW>
@@ -351,16 +422,27 @@ __device__ __forceinline__ void down_load_w(DownW<FMT, MT, NW> &Wt, const QMatDe
     const int e = shared ? 0 : grp.expert;
     const int KC = f / 128;
     const size_t ubase = ((size_t)e * (d / 16) + ot) * KC;
+    constexpr int NB = DownW<FMT, MT, NW>::NB, NPL = DownW<FMT, MT, NW>::NPL;
+    (void)rr;
+    // the batch's scale pieces first (piece p: unit p / NPL, plane p % NPL)
+    {
+        const uint64_t sc = (uint64_t)W.scale, mn = (uint64_t)W.min;
+        Wt.pg.issue([=](int p) {
+            int u = u0 + NW * (p / NPL);
+            u = u < KC ? u : KC - 1;
+            uint64_t base = p % NPL ? mn : sc;
+            __asm__ volatile("" : "+v"(base));
+            return base + (ubase + u) * 128;
+        });
+    }
 #pragma unroll
-    for (int b = 0; b < DownW<FMT, MT, NW>::NB; ++b) {
+    for (int b = 0; b < NB; ++b) {
         int u = u0 + NW * b;
         u = u < KC ? u : KC - 1;   // clamped: unconditional loads, unused past KC
         const size_t unit = ubase + u;
         auto ld = [](const auto *p) { return __builtin_nontemporal_load(p); };   // read once
         Wt.lw[b] = ld(reinterpret_cast<const u32x2 *>(W.lo + unit * 512 + lane * 8));
         if constexpr (FMT == MOE_FMT_Q3_B32) Wt.hw[b] = ld(reinterpret_cast<const uint32_t *>(W.hi + unit * 256 + lane * 4));
-        Wt.sw[b] = ld(reinterpret_cast<const u32x2 *>(W.scale + unit * 64 + rr * 4));
-        if constexpr (FMT == MOE_FMT_Q2_B32) Wt.mw[b] = ld(reinterpret_cast<const u32x2 *>(W.min + unit * 64 + rr * 4));
     }
 }
 
@@ -377,7 +459,7 @@ __device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev 
                                           const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
                                           const int32_t *__restrict__ hx, int d, int f, const Group &grp, int ot,
                                           int wq, float (*red)[MT][IMAX][64], float *__restrict__ y_pairs,
-                                          float *__restrict__ y_shared, uint16_t *hs) {
+                                          float *__restrict__ y_shared, uint16_t *hs, u32x4 *pieces) {
     static_assert(!HL || MT == 1, "staged h: groups of at most 8 rows");
     const int lane = __lane_id();
     const int gq = lane >> 4, rr = lane & 15;
@@ -425,14 +507,16 @@ __device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev 
     constexpr int NB = DownW<FMT, MT, NW>::NB;
     for (int u0 = wq; u0 < KC; u0 += NW * NB) {
         if (u0 != wq) down_load_w<FMT, MT, NW>(Wt, down, sdown, d, f, grp, ot, u0);
+        constexpr int NPL = DownW<FMT, MT, NW>::NPL;
+        Wt.pg.store(pieces);
         DownUnit<FMT, MT> U[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             int u = u0 + NW * b;
             u = u < KC ? u : KC - 1;
             U[b].lw = Wt.lw[b];
-            U[b].sw = Wt.sw[b];
-            if constexpr (FMT == MOE_FMT_Q2_B32) U[b].mw = Wt.mw[b];
+            U[b].sw = piece_row(pieces, b * NPL, rr);
+            if constexpr (FMT == MOE_FMT_Q2_B32) U[b].mw = piece_row(pieces, b * NPL + 1, rr);
             if constexpr (FMT == MOE_FMT_Q3_B32) U[b].hw = Wt.hw[b];
             if constexpr (!HL) {
 #pragma unroll
@@ -560,6 +644,8 @@ __global__ __launch_bounds__(64 * NW * TPW) void gateup_small_kernel(
     uint16_t *__restrict__ h_lo, int32_t *__restrict__ hx, Group *__restrict__ table, int slot0) {
     __shared__ float red[NW * TPW][2][IMAX][64];
     __shared__ uint32_t redx[NW * TPW][16];
+    // per wave: a batch's scale pieces (16 units' worth: 2 matrices x 2 planes)
+    __shared__ u32x4 pieces[NW * TPW][8 * (16 / NW) * 2 * 2];
     extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];   // XL: x, T * d halves
     if constexpr (XL) {
         // x [T][d] into LDS once per workgroup by global-to-LDS copies (no
@@ -601,7 +687,7 @@ __global__ __launch_bounds__(64 * NW * TPW) void gateup_small_kernel(
         return;
     }
     gateup_task<FMT, IMAX, NW, XL, TPW>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp,
-                                        (int)blockIdx.x * TPW, red, redx, h_hi, h_lo, hx, xs_dyn);
+                                        (int)blockIdx.x * TPW, red, redx, h_hi, h_lo, hx, xs_dyn, &pieces[0][0]);
     if (rec) *reinterpret_cast<u32x4 *>(&table[blockIdx.y]) = __builtin_bit_cast(u32x4, grp);
 }
 
@@ -613,6 +699,7 @@ __global__ __launch_bounds__(64 * NW) void down_small_kernel(
     const int32_t *__restrict__ hx, int d, int f, const Group *__restrict__ table, float *__restrict__ y_pairs,
     float *__restrict__ y_shared, CombineArgs cb) {
     __shared__ float red[NW][MT][IMAX][64];
+    __shared__ u32x4 pieces[NW][64 * PieceGather<kDownBatch * 2>::N];   // per wave: a batch's scale pieces
     extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];   // HL: the group's h rows
     const Group grp = table[blockIdx.y];   // written by the gate/up kernel
     if (grp.nrows != 0) {
@@ -620,7 +707,7 @@ __global__ __launch_bounds__(64 * NW) void down_small_kernel(
         DownW<FMT, MT, NW> Wt;
         down_load_w<FMT, MT, NW>(Wt, down, sdown, d, f, grp, blockIdx.x, wq);
         down_task<FMT, MT, IMAX, NW, FUSE, HL>(Wt, down, sdown, h_hi, h_lo, hx, d, f, grp, blockIdx.x, wq, red,
-                                               y_pairs, y_shared, xs_dyn);
+                                               y_pairs, y_shared, xs_dyn, pieces[wq]);
     }
     if constexpr (FUSE) combine_tile(cb, y_pairs, y_shared, d, blockIdx.x, gridDim.y);
 }
@@ -637,6 +724,15 @@ __global__ __launch_bounds__(64 * NW) void down_small_kernel(
 // chunks each arrives on the tile's counter after its y stores and the last
 // one merges from memory (combine_tile).
 constexpr int kTileUnits = 6;   // d_ff / 128 <= 6
+// LDS halves per wave of down_tile_kernel: the group's h rows (hi and lo, RMAX
+// each), and first the scale pieces of its units (a region of whole 64-chunk
+// blocks)
+template <int FMT, int RMAX>
+__host__ __device__ constexpr int tile_region_halves(int f) {
+    const int np = kTileUnits * (FMT == MOE_FMT_Q2_B32 ? 2 : 1);
+    const int pieces = ((8 * np + 63) / 64) * 64 * 8;
+    return 2 * RMAX * f > pieces ? 2 * RMAX * f : pieces;
+}
 template <int FMT, int RMAX, bool FUSE>
 __global__ __launch_bounds__(64 * 16) void down_tile_kernel(
     QMatDev down, QMatDev sdown, const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
@@ -664,7 +760,25 @@ __global__ __launch_bounds__(64 * 16) void down_tile_kernel(
     float yv[RMAX];
     if (n > 0) {
         const int KC = f / 128, cpr = f / 8;
-        uint16_t *hs = hs_dyn + (size_t)wv * (2 * RMAX * f);
+        uint16_t *hs = hs_dyn + (size_t)wv * tile_region_halves<FMT, RMAX>(f);
+        const bool shared = grp.expert < 0;
+        const QMatDev W = shared ? sdown : down;
+        const size_t ubase = ((size_t)(shared ? 0 : grp.expert) * (d / 16) + ot) * KC;
+        // 0. the block scales (and Q2 minimums) of the wave's units, first:
+        //    piece p = unit p / NPL, plane p % NPL (staged through the wave's
+        //    h region before h lands there)
+        constexpr int NPL = FMT == MOE_FMT_Q2_B32 ? 2 : 1;
+        constexpr int NP = kTileUnits * NPL;
+        PieceGather<NP> pg;
+        {
+            const uint64_t sc = (uint64_t)W.scale, mn = (uint64_t)W.min;
+            pg.issue([=](int p) {
+                const int b = p / NPL;
+                uint64_t base = p % NPL ? mn : sc;
+                __asm__ volatile("" : "+v"(base));
+                return base + (ubase + (b < KC ? b : KC - 1)) * 128;
+            });
+        }
         // 1. the group's h rows, loaded into registers first and written to
         //    this wave's LDS once they land (register loads, not global-to-LDS
         //    copies: the compiler then waits for exactly these and leaves the
@@ -690,10 +804,7 @@ __global__ __launch_bounds__(64 * 16) void down_tile_kernel(
             const int r = 4 * gq + i < n ? 4 * gq + i : n - 1;
             ya[i] = 2 * hx[grp.hrow0 + r];
         }
-        // 3. all of the wave's weights (unconditional, clamped past KC)
-        const bool shared = grp.expert < 0;
-        const QMatDev W = shared ? sdown : down;
-        const size_t ubase = ((size_t)(shared ? 0 : grp.expert) * (d / 16) + ot) * KC;
+        // 3. all of the wave's codes (unconditional, clamped past KC)
         DownUnit<FMT, 1> U[kTileUnits];
 #pragma unroll
         for (int b = 0; b < kTileUnits; ++b) {
@@ -701,9 +812,15 @@ __global__ __launch_bounds__(64 * 16) void down_tile_kernel(
             auto ld = [](const auto *p) { return __builtin_nontemporal_load(p); };
             U[b].lw = ld(reinterpret_cast<const u32x2 *>(W.lo + unit * 512 + lane * 8));
             if constexpr (FMT == MOE_FMT_Q3_B32) U[b].hw = ld(reinterpret_cast<const uint32_t *>(W.hi + unit * 256 + lane * 4));
-            U[b].sw = ld(reinterpret_cast<const u32x2 *>(W.scale + unit * 64 + rr * 4));
-            if constexpr (FMT == MOE_FMT_Q2_B32) U[b].mw = ld(reinterpret_cast<const u32x2 *>(W.min + unit * 64 + rr * 4));
             __asm__ volatile("" ::: "memory");   // issue in unit order: unit 0 lands first
+        }
+        // the scales through the h region, then h itself (LDS accesses of one
+        // wave complete in order)
+        pg.store(reinterpret_cast<u32x4 *>(hs));
+#pragma unroll
+        for (int b = 0; b < kTileUnits; ++b) {
+            U[b].sw = piece_row(reinterpret_cast<const u32x4 *>(hs), b * NPL, rr);
+            if constexpr (FMT == MOE_FMT_Q2_B32) U[b].mw = piece_row(reinterpret_cast<const u32x4 *>(hs), b * NPL + 1, rr);
         }
 #pragma unroll
         for (int q = 0; q < QMAX; ++q)
@@ -831,10 +948,11 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
     if (MTD == 1 && T == 1 && k <= kTileMaxK && f <= 128 * kTileUnits && f % 128 == 0) {
         constexpr int RMAX = IMAX;
         int CH = slots < 16 ? slots : 16;
-        const int lds_ch = 49152 / (2 * RMAX * f * 2);   // waves whose h rows fit 48 KiB
+        const int region = tile_region_halves<FMT, RMAX>(f) * 2;   // bytes per wave
+        const int lds_ch = 49152 / region;                          // waves whose regions fit 48 KiB
         CH = CH < lds_ch ? CH : lds_ch;
         const int nchunks = (slots + CH - 1) / CH;
-        const unsigned lds = (unsigned)(CH * 2 * RMAX * f * 2);
+        const unsigned lds = (unsigned)(CH * region);
         if (cb.out)
             hipLaunchKernelGGL((down_tile_kernel<FMT, RMAX, true>), dim3(d / 16, nchunks), dim3(64 * CH), lds, s,
                                qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f, table, slots, nchunks, y_pairs,
