@@ -184,6 +184,13 @@ __device__ __forceinline__ void wait_vm() {
 // its own matrix ops before it arrives, so a stage that is refilled after the
 // barrier has no reads pending.
 __device__ __forceinline__ void wg_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
+// A barrier over LDS only: this wave's LDS accesses complete, then meet.  For
+// a block that has global stores (or loads) in flight that no other thread
+// reads back, where __syncthreads() would wait for them all first.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    wg_barrier();
+}
 
 // Locate the group handled by `slot`: slot 0 = shared expert (rows 0..T-1 in
 // token order), slot s >= 1 = the (s-1)-th expert with a non-empty segment.

@@ -449,11 +449,11 @@ __device__ void list_pairs(const int32_t *ids_s, int T, int E, int k, int tail_f
     constexpr uint32_t KEEP = 1u << 31;
     const int tid = threadIdx.x, wv = tid >> 6;
     for (int e = tid; e < 1024; e += 256) emask[e] = 0u;
-    __syncthreads();
+    lds_barrier();
     const int P = T * k;
     for (int p = tid; p < P; p += 256)
         atomicOr(&emask[ids_s[p]], (1u << (p / k)) | (p % k < tail_from ? KEEP : 0u));
-    __syncthreads();
+    lds_barrier();
     // exclusive scan of the per-expert counts, four experts per thread
     auto kept_count = [](uint32_t m) { return (m & KEEP) ? __popc(m & ~KEEP) : 0; };
     const int e0 = 4 * tid;
@@ -465,7 +465,7 @@ __device__ void list_pairs(const int32_t *ids_s, int T, int E, int k, int tail_f
     }
     const int incl = wave_scan_dpp(sum);
     if (__lane_id() == 63) wtot[wv] = incl;
-    __syncthreads();
+    lds_barrier();
     int run = incl - sum;
     for (int w2 = 0; w2 < wv; ++w2) run += wtot[w2];
 #pragma unroll
@@ -475,7 +475,7 @@ __device__ void list_pairs(const int32_t *ids_s, int T, int E, int k, int tail_f
         run += c[i];
     }
     if (tid == 255) offsets[E] = run;   // all (kept) pairs; slots past E count none
-    __syncthreads();
+    lds_barrier();
     for (int p = tid; p < P; p += 256) {
         const int e = ids_s[p], t = p / k;
         const uint32_t m = emask[e];
@@ -604,7 +604,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
 #pragma unroll
             for (int j = 0; j < 8; ++j) xT[ch * 8 + j][t] = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
         }
-        __syncthreads();
+        lds_barrier();
         float acc[TT][4];
 #pragma unroll
         for (int t = 0; t < TT; ++t)
@@ -758,8 +758,10 @@ __global__ __launch_bounds__(256) void route_small_kernel(
         // zero keys from 4 ceil(E/4) to the row's 64 Pk
         const int pad0 = 4 * E4, padn = 64 * Pk - pad0;
         for (int i = tid; i < nt * padn; i += 256) keys[i / padn][pad0 + i % padn] = 0ull;
-        if (k > kWaveTopkMaxK) __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // logits re-read below
-        __syncthreads();
+        // LDS only: the logits stores may land later (for large k, re-read
+        // below from memory, wait for them first)
+        if (k > kWaveTopkMaxK) __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
         if (wv < nt) {
             const int t = g0 + wv;
             int32_t *const id_t = ids + (size_t)(t0 + t) * k;
@@ -782,7 +784,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
                 wave_topk_any<true>(logits + (size_t)(t0 + t) * E, E, k, id_t, w_t, selv, seli);
             }
         }
-        __syncthreads();   // the key rows serve the next group
+        lds_barrier();   // the key rows serve the next group
     }
     if (listing) {
         if (Tt == 1)
