@@ -71,7 +71,6 @@ constexpr int PF_MT = MOE_PF_ROWS;                // rows per work item (multipl
 constexpr int PF_KS = 128;                        // K per pipeline stage
 constexpr int PF_STAGE = PF_MT * PF_KS * 2;       // bytes of one A stage
 constexpr int PF_NSTAGE = 3;                      // A stages in flight
-constexpr int PF_NI = PF_MT / 16;                 // A copy instructions per wave per stage
 static_assert(PF_MT % 64 == 0 && PF_MT <= 192, "item rows: a multiple of 64, at most 192");
 constexpr int PF_NXCD = 8;                        // XCDs (L2 domains) per device
 constexpr int PF_SORT = 2048;                     // sort slots, >= E + 1
@@ -408,8 +407,10 @@ struct PfGemmArgs {
 #ifndef MOE_PF_NTW
 #define MOE_PF_NTW 2
 #endif
-template <int NTW>
+template <int NTW, int NW>
 struct PfGeom {
+    static constexpr int NI = PF_MT / (4 * NW);     // A copy instructions per wave per stage
+    static_assert(NI * 4 * NW == PF_MT, "a stage's rows split evenly over the waves");
     static constexpr int HCOLS = 16 * NTW;          // gate/up: h columns per wave
     static constexpr int OCOLS = 32 * NTW;          // down: output columns per wave
     // epilogue staging per wave (in the A stages); pitches put rows 4 apart
@@ -418,13 +419,23 @@ struct PfGeom {
     static constexpr int EP0H_PITCH = HCOLS + 8;    // gate/up: [h | h_lo][32][EP0H_PITCH] halves
     static constexpr int EP1_PITCH = OCOLS + 8;     // [32][EP1_PITCH] floats
     static constexpr int EP_WAVE = (2 * 32 * EP0_PITCH > 32 * EP1_PITCH ? 2 * 32 * EP0_PITCH : 32 * EP1_PITCH) * 4;
-    static_assert(4 * EP_WAVE <= PF_NSTAGE * PF_STAGE, "epilogue staging must fit in the A stages");
+    static_assert(NW * EP_WAVE <= PF_NSTAGE * PF_STAGE, "epilogue staging must fit in the A stages");
     // sub-steps that issue the next stages' loads: weights in [0, NBS), A
-    // copies (two per sub-step) in [NBS, NBS + PF_NI / 2)
+    // copies (two per sub-step) in [NBS, NBS + NI / 2)
     static constexpr int NBS = NTW / 2 > 0 ? NTW / 2 : 1;
-    static_assert(NBS + PF_NI / 2 <= 8, "loads must fit in the eight sub-steps");
+    static_assert(NBS + NI / 2 <= 8 && NI % 2 == 0, "loads must fit in the eight sub-steps");
 };
 constexpr int kPfNtw = MOE_PF_NTW;
+// down: waves per workgroup and 32-column n-tiles per wave
+#ifndef MOE_PF_DOWN_NW
+#if MOE_PF_OCC == 1
+#define MOE_PF_DOWN_NW 8
+#else
+#define MOE_PF_DOWN_NW 4
+#endif
+#endif
+constexpr int kPfDownNw = MOE_PF_DOWN_NW;
+constexpr int kPfDownNtw = kPfDownNw == 8 ? 1 : kPfNtw;
 
 // silu(g) * u * 2^-2a from the accumulators g_a = g * 2^-a, u_a = u * 2^-a:
 // g_a * sigmoid(g) * u_a, the sigmoid taken at the true g = g_a * 2^a, with
@@ -443,11 +454,12 @@ __device__ __forceinline__ float swiglu_scaled(float ga, float ua, int a) {
 // SH (shared expert): exact weights as hi + lo.  For MODE 1 the K loop runs
 //   twice: A = h_hi with B hi and lo, then A = h_lo with B hi.
 // MT: 32-row m-tiles that hold rows of the item (1..4).
-template <int FMT, int MODE, bool SH, int MT, int NTW>
+template <int FMT, int MODE, bool SH, int MT, int NTW, int NW>
 __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item, int tile,
                                         uint8_t *As, int *s_row, int *s_exp, const PfItem *pf_items, int pf_t,
                                         int pf_n, PfItem *pf_dst) {
-    using G = PfGeom<NTW>;
+    using G = PfGeom<NTW, NW>;
+    constexpr int PF_NI = G::NI;
     const int tid = threadIdx.x, l = __lane_id();
     const int wv = wave_uniform(tid >> 6);
     const int h = l >> 5, uu = (l >> 4) & 1, rr = l & 15;
@@ -464,7 +476,7 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
     bool cols_valid;
     if constexpr (MODE == 0) {
         const int rpe = a.f / 16;
-        const int c0 = tile * 4 * G::HCOLS + wv * G::HCOLS;
+        const int c0 = tile * NW * G::HCOLS + wv * G::HCOLS;
         cols_valid = c0 < a.f;
 #pragma unroll
         for (int n = 0; n < NTW; ++n) {
@@ -474,7 +486,7 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
         }
     } else {
         const int rpe = a.d / 16;
-        const int c0 = tile * 4 * G::OCOLS + wv * G::OCOLS;
+        const int c0 = tile * NW * G::OCOLS + wv * G::OCOLS;
         cols_valid = c0 < a.d;
 #pragma unroll
         for (int n = 0; n < NTW; ++n) {
@@ -705,7 +717,7 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
                     }
                 __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
                 constexpr int LPR = G::HCOLS / 8;    // lanes per row (8 columns each)
-                const int c0 = tile * 4 * G::HCOLS + wv * G::HCOLS + (l % LPR) * 8;
+                const int c0 = tile * NW * G::HCOLS + wv * G::HCOLS + (l % LPR) * 8;
 #pragma unroll
                 for (int it = 0; it < 32 * LPR / 64; ++it) {
                     const int row = it * (64 / LPR) + l / LPR;
@@ -731,7 +743,7 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
                 __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
                 float *out = SH ? a.y_shared : a.y_pairs;
                 constexpr int LPR = G::OCOLS / 4;    // lanes per row (4 columns each)
-                const int c0 = tile * 4 * G::OCOLS + wv * G::OCOLS + (l % LPR) * 4;
+                const int c0 = tile * NW * G::OCOLS + wv * G::OCOLS + (l % LPR) * 4;
 #pragma unroll 2
                 for (int it = 0; it < 32 * LPR / 64; ++it) {
                     const int row = it * (64 / LPR) + l / LPR;
@@ -758,8 +770,8 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
 
 // Persistent grouped GEMM: workgroups take (item, column tile) units by
 // ticket from their XCD's queue, then from the others.
-template <int FMT, int MODE, int NTW>
-__global__ __launch_bounds__(256, MOE_PF_OCC) void pf_gemm_kernel(PfGemmArgs a) {
+template <int FMT, int MODE, int NTW, int NW>
+__global__ __launch_bounds__(64 * NW, MOE_PF_OCC) void pf_gemm_kernel(PfGemmArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t As[PF_NSTAGE * PF_STAGE];
     __shared__ int s_row[PF_MT];
     __shared__ int s_exp[PF_MT];
@@ -805,15 +817,15 @@ __global__ __launch_bounds__(256, MOE_PF_OCC) void pf_gemm_kernel(PfGemmArgs a) 
         const int tile = t % a.nt;
         constexpr int MTX = PF_MT / 32;
         if (item.expert < 0) {
-            pf_unit<FMT, MODE, true, MTX, NTW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next);
+            pf_unit<FMT, MODE, true, MTX, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next);
         } else {
             switch ((item.nrows + 31) >> 5) {
-                case 1: pf_unit<FMT, MODE, false, 1, NTW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
-                case 2: pf_unit<FMT, MODE, false, 2, NTW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
-                case 3: pf_unit<FMT, MODE, false, 3, NTW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
-                case 4: pf_unit<FMT, MODE, false, 4 < MTX ? 4 : MTX, NTW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
-                case 5: pf_unit<FMT, MODE, false, 5 < MTX ? 5 : MTX, NTW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
-                default: pf_unit<FMT, MODE, false, MTX, NTW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                case 1: pf_unit<FMT, MODE, false, 1, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                case 2: pf_unit<FMT, MODE, false, 2, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                case 3: pf_unit<FMT, MODE, false, 3, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                case 4: pf_unit<FMT, MODE, false, 4 < MTX ? 4 : MTX, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                case 5: pf_unit<FMT, MODE, false, 5 < MTX ? 5 : MTX, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                default: pf_unit<FMT, MODE, false, MTX, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
             }
         }
         // pf_unit ended with a barrier: every thread has read s_ticket
@@ -904,7 +916,8 @@ static void pf_launch_fmt(const moe_layer &L, const uint16_t *x, int T, int k, c
     a.k = k;
     a.d = d;
     a.f = f;
-    using G = PfGeom<kPfNtw>;
+    using G = PfGeom<kPfNtw, 4>;
+    using GD = PfGeom<kPfDownNtw, kPfDownNw>;
     const int grid = pf_grid(MOE_PF_OCC);
     // gate/up + SwiGLU
     a.w0 = QMatDev{L.gate.lo, L.gate.hi, L.gate.scale, L.gate.min};
@@ -915,15 +928,15 @@ static void pf_launch_fmt(const moe_layer &L, const uint16_t *x, int T, int k, c
     a.a_lo = nullptr;
     a.nt = (f + 4 * G::HCOLS - 1) / (4 * G::HCOLS);
     a.launch = 0;
-    hipLaunchKernelGGL((pf_gemm_kernel<FMT, 0, kPfNtw>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((pf_gemm_kernel<FMT, 0, kPfNtw, 4>), dim3(grid), dim3(256), 0, s, a);
     // down
     a.w0 = a.w1 = QMatDev{L.down.lo, L.down.hi, L.down.scale, L.down.min};
     a.s0 = a.s1 = QMatDev{L.sh_down.lo, L.sh_down.hi, L.sh_down.scale, L.sh_down.min};
     a.a_hi = w.h;
     a.a_lo = w.h_lo;
-    a.nt = (d + 4 * G::OCOLS - 1) / (4 * G::OCOLS);
+    a.nt = (d + kPfDownNw * GD::OCOLS - 1) / (kPfDownNw * GD::OCOLS);
     a.launch = 1;
-    hipLaunchKernelGGL((pf_gemm_kernel<FMT, 1, kPfNtw>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((pf_gemm_kernel<FMT, 1, kPfDownNtw, kPfDownNw>), dim3(grid), dim3(64 * kPfDownNw), 0, s, a);
 }
 
 static hipError_t launch(const moe_layer &L, const uint16_t *x, int T, int k, const int32_t *offsets,
