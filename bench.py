@@ -65,10 +65,10 @@ METRIC = "MoE-layer tokens/s (decode T=1/4, prefill 8192); % HBM BW or % MFMA pe
 # the kernel sources it was taken on and is reported as null once those
 # sources change.
 TRAFFIC = {
-    1: (("common.h", "ffn_small.hip"), "6c8ab70c15c43e43", 20203520),
-    2: (("common.h", "ffn_small.hip"), "6c8ab70c15c43e43", 49151385),
-    3: (("common.h", "ffn_prefill.hip"), "b267e8c39e1bdf1e", 2569451315),
-    4: (("common.h", "ffn_prefill.hip"), "b267e8c39e1bdf1e", 2187057459),
+    1: (("common.h", "ffn_small.hip"), "79b719b83fd90c90", 20205076),
+    2: (("common.h", "ffn_small.hip"), "79b719b83fd90c90", 49141813),
+    3: (("common.h", "ffn_prefill.hip"), "b24aec8d00ca9ac9", 2557251860),
+    4: (("common.h", "ffn_prefill.hip"), "b24aec8d00ca9ac9", 2186023823),
 }
 
 
