@@ -23,7 +23,12 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
 
 # small-batch expert kernels read every matrix-core result right away: keep
 # the results in VGPRs instead of accumulation registers
-EXTRA = {"ffn_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# the grouped GEMM takes its work tickets with one lane's atomic add, whose
+# result is used only later: without the compiler's atomic optimizer the add
+# is not widened into a wave reduction that waits for it (and for every
+# load and store in flight) on the spot
+EXTRA = {"ffn_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "ffn_prefill.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _compile(entry) -> str:

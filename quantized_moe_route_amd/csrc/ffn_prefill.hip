@@ -456,8 +456,8 @@ __device__ __forceinline__ float swiglu_scaled(float ga, float ua, int a) {
 // MT: 32-row m-tiles that hold rows of the item (1..4).
 template <int FMT, int MODE, bool SH, int MT, int NTW, int NW>
 __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item, int tile,
-                                        uint8_t *As, int *s_row, int *s_exp, const PfItem *pf_items, int pf_t,
-                                        int pf_n, PfItem *pf_dst) {
+                                        uint8_t *As, int *s_row, int *s_exp, const PfItem *pf_items,
+                                        int *pf_ticket, int &pf_t, int pf_n, PfItem *pf_dst) {
     using G = PfGeom<NTW, NW>;
     constexpr int PF_NI = G::NI;
     const int tid = threadIdx.x, l = __lane_id();
@@ -602,8 +602,15 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
     // of the steps, so the copy of step kc + 2 stays in flight through the
     // barrier that ends step kc
     __syncthreads();
+    // The next unit's ticket (thread 0; pf_ticket is this queue's counter)
+    // is taken two k-steps before the end: late enough that no WG holds a
+    // ticket for a unit it will not start soon (an early ticket leaves the
+    // queue's last units waiting behind long ones while other WGs idle),
+    // early enough that the atomic has returned when the loop ends.
+    const int kt = NSTEP > 2 ? NSTEP - 2 : 0;
     for (int kc = 0; kc < NSTEP; ++kc) {
         const int st = kc % PF_NSTAGE;
+        if (tid == 0 && kc == kt) pf_t = atomicAdd(pf_ticket, 1);
         const bool more1 = kc + 1 < NSTEP, more2 = kc + 2 < NSTEP;
         const int kb = kc + 1 < KC ? kc + 1 : kc + 1 - KC;
         const int ka = kc + 2;     // A stage copied during this step
@@ -677,7 +684,7 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
     __syncthreads();
     // the next unit's item (thread 0), loaded while the epilogue runs
     // (thread 0: pf_t is the next ticket of this queue, pf_items its items,
-    // pf_n its unit count)
+    // pf_n its unit count; other threads: pf_t = pf_n)
     u32x4 pfv = {0u, 0u, 0u, 0u};
     const int pt = pf_t;
     const bool pf_on = tid == 0 && pt < pf_n;
@@ -804,8 +811,8 @@ __global__ __launch_bounds__(64 * NW, MOE_PF_OCC) void pf_gemm_kernel(PfGemmArgs
             __syncthreads();
             continue;
         }
-        int nxt = 0;
-        if (threadIdx.x == 0) nxt = atomicAdd(&a.sched->ticket[a.launch][x], 1);
+        int nxt = n_units;   // thread 0: the next ticket, taken inside the unit
+        int *tk = &a.sched->ticket[a.launch][x];
         const bool have = s_next_t == t && s_next_x == x;   // uniform
         typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
         u32x4 iv;
@@ -817,15 +824,15 @@ __global__ __launch_bounds__(64 * NW, MOE_PF_OCC) void pf_gemm_kernel(PfGemmArgs
         const int tile = t % a.nt;
         constexpr int MTX = PF_MT / 32;
         if (item.expert < 0) {
-            pf_unit<FMT, MODE, true, MTX, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next);
+            pf_unit<FMT, MODE, true, MTX, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, tk, nxt, n_units, &s_next);
         } else {
             switch ((item.nrows + 31) >> 5) {
-                case 1: pf_unit<FMT, MODE, false, 1, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
-                case 2: pf_unit<FMT, MODE, false, 2, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
-                case 3: pf_unit<FMT, MODE, false, 3, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
-                case 4: pf_unit<FMT, MODE, false, 4 < MTX ? 4 : MTX, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
-                case 5: pf_unit<FMT, MODE, false, 5 < MTX ? 5 : MTX, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
-                default: pf_unit<FMT, MODE, false, MTX, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, threadIdx.x == 0 ? nxt : n_units, n_units, &s_next); break;
+                case 1: pf_unit<FMT, MODE, false, 1, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, tk, nxt, n_units, &s_next); break;
+                case 2: pf_unit<FMT, MODE, false, 2, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, tk, nxt, n_units, &s_next); break;
+                case 3: pf_unit<FMT, MODE, false, 3, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, tk, nxt, n_units, &s_next); break;
+                case 4: pf_unit<FMT, MODE, false, 4 < MTX ? 4 : MTX, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, tk, nxt, n_units, &s_next); break;
+                case 5: pf_unit<FMT, MODE, false, 5 < MTX ? 5 : MTX, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, tk, nxt, n_units, &s_next); break;
+                default: pf_unit<FMT, MODE, false, MTX, NTW, NW>(a, item, tile, As, s_row, s_exp, a.items + i0, tk, nxt, n_units, &s_next); break;
             }
         }
         // pf_unit ended with a barrier: every thread has read s_ticket
