@@ -436,6 +436,16 @@ constexpr int kPfNtw = MOE_PF_NTW;
 #endif
 constexpr int kPfDownNw = MOE_PF_DOWN_NW;
 constexpr int kPfDownNtw = kPfDownNw == 8 ? 1 : kPfNtw;
+// gate/up: eight waves of one n-tile (gate or up rows) or four of two
+#ifndef MOE_PF_GU_NW
+#if MOE_PF_OCC == 1
+#define MOE_PF_GU_NW 8
+#else
+#define MOE_PF_GU_NW 4
+#endif
+#endif
+constexpr int kPfGuNw = MOE_PF_GU_NW;
+constexpr int kPfGuNtw = kPfGuNw == 8 ? 1 : kPfNtw;
 
 // silu(g) * u * 2^-2a from the accumulators g_a = g * 2^-a, u_a = u * 2^-a:
 // g_a * sigmoid(g) * u_a, the sigmoid taken at the true g = g_a * 2^a, with
@@ -460,6 +470,10 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
                                         int *pf_ticket, int &pf_t, int pf_n, PfItem *pf_dst) {
     using G = PfGeom<NTW, NW>;
     constexpr int PF_NI = G::NI;
+    // gate/up with eight waves, one n-tile each: waves 0-3 hold gate rows,
+    // waves 4-7 the up rows of the same 32 h columns (pair wv & 3)
+    constexpr bool GU8 = MODE == 0 && NW == 8;
+    static_assert(!GU8 || NTW == 1, "eight gate/up waves take one n-tile each");
     const int tid = threadIdx.x, l = __lane_id();
     const int wv = wave_uniform(tid >> 6);
     const int h = l >> 5, uu = (l >> 4) & 1, rr = l & 15;
@@ -474,7 +488,14 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
     const QMatDev W1 = SH ? a.s1 : a.w1;
     size_t ub[NTW];
     bool cols_valid;
-    if constexpr (MODE == 0) {
+    if constexpr (GU8) {
+        const int rpe = a.f / 16;
+        const int c0 = tile * 4 * 32 + (wv & 3) * 32;
+        cols_valid = c0 < a.f;
+        int t16 = c0 / 16 + uu;
+        t16 = t16 < rpe ? t16 : rpe - 1;
+        ub[0] = ((size_t)e * rpe + t16) * KC;
+    } else if constexpr (MODE == 0) {
         const int rpe = a.f / 16;
         const int c0 = tile * NW * G::HCOLS + wv * G::HCOLS;
         cols_valid = c0 < a.f;
@@ -497,7 +518,7 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
     }
     // slot 0 = (h, rr) -> columns 32j + 8h; slot 1 = (2 + h, rr) -> 32j + 16 + 8h
     auto load_b_tile = [&](BRaw<FMT> (&br)[NTW][2], int kc, int n) {
-        const QMatDev &W = (MODE == 0 && n >= NTW / 2) ? W1 : W0;
+        const QMatDev &W = (MODE == 0 && (GU8 ? wv >= 4 : n >= NTW / 2)) ? W1 : W0;
         const size_t u = ub[n] + kc;
         const uint8_t *lo = W.lo + u * 512;
         // a routed expert's weights are mostly read by one item: nontemporal
@@ -696,7 +717,62 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
     // stages are free now): accumulators out as written by the matrix core
     // (D row 8 (r / 4) + 4 h + r % 4, column l % 32), then read back along
     // rows so each lane stores 16 contiguous bytes.
-    if (cols_valid) {
+    if constexpr (GU8) {
+        // The up waves hand their sums to the gate waves of the same columns
+        // through LDS ([pair][m][r][lane] floats, 16 KiB per m-tile); the
+        // gate waves then apply SwiGLU and store h as below.
+        constexpr int XCH = 4 * (PF_MT / 32) * 16 * 64 * 4;
+        constexpr int EPH = 40;                          // h staging pitch (32 columns + 8), halves
+        constexpr int EPW = 2 * 32 * EPH * 2;            // h and h_lo, bytes per gate wave
+        static_assert(XCH + 4 * EPW <= PF_NSTAGE * PF_STAGE, "exchange and staging fit in the A stages");
+        float *xch = reinterpret_cast<float *>(As);
+        if (cols_valid && wv >= 4) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xch[(((wv - 4) * MT + m) * 16 + r) * 64 + l] = acc[m][0][r];
+        }
+        lds_barrier();
+        if (cols_valid && wv < 4) {
+            uint16_t *eh = reinterpret_cast<uint16_t *>(As + XCH + wv * EPW);
+            uint16_t *el = eh + 32 * EPH;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                int rx[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) rx[r] = s_exp[m * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+                    const float uv = xch[((wv * MT + m) * 16 + r) * 64 + l];
+                    const float hv = swiglu_scaled(acc[m][0][r], uv, rx[r]);
+                    const _Float16 hh = static_cast<_Float16>(hv);
+                    eh[row * EPH + (l & 31)] = __builtin_bit_cast(uint16_t, hh);
+                    if constexpr (SH)
+                        el[row * EPH + (l & 31)] =
+                            __builtin_bit_cast(uint16_t, static_cast<_Float16>(hv - static_cast<float>(hh)));
+                }
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                // 4 lanes per row, 8 columns each
+                const int c0 = tile * 4 * 32 + wv * 32 + (l & 3) * 8;
+#pragma unroll
+                for (int it = 0; it < 2; ++it) {
+                    const int row = it * 16 + (l >> 2);
+                    const int grow = m * 32 + row;
+                    const u32x4 hw = *reinterpret_cast<const u32x4 *>(eh + row * EPH + (l & 3) * 8);
+                    u32x4 lw;
+                    if constexpr (SH) lw = *reinterpret_cast<const u32x4 *>(el + row * EPH + (l & 3) * 8);
+                    if (grow < nrows) {
+                        *reinterpret_cast<u32x4 *>(a.h_out + (size_t)(item.hrow0 + grow) * a.f + c0) = hw;
+                        if constexpr (SH)
+                            *reinterpret_cast<u32x4 *>(a.h_lo_out + (size_t)(item.row0 + grow) * a.f + c0) = lw;
+                    }
+                }
+                // the next m-tile overwrites the staging: finish reading it first
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+            }
+        }
+    } else if (cols_valid) {
         float *ep = reinterpret_cast<float *>(As + wv * G::EP_WAVE);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -923,7 +999,7 @@ static void pf_launch_fmt(const moe_layer &L, const uint16_t *x, int T, int k, c
     a.k = k;
     a.d = d;
     a.f = f;
-    using G = PfGeom<kPfNtw, 4>;
+    using G = PfGeom<kPfNtw, 4>;   // a gate/up unit spans 4 x 32 h columns either way
     using GD = PfGeom<kPfDownNtw, kPfDownNw>;
     const int grid = pf_grid(MOE_PF_OCC);
     // gate/up + SwiGLU
@@ -935,7 +1011,7 @@ static void pf_launch_fmt(const moe_layer &L, const uint16_t *x, int T, int k, c
     a.a_lo = nullptr;
     a.nt = (f + 4 * G::HCOLS - 1) / (4 * G::HCOLS);
     a.launch = 0;
-    hipLaunchKernelGGL((pf_gemm_kernel<FMT, 0, kPfNtw, 4>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((pf_gemm_kernel<FMT, 0, kPfGuNtw, kPfGuNw>), dim3(grid), dim3(64 * kPfGuNw), 0, s, a);
     // down
     a.w0 = a.w1 = QMatDev{L.down.lo, L.down.hi, L.down.scale, L.down.min};
     a.s0 = a.s1 = QMatDev{L.sh_down.lo, L.sh_down.hi, L.sh_down.scale, L.sh_down.min};
