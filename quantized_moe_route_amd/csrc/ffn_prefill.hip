@@ -718,34 +718,43 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
     // (D row 8 (r / 4) + 4 h + r % 4, column l % 32), then read back along
     // rows so each lane stores 16 contiguous bytes.
     if constexpr (GU8) {
-        // The up waves hand their sums to the gate waves of the same columns
-        // through LDS ([pair][m][r][lane] floats, 16 KiB per m-tile); the
-        // gate waves then apply SwiGLU and store h as below.
+        // The two waves of a column pair split the m-tiles: the gate wave
+        // takes the first MH, the up wave the rest.  Each first hands the
+        // other its sums for the other's m-tiles through LDS ([pair][m][r]
+        // [lane] floats, 4 KiB per pair and m-tile), then applies SwiGLU to
+        // its own m-tiles and stores h as below.
+        constexpr int MH = (MT + 1) / 2;
         constexpr int XCH = 4 * (PF_MT / 32) * 16 * 64 * 4;
         constexpr int EPH = 40;                          // h staging pitch (32 columns + 8), halves
-        constexpr int EPW = 2 * 32 * EPH * 2;            // h and h_lo, bytes per gate wave
-        static_assert(XCH + 4 * EPW <= PF_NSTAGE * PF_STAGE, "exchange and staging fit in the A stages");
+        constexpr int EPW = 2 * 32 * EPH * 2;            // h and h_lo, bytes per wave
+        static_assert(XCH + 8 * EPW <= PF_NSTAGE * PF_STAGE, "exchange and staging fit in the A stages");
+        const int pr = wv & 3;
+        const bool upw = wv >= 4;
         float *xch = reinterpret_cast<float *>(As);
-        if (cols_valid && wv >= 4) {
+        if (cols_valid) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)
+                if (upw ? m < MH : m >= MH) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) xch[(((wv - 4) * MT + m) * 16 + r) * 64 + l] = acc[m][0][r];
+                    for (int r = 0; r < 16; ++r) xch[((pr * MT + m) * 16 + r) * 64 + l] = acc[m][0][r];
+                }
         }
         lds_barrier();
-        if (cols_valid && wv < 4) {
+        if (cols_valid) {
             uint16_t *eh = reinterpret_cast<uint16_t *>(As + XCH + wv * EPW);
             uint16_t *el = eh + 32 * EPH;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
+                if (upw ? m < MH : m >= MH) continue;
                 int rx[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) rx[r] = s_exp[m * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = 8 * (r >> 2) + 4 * h + (r & 3);
-                    const float uv = xch[((wv * MT + m) * 16 + r) * 64 + l];
-                    const float hv = swiglu_scaled(acc[m][0][r], uv, rx[r]);
+                    const float ov = xch[((pr * MT + m) * 16 + r) * 64 + l];
+                    const float gv = upw ? ov : acc[m][0][r], uv = upw ? acc[m][0][r] : ov;
+                    const float hv = swiglu_scaled(gv, uv, rx[r]);
                     const _Float16 hh = static_cast<_Float16>(hv);
                     eh[row * EPH + (l & 31)] = __builtin_bit_cast(uint16_t, hh);
                     if constexpr (SH)
@@ -754,7 +763,7 @@ __device__ __forceinline__ void pf_unit(const PfGemmArgs &a, const PfItem &item,
                 }
                 __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
                 // 4 lanes per row, 8 columns each
-                const int c0 = tile * 4 * 32 + wv * 32 + (l & 3) * 8;
+                const int c0 = tile * 4 * 32 + pr * 32 + (l & 3) * 8;
 #pragma unroll
                 for (int it = 0; it < 2; ++it) {
                     const int row = it * 16 + (l >> 2);
