@@ -67,8 +67,8 @@ METRIC = "MoE-layer tokens/s (decode T=1/4, prefill 8192); % HBM BW or % MFMA pe
 TRAFFIC = {
     1: (("common.h", "ffn_small.hip"), "79b719b83fd90c90", 20205076),
     2: (("common.h", "ffn_small.hip"), "79b719b83fd90c90", 49141813),
-    3: (("common.h", "ffn_prefill.hip"), "b24aec8d00ca9ac9", 2557251860),
-    4: (("common.h", "ffn_prefill.hip"), "b24aec8d00ca9ac9", 2186023823),
+    3: (("common.h", "ffn_prefill.hip"), "d5ceeb8a1c8afa74", 2504851340),
+    4: (("common.h", "ffn_prefill.hip"), "d5ceeb8a1c8afa74", 2159141085),
 }
 
 
