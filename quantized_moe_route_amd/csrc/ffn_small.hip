@@ -635,9 +635,11 @@ __device__ __forceinline__ void combine_tile(const CombineArgs &cb, const float 
 // grid: (d_ff/16 row tiles, group slots slot0 + blockIdx.y: slot 0 the shared
 // expert, slots 1 .. min(E, P) the routed groups); NW waves split K.  The
 // first tile of each slot also records the slot's group (nrows 0: none) in
-// `table`, so the down kernel reads it with one load.
-template <int FMT, int IMAX, int NW, bool XL, int TPW>
-__global__ __launch_bounds__(64 * NW * TPW) void gateup_small_kernel(
+// `table`, so the down kernel reads it with one load.  NB: units each wave
+// has in flight per batch (fewer hold fewer registers).
+template <int FMT, int IMAX, int NW, bool XL, int TPW, int NB = 16 / NW>
+__global__ __launch_bounds__(64 * NW * TPW) __attribute__((amdgpu_waves_per_eu(IMAX > 2 && NB == 2 ? 5 : 1)))
+void gateup_small_kernel(
     QMatDev gate, QMatDev up, QMatDev sgate, QMatDev sup, const uint16_t *__restrict__ x, int T,
     int k, int d, int f, int E, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ sorted_pair, uint16_t *__restrict__ h_hi,
@@ -645,7 +647,7 @@ __global__ __launch_bounds__(64 * NW * TPW) void gateup_small_kernel(
     __shared__ float red[NW * TPW][2][IMAX][64];
     __shared__ uint32_t redx[NW * TPW][16];
     // per wave: a batch's scale pieces (16 units' worth: 2 matrices x 2 planes)
-    __shared__ u32x4 pieces[NW * TPW][8 * (16 / NW) * 2 * 2];
+    __shared__ u32x4 pieces[NW * TPW][8 * NB * 2 * 2];
     extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];   // XL: x, T * d halves
     if constexpr (XL) {
         // x [T][d] into LDS once per workgroup by global-to-LDS copies (no
@@ -686,7 +688,7 @@ __global__ __launch_bounds__(64 * NW * TPW) void gateup_small_kernel(
         if (rec) *reinterpret_cast<u32x4 *>(&table[blockIdx.y]) = u32x4{0u, 0u, 0u, 0u};
         return;
     }
-    gateup_task<FMT, IMAX, NW, XL, TPW>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp,
+    gateup_task<FMT, IMAX, NW, XL, TPW, NB>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp,
                                         (int)blockIdx.x * TPW, red, redx, h_hi, h_lo, hx, xs_dyn, &pieces[0][0]);
     if (rec) *reinterpret_cast<u32x4 *>(&table[blockIdx.y]) = __builtin_bit_cast(u32x4, grp);
 }
@@ -926,7 +928,16 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
     // reads each x byte from L2 once per workgroup instead of once per wave
     // and lane group
     const size_t xbytes = (size_t)T * d * 2;
-    if (T <= 8 && xbytes <= kXsMaxBytes)
+    if (IMAX > 2 && T <= 4 && xbytes <= kXsMaxBytes)
+        // three or four tokens: batches of two units per wave, so that five
+        // workgroups fit a CU (96 VGPRs, 28 KiB of LDS) and every real
+        // group's workgroups are resident at once (with four-unit batches,
+        // 124 VGPRs, only four fit and the last groups ran as a second
+        // round: workload 2 +3.5%, T = 4 Q2 +3%; at T = 8 it lost 0.5%)
+        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, true, 1, 2>), dim3(f / 16, slots),
+                           dim3(64 * NWG), (unsigned)xbytes, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up),
+                           x, T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, hx, table, slot0);
+    else if (T <= 8 && xbytes <= kXsMaxBytes)
         hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, true, 1>), dim3(f / 16, slots),
                            dim3(64 * NWG), (unsigned)xbytes, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up),
                            x, T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, hx, table, slot0);
