@@ -229,15 +229,13 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
     const size_t ubase = ((size_t)e * (f / 16) + nt) * KC;
     const int nrows = grp.nrows;
 
-    // token of output row 4 gq + i; lanes past the group's last row use its
-    // last row (never stored), so the loads are unconditional and go out
-    // together, before the weights
-    int otok[IMAX];
-#pragma unroll
-    for (int i = 0; i < IMAX; ++i) {
-        int r = 4 * gq + i;
-        r = r < nrows ? r : nrows - 1;
-        otok[i] = shared ? r : sorted_pair[grp.row0 + r];
+    // the pair of output row r = lane % 16 (rows past the group's last row
+    // use its last row, never stored): one register, loaded unconditionally
+    // before the weights, read by wave 0 at the end through a lane shuffle
+    int rtok;
+    {
+        const int r = rr < nrows ? rr : nrows - 1;
+        rtok = shared ? r : sorted_pair[grp.row0 + r];
     }
     f32x4 ag[1], au[1];
     ag[0] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -348,8 +346,9 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
 #pragma unroll
     for (int i = 0; i < IMAX; ++i) {
         const int r = 4 * gq + i;
+        const int tk = __shfl(rtok, r, 64);
         if (r >= nrows) continue;
-        const int t = shared ? otok[i] : otok[i] / k;
+        const int t = shared ? tk : tk / k;
         const int sl = (t >> 2) * 16 + rr, si = t & 3;
         float gs = red[0][0][si][sl], us = red[0][1][si][sl];
         uint32_t mx = redx[0][t];
