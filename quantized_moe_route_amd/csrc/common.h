@@ -142,6 +142,28 @@ __device__ __forceinline__ u32x4 hi_operand(uint32_t H) {
     return r;
 }
 
+// Q3 code bit 2 of block j as an operand holding 4*bit - 4 (-4 or 0): the
+// nibbles where the bit is clear become 9 = fp4 -0.5, scaled by 8; the others
+// stay 0.  With the low-bits operand the matrix op then sums x * (q - 4).
+template <int J, bool F16>
+__device__ __forceinline__ u32x4 hi_operand_m4(uint32_t H) {
+    uint32_t v = ((H >> J) & 0x11111111u) ^ 0x11111111u;
+    v |= v << 3;
+    u32x4 r;
+    if constexpr (F16) {
+        r[0] = cvt_fp4_f16<0>(v, 8.0f);
+        r[1] = cvt_fp4_f16<1>(v, 8.0f);
+        r[2] = cvt_fp4_f16<2>(v, 8.0f);
+        r[3] = cvt_fp4_f16<3>(v, 8.0f);
+    } else {
+        r[0] = cvt_fp4_bf16<0>(v, 8.0f);
+        r[1] = cvt_fp4_bf16<1>(v, 8.0f);
+        r[2] = cvt_fp4_bf16<2>(v, 8.0f);
+        r[3] = cvt_fp4_bf16<3>(v, 8.0f);
+    }
+    return r;
+}
+
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

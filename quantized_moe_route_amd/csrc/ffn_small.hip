@@ -14,11 +14,12 @@
 //     wave load is 512 contiguous bytes;
 //   - 2-bit codes become exact bf16/fp16 integers with the fp4 conversion
 //     (two masks + four converts per 16 codes); Q3's third bit is a second
-//     operand holding 4*bit;
+//     operand holding 4*bit - 4 (-4 or 0), so the two hold q - 4;
 //   - the 32-wide K block is exactly one 16x16x32 matrix-core step, so the
 //     product codes x activations comes out per block, and the block scale and
-//     minimum are applied in fp32: acc += d*P + m*X (Q2) or d*(P - 4X) (Q3),
-//     X = sum of the block's activations (a matrix-core step against ones).
+//     minimum are applied in fp32: acc += d*P + m*X (Q2, X = sum of the
+//     block's activations, a matrix-core step against ones) or d*P (Q3, P
+//     over q - 4).
 //   Weights are therefore used exactly (no rounding of d*q + m), and all sums
 //   are fp32.
 //   - gate/up: A = the batch's x rows (bf16, exact; each group row then takes
@@ -120,7 +121,7 @@ __device__ __forceinline__ void gateup_load_x(GateUpUnit<FMT, MT> &U, int u, int
 template <int J, bool F16, int FMT>
 __device__ __forceinline__ void block_operands(uint32_t lo_dw, uint32_t hi_w, u32x4 &B, u32x4 &H) {
     B = lo_operand<J & 1, F16>(lo_dw);
-    if constexpr (FMT == MOE_FMT_Q3_B32) H = hi_operand<J, F16>(hi_w);
+    if constexpr (FMT == MOE_FMT_Q3_B32) H = hi_operand_m4<J, F16>(hi_w);   // 4 bit2 - 4
 }
 
 __device__ __forceinline__ float half_of(const u32x2 &v, int j) {
@@ -148,18 +149,20 @@ __device__ __forceinline__ void gateup_block(const GateUpUnit<FMT, MT> &U, f32x4
         f32x4 pg = mfma_bf16(U.A[mt][J], Bg, zero);
         f32x4 pu = mfma_bf16(U.A[mt][J], Bu, zero);
         if constexpr (FMT == MOE_FMT_Q3_B32) {
+            // x . (q - 4): the offset rides in the bit-2 operand
             pg = mfma_bf16(U.A[mt][J], Hg, pg);
             pu = mfma_bf16(U.A[mt][J], Hu, pu);
-        }
-        const f32x4 xs = mfma_bf16(U.A[mt][J], ones, zero);
 #pragma unroll
-        for (int i = 0; i < IMAX; ++i) {
-            if constexpr (FMT == MOE_FMT_Q2_B32) {
+            for (int i = 0; i < IMAX; ++i) {
+                ag[mt][i] = fmaf(dg, pg[i], ag[mt][i]);
+                au[mt][i] = fmaf(du, pu[i], au[mt][i]);
+            }
+        } else {
+            const f32x4 xs = mfma_bf16(U.A[mt][J], ones, zero);
+#pragma unroll
+            for (int i = 0; i < IMAX; ++i) {
                 ag[mt][i] = fmaf(dg, pg[i], fmaf(mgv, xs[i], ag[mt][i]));
                 au[mt][i] = fmaf(du, pu[i], fmaf(muv, xs[i], au[mt][i]));
-            } else {
-                ag[mt][i] = fmaf(dg, fmaf(-4.0f, xs[i], pg[i]), ag[mt][i]);
-                au[mt][i] = fmaf(du, fmaf(-4.0f, xs[i], pu[i]), au[mt][i]);
             }
         }
     }
@@ -389,14 +392,15 @@ __device__ __forceinline__ void down_block(const DownUnit<FMT, MT> &U, f32x4 *ac
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         f32x4 p = mfma_f16(U.A[mt][J], B, zero);
-        if constexpr (FMT == MOE_FMT_Q3_B32) p = mfma_f16(U.A[mt][J], H, p);
-        const f32x4 hs = mfma_f16(U.A[mt][J], ones, zero);
+        if constexpr (FMT == MOE_FMT_Q3_B32) {
+            // h . (q - 4): the offset rides in the bit-2 operand
+            p = mfma_f16(U.A[mt][J], H, p);
 #pragma unroll
-        for (int i = 0; i < IMAX; ++i) {
-            if constexpr (FMT == MOE_FMT_Q2_B32)
-                acc[mt][i] = fmaf(dv, p[i], fmaf(mv, hs[i], acc[mt][i]));
-            else
-                acc[mt][i] = fmaf(dv, fmaf(-4.0f, hs[i], p[i]), acc[mt][i]);
+            for (int i = 0; i < IMAX; ++i) acc[mt][i] = fmaf(dv, p[i], acc[mt][i]);
+        } else {
+            const f32x4 hs = mfma_f16(U.A[mt][J], ones, zero);
+#pragma unroll
+            for (int i = 0; i < IMAX; ++i) acc[mt][i] = fmaf(dv, p[i], fmaf(mv, hs[i], acc[mt][i]));
         }
     }
 }
