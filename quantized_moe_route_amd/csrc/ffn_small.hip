@@ -279,7 +279,24 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
         gateup_load_codes(U[b], Wg, Wu, ubase + (u < KC ? u : KC - 1), lane);
     }
     // XL: x was staged and waited for by every wave before the barrier that
-    // published the group
+    // published the group.  The largest |x| of each token row (for h's
+    // scaling) comes from the staged rows once, wave wv taking rows wv,
+    // wv + NW, ..., while this wave's first weights are in flight: tracked
+    // per unit instead, it cost as many VALU instructions as the
+    // dequantisation.
+    if constexpr (XL) {
+        for (int t = wv; t < T; t += NW) {
+            uint32_t m = 0u;
+            for (int c = lane; c < cpr; c += 64)
+                m = max_mag_bf16x8(*reinterpret_cast<const u32x4 *>(xs + ((size_t)t * cpr + (c ^ (t & 7))) * 8), m);
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const uint32_t v = (uint32_t)__shfl_xor((int)m, o, 64);
+                m = v > m ? v : m;
+            }
+            if (lane == 0) redx[wv][t] = m;
+        }
+    }
     for (int u0 = wv; u0 < KC; u0 += NW * NB) {
         if (u0 != wv) {
             pg = gather(u0);
@@ -320,8 +337,10 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
                             xs + ((size_t)xr * cpr + (c ^ (xr & 7))) * 8);
                     }
                 }
+                if constexpr (!XL) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) xmax = max_mag_bf16x8(U[b].A[0][j], xmax);
+                    for (int j = 0; j < 4; ++j) xmax = max_mag_bf16x8(U[b].A[0][j], xmax);
+                }
                 gateup_block<FMT, 1, IMAX, 0>(U[b], ag, au);
                 gateup_block<FMT, 1, IMAX, 1>(U[b], ag, au);
                 gateup_block<FMT, 1, IMAX, 2>(U[b], ag, au);
@@ -334,8 +353,8 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
         red[wv][0][i][lane] = ag[0][i];
         red[wv][1][i][lane] = au[0][i];
     }
-    // the row's (lane rr's token) largest |x| over the four lane groups
-    {
+    // !XL: the row's (lane rr's token) largest |x| over the four lane groups
+    if constexpr (!XL) {
         uint32_t o = (uint32_t)__shfl_xor((int)xmax, 16, 64);
         xmax = o > xmax ? o : xmax;
         o = (uint32_t)__shfl_xor((int)xmax, 32, 64);
@@ -354,12 +373,12 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
         const int t = shared ? tk : tk / k;
         const int sl = (t >> 2) * 16 + rr, si = t & 3;
         float gs = red[0][0][si][sl], us = red[0][1][si][sl];
-        uint32_t mx = redx[0][t];
+        uint32_t mx = XL ? redx[t % NW][t] : redx[0][t];
 #pragma unroll
         for (int w2 = 1; w2 < NW; ++w2) {
             gs += red[w2][0][si][sl];
             us += red[w2][1][si][sl];
-            mx = redx[w2][t] > mx ? redx[w2][t] : mx;
+            if constexpr (!XL) mx = redx[w2][t] > mx ? redx[w2][t] : mx;
         }
         // h * 2^-2a = (g 2^-a) sigmoid(g) (u 2^-a): exact scalings
         const int a = exp_of_max_bits(mx);
