@@ -343,6 +343,16 @@ __device__ __forceinline__ unsigned long long group_max_u64(unsigned long long v
     if (L > 32) v = max_u64(v, __shfl_xor(v, 32, 64));
     return v;
 }
+// The same on 32-bit words.
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v, int L) {
+    if (L > 1) v = dpp_max_u32<0xB1, 0xF>(v);
+    if (L > 2) v = dpp_max_u32<0x4E, 0xF>(v);
+    if (L > 4) v = dpp_max_u32<0x141, 0xF>(v);
+    if (L > 8) v = dpp_max_u32<0x140, 0xF>(v);
+    if (L > 16) v = max(v, (uint32_t)__shfl_xor((int)v, 16, 64));
+    if (L > 32) v = max(v, (uint32_t)__shfl_xor((int)v, 32, 64));
+    return v;
+}
 __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int lane) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
@@ -351,50 +361,63 @@ __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v,
 
 // The k (<= 64) largest keys of a wave; lane j returns the j-th (0 in lanes
 // >= k).  Lane l holds v[i], the key of item l + 64 i (0 = no item; keys are
-// unique and nonzero) and the wave holds at least k items.  A lower bound
-// prunes first: the lanes form G >= k groups of L = 64 / G; the k-th largest
-// of the G group maxima is reached by at least k keys (those maxima), so
-// every key of the top k reaches it.  The keys at or above the bound -- a few
-// more than k for typical logits -- are compacted into LDS and ranked
-// exactly against each other.  Per-wave LDS scratch: M and sel of 64 keys
-// each, S of 64 P + 16 keys.
+// unique, and a present key's low word, the inverted expert, is nonzero) and
+// the wave holds at least k items.  A lower bound prunes first, on the value
+// words alone: the lanes form G >= k groups of L = 64 / G; the k-th largest
+// of the G group maxima (of value words), x, is reached by at least k keys,
+// so every key of the top k has a value word >= x.  The keys whose value word
+// reaches x -- a few more than k for typical logits -- are compacted into LDS
+// and ranked exactly (full keys) against each other.  Per-wave LDS scratch:
+// M of 64 words, sel of 64 keys, S of 64 P + 16 keys.
 template <int P>
-__device__ unsigned long long wave_select(const unsigned long long (&v)[P], int k, unsigned long long *M,
+__device__ unsigned long long wave_select(const unsigned long long (&v)[P], int k, uint32_t *M,
                                           unsigned long long *sel, unsigned long long *S) {
     const int l = __lane_id();
     int G = 1;
     while (G < k) G <<= 1;
     const int lg = 6 - __builtin_ctz(G);    // log2 of L = 64 / G
-    unsigned long long gm = v[0];
+    uint32_t hv[P];
 #pragma unroll
-    for (int i = 1; i < P; ++i) gm = max_u64(gm, v[i]);
-    gm = group_max_u64(gm, 1 << lg);
+    for (int i = 0; i < P; ++i) hv[i] = (uint32_t)(v[i] >> 32);
+    uint32_t gm = hv[0];
+#pragma unroll
+    for (int i = 1; i < P; ++i) gm = max(gm, hv[i]);
+    gm = group_max_u32(gm, 1 << lg);
     // the group maxima, padded with zeros to whole reads of 16
     const int Gp = (G + 15) & ~15;
-    if (l < Gp) M[l] = 0ull;
+    if (l < Gp) M[l] = 0u;
     if ((l & ((1 << lg) - 1)) == 0) M[l >> lg] = gm;
-    int rk = 0;
+    int rk = 0;   // group maxima above this lane's
     for (int j0 = 0; j0 < Gp; j0 += 16) {
-        unsigned long long o[16];
+        u32x4 o[4];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) o[j] = M[j0 + j];
+        for (int q = 0; q < 4; ++q) o[q] = *reinterpret_cast<const u32x4 *>(M + j0 + 4 * q);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) rk += o[j] > gm ? 1 : 0;
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) rk += o[q][c] > gm ? 1 : 0;
     }
-    // the bound: the group maximum of rank k - 1 (with fewer than k nonzero
-    // maxima every key stays)
-    const unsigned long long hit = __ballot(rk == k - 1 && gm != 0ull);
-    const unsigned long long th = hit ? readlane_u64(gm, __builtin_ctzll(hit)) : 1ull;
+    // x: the least group maximum with fewer than k maxima above it (0 when
+    // fewer than k groups hold a key: then every key stays)
+    const uint32_t x = wave_min_u32(rk < k ? gm : 0xFFFFFFFFu);
+    bool kp[P];
+    if (x != 0u) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) kp[i] = hv[i] >= x;
+    } else {
+#pragma unroll
+        for (int i = 0; i < P; ++i) kp[i] = v[i] != 0ull;
+    }
     // survivors, compacted in lane order
     int c = 0;
 #pragma unroll
-    for (int i = 0; i < P; ++i) c += v[i] >= th ? 1 : 0;
+    for (int i = 0; i < P; ++i) c += kp[i] ? 1 : 0;
     const int incl = wave_scan_dpp(c);
     const int n = __builtin_amdgcn_readlane(incl, 63);
     int pos = incl - c;
 #pragma unroll
     for (int i = 0; i < P; ++i)
-        if (v[i] >= th) S[pos++] = v[i];
+        if (kp[i]) S[pos++] = v[i];
     if (l < 16) S[n + l] = 0ull;   // zero keys rank below every key
     // exact ranks: 16 LDS reads in flight per step
     for (int i0 = 0; i0 < n; i0 += 64) {
@@ -416,9 +439,10 @@ __device__ unsigned long long wave_select(const unsigned long long (&v)[P], int 
 // One token's selection from its LDS key row (row[e] for e < 64 P, zero past
 // E): ids, weights (softmax over the k picks) and, if asked, the picks in
 // ids_lds for the listing.  The row is reused as the survivors' scratch.
+// Lane j < k returns pick j's expert, the other lanes -1.
 template <int P>
-__device__ void select_token(unsigned long long *row, int k, unsigned long long *M, unsigned long long *sel,
-                             int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_lds) {
+__device__ int select_token(unsigned long long *row, int k, uint32_t *M, unsigned long long *sel,
+                            int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_lds) {
     const int l = __lane_id();
     unsigned long long v[P];
 #pragma unroll
@@ -428,12 +452,14 @@ __device__ void select_token(unsigned long long *row, int k, unsigned long long 
     const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), 0));
     const float ev = l < k ? expf(lv - l0) : 0.0f;
     const float inv = 1.0f / wave_sum(ev);
+    int e = -1;
     if (l < k) {
-        const int e = key_expert(my);
+        e = key_expert(my);
         ids[l] = e;
         w[l] = ev * inv;
         if (ids_lds) ids_lds[l] = e;
     }
+    return e;
 }
 
 // The listing of moe_dispatch from the batch's picks (ids_s [T][k] in LDS):
@@ -489,47 +515,39 @@ __device__ void list_pairs(const int32_t *ids_s, int T, int E, int k, int tail_f
     }
 }
 
-// The listing for a single token (pairs p = j): the kept picks (ranks j <
-// tail_from) sorted by expert; pair j's position is the number of kept picks
-// with a lower expert (a token picks an expert once) and offsets[e] counts
-// the kept picks below e.  All 256 threads; ids_s [>= 64] in LDS, k <= 64,
-// E <= 1024.  Counts stay in registers until the end.
-__device__ void list_pairs_one(const int32_t *ids_s, int E, int k, int tail_from, int32_t *__restrict__ offsets,
-                               int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pair_pos) {
-    const int tid = threadIdx.x;
+// The listing for a single token (pairs p = j) from its kept picks (ranks j
+// < tail_from) as bits of an expert mask, bit e & 31 of word e >> 5 (E <=
+// 1024): pair j's position and offsets[e] both count the kept picks with a
+// lower expert (a token picks an expert once).  mark_one, by the selecting
+// wave (lane j < k holds pick j's expert): sets the bits in words bits[0 ..
+// 31] (cleared beforehand; bits[32] stays zero), stores each word's exclusive
+// prefix count in cnt[0 .. 32] and lists the pairs.  After a barrier,
+// offsets_one fills offsets[0 .. E] from the words (all threads).
+__device__ void mark_one(int e_pick, int k, int tail_from, uint32_t *bits, int32_t *cnt,
+                         int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pair_pos) {
+    const int l = __lane_id();
     const int kk = tail_from < k ? tail_from : k;   // picks 0 .. kk-1 are kept
-    const int R = E / 256 + 1;                      // offsets slots per thread: e = tid + 256 r <= E
-    const int me = ids_s[tid & 63];
-    int n[5] = {0, 0, 0, 0, 0};
-    int pos = 0;
-    for (int j0 = 0; j0 < kk; j0 += 16) {
-        // 16 picks at a time: unconditional LDS reads (ids_s holds 64),
-        // picks past kk count as no expert
-        int id[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int r = ids_s[j0 + j];
-            id[j] = j0 + j < kk ? r : 0x7fffffff;
-        }
-#pragma unroll
-        for (int r = 0; r < 5; ++r) {
-            if (r < R) {
-                const int e = tid + 256 * r;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) n[r] += id[j] < e ? 1 : 0;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) pos += id[j] < me ? 1 : 0;
+    if (l < kk) atomicOr(&bits[e_pick >> 5], 1u << (e_pick & 31));
+    // the same wave reads the words back: its LDS operations run in order
+    const uint32_t m = l < 32 ? bits[l] : 0u;
+    const int c = __popc(m);
+    const int below = wave_scan_dpp(c) - c;
+    if (l <= 32) cnt[l] = below;
+    const int wd = l < kk ? e_pick >> 5 : 0;
+    const uint32_t mw = (uint32_t)__shfl((int)m, wd, 64);
+    const int bw = __shfl(below, wd, 64);
+    if (l < kk) {
+        const int pos = bw + __popc(mw & ((1u << (e_pick & 31)) - 1u));
+        pair_pos[l] = pos;
+        sorted_pair[pos] = l;
+    } else if (l < k) {
+        pair_pos[l] = -1;
     }
-#pragma unroll
-    for (int r = 0; r < 5; ++r)
-        if (r < R && tid + 256 * r <= E) offsets[tid + 256 * r] = n[r];
-    if (tid < kk) {
-        pair_pos[tid] = pos;
-        sorted_pair[pos] = tid;
-    } else if (tid < k) {
-        pair_pos[tid] = -1;
+}
+__device__ void offsets_one(const uint32_t *bits, const int32_t *cnt, int E, int32_t *__restrict__ offsets) {
+    for (int e = threadIdx.x; e <= E; e += 256) {
+        const int wd = e >> 5;
+        offsets[e] = cnt[wd] + __popc(bits[wd] & ((1u << (e & 31)) - 1u));
     }
 }
 
@@ -665,12 +683,15 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     }
     __syncthreads();
     if (!tile_flag) return;
+    const bool listing = offsets != nullptr;
+    // one token: the listing's expert mask, cleared before the first barrier
+    // below (the selecting wave sets it)
+    if (listing && Tt == 1 && tid <= 32) emask[tid] = 0u;
     // The tile's last workgroup resets the tile's counters at its very end: a
     // store issued before its loads would delay them (the memory counter
     // retires in order).
 
     // ------------------------------------------------------------- phase B
-    const bool listing = offsets != nullptr;
     const int E4 = (E + 3) >> 2;
     const int Pk = E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16;   // keys per lane
     const __amdgpu_buffer_rsrc_t prs =
@@ -767,15 +788,18 @@ __global__ __launch_bounds__(256) void route_small_kernel(
             int32_t *const id_t = ids + (size_t)(t0 + t) * k;
             float *const w_t = w + (size_t)(t0 + t) * k;
             if (k <= kWaveTopkMaxK) {
-                unsigned long long *M = wscr[wv], *sel = wscr[wv] + 64;
-                int32_t *il = listing ? sel_ids + t * k : nullptr;
+                uint32_t *M = reinterpret_cast<uint32_t *>(wscr[wv]);
+                unsigned long long *sel = wscr[wv] + 64;
+                int32_t *il = listing && Tt > 1 ? sel_ids + t * k : nullptr;
+                int e_pick;
                 switch (Pk) {
-                case 1: select_token<1>(keys[wv], k, M, sel, id_t, w_t, il); break;
-                case 2: select_token<2>(keys[wv], k, M, sel, id_t, w_t, il); break;
-                case 4: select_token<4>(keys[wv], k, M, sel, id_t, w_t, il); break;
-                case 8: select_token<8>(keys[wv], k, M, sel, id_t, w_t, il); break;
-                default: select_token<16>(keys[wv], k, M, sel, id_t, w_t, il); break;
+                case 1: e_pick = select_token<1>(keys[wv], k, M, sel, id_t, w_t, il); break;
+                case 2: e_pick = select_token<2>(keys[wv], k, M, sel, id_t, w_t, il); break;
+                case 4: e_pick = select_token<4>(keys[wv], k, M, sel, id_t, w_t, il); break;
+                case 8: e_pick = select_token<8>(keys[wv], k, M, sel, id_t, w_t, il); break;
+                default: e_pick = select_token<16>(keys[wv], k, M, sel, id_t, w_t, il); break;
                 }
+                if (listing && Tt == 1) mark_one(e_pick, k, tail_from, emask, eoff, sorted_pair, pair_pos);
             } else {
                 // large k: the serial wave top-k on the logits just written
                 // (device-scope loads), scratch in this wave's key row
@@ -788,7 +812,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     }
     if (listing) {
         if (Tt == 1)
-            list_pairs_one(sel_ids, E, k, tail_from, offsets, sorted_pair, pair_pos);
+            offsets_one(emask, eoff, E, offsets);
         else
             list_pairs(sel_ids, Tt, E, k, tail_from, emask, eoff, wtot, offsets, sorted_pair, pair_pos);
     }

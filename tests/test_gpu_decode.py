@@ -169,6 +169,40 @@ def test_route_small_path_shapes(q, T, E, k, d):
         assert np.max(np.abs(wt.cpu().numpy() - w_ref)) <= 1e-6
 
 
+@pytest.mark.parametrize("T,E,k,d", [(1, 512, 10, 2048), (4, 512, 10, 512), (8, 1024, 64, 256),
+                                     (1, 64, 40, 128), (1, 1024, 64, 128)])
+def test_route_small_exact_ties(q, T, E, k, d):
+    """One-launch router and listing on logits with exact ties: the router
+    columns are 8 distinct ones repeated, so runs of experts share a logit bit
+    for bit and the pruning bound ties across groups.  ids (lower expert first
+    on a tie), weights and the listing against the oracle on the GPU's logits."""
+    rng = np.random.default_rng(7 * T + E + k)
+    x = synth._f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    cols = rng.integers(0, 8, E)
+    wr = np.ascontiguousarray((rng.standard_normal((d, 8)) / np.sqrt(d)).astype(np.float32)[:, cols])
+    ws_bytes = q.moe_workspace_size(d, 128, E, T, k)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    lg = torch.empty(T, E, device="cuda")
+    ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    wt = torch.empty(T, k, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    c = lambda a: torch.from_numpy(a).cuda()
+    q.moe_route_dispatch(c(x.view(np.int16)), c(wr), None, lg, T, d, E, k, ids, wt, off, sp, pp, ws, ws_bytes)
+    torch.cuda.synchronize()
+    lg_h = lg.cpu().numpy()
+    for j in range(8):   # equal columns give equal logits
+        same = lg_h[:, cols == j]
+        assert same.size == 0 or np.array_equal(same, np.repeat(same[:, :1], same.shape[1], axis=1))
+    ids_ref, w_ref = oracle.topk_softmax(lg_h, k)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.max(np.abs(wt.cpu().numpy() - w_ref)) <= 1e-6
+    off_ref, sp_ref, pp_ref = oracle.dispatch(ids_ref, E)
+    assert np.array_equal(off.cpu().numpy(), off_ref) and np.array_equal(sp.cpu().numpy(), sp_ref)
+    assert np.array_equal(pp.cpu().numpy(), pp_ref)
+
+
 @pytest.mark.parametrize("T,E,k,d", [(300, 300, 40, 384), (257, 1000, 70, 256), (1000, 64, 8, 128),
                                      (513, 17, 3, 2048), (129, 512, 10, 2048)])
 def test_route_gemm_path_shapes(q, T, E, k, d):
