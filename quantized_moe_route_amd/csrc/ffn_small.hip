@@ -900,12 +900,28 @@ __global__ __launch_bounds__(64 * 16) void down_tile_kernel(
         // only LDS traffic to wait for: no global store is outstanding
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
         wg_barrier();
+        // shared term first, then j order, one fma per pair (moe_combine's
+        // order); the pair positions and weights of a batch of 8 picks, then
+        // their y values, are read before the first fma (a read, then a
+        // dependent read, per pick cost two LDS round trips each)
+        constexpr int B = 8;
         for (int i = threadIdx.x; i < T * 16; i += blockDim.x) {
             const int t = i >> 4, c = i & 15;
             float acc = ylds[(P + t) * 16 + c];
-            for (int j = 0; j < k; ++j) {
-                const int p = pp_s[t * k + j];
-                if (p >= 0) acc = fmaf(w_s[t * k + j], ylds[p * 16 + c], acc);
+            for (int j0 = 0; j0 < k; j0 += B) {
+                int p[B];
+                float wj[B], v[B];
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const int j = j0 + b < k ? j0 + b : k - 1;   // clamped: read, not used
+                    p[b] = pp_s[t * k + j];
+                    wj[b] = w_s[t * k + j];
+                }
+#pragma unroll
+                for (int b = 0; b < B; ++b) v[b] = ylds[(p[b] >= 0 ? p[b] : 0) * 16 + c];
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+                    if (j0 + b < k && p[b] >= 0) acc = fmaf(wj[b], v[b], acc);
             }
             cb.out[(size_t)t * d + ot * 16 + c] = acc;
         }
@@ -950,6 +966,25 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
     // reads each x byte from L2 once per workgroup instead of once per wave
     // and lane group
     const size_t xbytes = (size_t)T * d * 2;
+    // one token (and k <= 16, d_ff <= 768): the down projection runs per
+    // 16-column output tile (down_tile_kernel), one wave per group.  Without
+    // the merge, eight or more group slots are split over two workgroups per
+    // tile, so all CUs take part (FFN 13.7 -> 13.0 us at T = 1, top-10);
+    // with it, one workgroup holds every group of its tile and merges in LDS
+    // (a merge across two workgroups, through device-scope float adds into
+    // a cleared out, took the fused call from 14.7 to 21 us)
+    const bool tile_path = MTD == 1 && T == 1 && k <= kTileMaxK && f <= 128 * kTileUnits && f % 128 == 0;
+    int CH = 0, nchunks = 0;
+    unsigned tile_lds = 0;
+    if (tile_path) {
+        CH = !cb.out && slots >= 8 ? (slots + 1) / 2 : slots;
+        CH = CH < 16 ? CH : 16;
+        const int region = tile_region_halves<FMT, IMAX>(f) * 2;   // bytes per wave
+        const int lds_ch = 49152 / region;                          // waves whose regions fit 48 KiB
+        CH = CH < lds_ch ? CH : lds_ch;
+        nchunks = (slots + CH - 1) / CH;
+        tile_lds = (unsigned)(CH * region);
+    }
     if (IMAX > 2 && T <= 4 && xbytes <= kXsMaxBytes)
         // three or four tokens: batches of two units per wave, so that five
         // workgroups fit a CU (96 VGPRs, 28 KiB of LDS) and every real
@@ -975,17 +1010,11 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
         hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, false, 1>), dim3(f / 16, slots),
                            dim3(64 * NWG), 0, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up), x,
                            T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, hx, table, slot0);
-    // one token (and k <= 16, d_ff <= 768): all groups of an output tile in
-    // one workgroup, one wave per group (measured at T = 4 with 41 groups in
-    // chunks of 4 it lost to one workgroup per group and tile)
-    if (MTD == 1 && T == 1 && k <= kTileMaxK && f <= 128 * kTileUnits && f % 128 == 0) {
+    // one token: the tile kernel (measured at T = 4 with 41 groups in chunks
+    // of 4 it lost to one workgroup per group and tile)
+    if (tile_path) {
         constexpr int RMAX = IMAX;
-        int CH = slots < 16 ? slots : 16;
-        const int region = tile_region_halves<FMT, RMAX>(f) * 2;   // bytes per wave
-        const int lds_ch = 49152 / region;                          // waves whose regions fit 48 KiB
-        CH = CH < lds_ch ? CH : lds_ch;
-        const int nchunks = (slots + CH - 1) / CH;
-        const unsigned lds = (unsigned)(CH * region);
+        const unsigned lds = tile_lds;
         if (cb.out)
             hipLaunchKernelGGL((down_tile_kernel<FMT, RMAX, true>), dim3(d / 16, nchunks), dim3(64 * CH), lds, s,
                                qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f, table, slots, nchunks, y_pairs,
