@@ -155,14 +155,10 @@ __device__ __forceinline__ void wave_topk_any(const float *lg, int E, int k, int
         wave_topk<16, DEV_LOADS>(lg, E, k, ids, w, sel, seli);
 }
 
-// ------------------------------------------- top-k on ordered keys (wave)
-// For k <= 64, one wave per token.  Each logit becomes an unsigned key that
-// orders like the float (sign-magnitude mapped to offset binary; -0.0 read as
-// +0.0); 0 marks an empty or already taken entry, which no finite logit maps
-// to.  Lane l owns experts l, l + 64, ...; each round takes the wave maximum
-// key with six DPP max steps, finds the lanes holding it by ballot and, only
-// on a tie, the lowest expert among them by a second reduction.  The owner
-// clears the entry; lane j keeps the j-th selection in registers.
+// ------------------------------------------- order-preserving keys
+// Each logit becomes an unsigned key that orders like the float
+// (sign-magnitude mapped to offset binary; -0.0 read as +0.0); 0 marks an
+// empty entry, which no finite logit maps to.
 __device__ __forceinline__ uint32_t ord_key(float v) {
     uint32_t f = __float_as_uint(v);
     if (f == 0x80000000u) f = 0u;
@@ -183,15 +179,6 @@ __device__ __forceinline__ uint32_t dpp_min_u32(uint32_t v) {
     const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, CTRL, ROW_MASK, 0xF, false);
     return o < v ? o : v;
 }
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = dpp_max_u32<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
-    v = dpp_max_u32<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
-    v = dpp_max_u32<0x141, 0xF>(v);   // row_half_mirror
-    v = dpp_max_u32<0x140, 0xF>(v);   // row_mirror
-    v = dpp_max_u32<0x142, 0xA>(v);   // row_bcast:15 -> rows 1, 3
-    v = dpp_max_u32<0x143, 0xC>(v);   // row_bcast:31 -> rows 2, 3
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
     v = dpp_min_u32<0xB1, 0xF>(v);
     v = dpp_min_u32<0x4E, 0xF>(v);
@@ -200,86 +187,6 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
     v = dpp_min_u32<0x142, 0xA>(v);
     v = dpp_min_u32<0x143, 0xC>(v);
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-template <int PER>
-__device__ void wave_topk_ord(const float *__restrict__ lg, int E, int k, int32_t *__restrict__ ids,
-                              float *__restrict__ w, int32_t *ids_lds = nullptr) {
-    const int l = __lane_id();
-    uint32_t key[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int e = l + 64 * i;
-        const float v = lg[e < E ? e : 0];
-        key[i] = e < E ? ord_key(v) : 0u;
-    }
-    // lane's best: largest key, lowest slot among equals (a pairwise tree,
-    // the right half taken only when strictly larger)
-    auto local_best = [&](uint32_t &bk, int &bs) {
-        uint32_t kk[PER];
-        int ss[PER];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            kk[i] = key[i];
-            ss[i] = i;
-        }
-#pragma unroll
-        for (int h = 1; h < PER; h *= 2)
-#pragma unroll
-            for (int i = 0; i + h < PER; i += 2 * h) {
-                const bool take = kk[i + h] > kk[i];
-                kk[i] = take ? kk[i + h] : kk[i];
-                ss[i] = take ? ss[i + h] : ss[i];
-            }
-        bk = kk[0];
-        bs = ss[0];
-    };
-    uint32_t bk;
-    int bs;
-    local_best(bk, bs);
-    uint32_t my_key = 0u;   // lane j: the j-th pick
-    int my_id = 0;
-    for (int j = 0; j < k; ++j) {
-        const uint32_t m = wave_max_u32(bk);
-        const unsigned long long hold = __ballot(bk == m);
-        int e;
-        if (__builtin_expect(__popcll(hold) != 1, 0))
-            e = (int)wave_min_u32(bk == m ? (uint32_t)(l + 64 * bs) : 0xffffffffu);
-        else {
-            const int owner = __builtin_ctzll(hold);
-            e = owner + 64 * __builtin_amdgcn_readlane(bs, owner);
-        }
-        my_key = l == j ? m : my_key;
-        my_id = l == j ? e : my_id;
-        // the owner clears its pick; every lane rescans (same issue cost as
-        // the owner alone, and no branch)
-        const int slot = wave_uniform(e >> 6);
-        key[slot] = l == (e & 63) ? 0u : key[slot];
-        local_best(bk, bs);
-    }
-    const float l0 = ord_value((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
-    const float ev = l < k ? expf(ord_value(my_key) - l0) : 0.0f;
-    const float inv = 1.0f / wave_sum(ev);
-    if (l < k) {
-        w[l] = ev * inv;
-        ids[l] = my_id;
-        if (ids_lds) ids_lds[l] = my_id;
-    }
-}
-
-
-__device__ __forceinline__ void wave_topk_ord_any(const float *lg, int E, int k, int32_t *ids, float *w,
-                                                  int32_t *ids_lds = nullptr) {
-    if (E <= 64)
-        wave_topk_ord<1>(lg, E, k, ids, w, ids_lds);
-    else if (E <= 128)
-        wave_topk_ord<2>(lg, E, k, ids, w, ids_lds);
-    else if (E <= 256)
-        wave_topk_ord<4>(lg, E, k, ids, w, ids_lds);
-    else if (E <= 512)
-        wave_topk_ord<8>(lg, E, k, ids, w, ids_lds);
-    else
-        wave_topk_ord<16>(lg, E, k, ids, w, ids_lds);
 }
 
 // ------------------------------------------------------- small T: one launch
@@ -870,17 +777,8 @@ hipError_t launch_route_small(const uint16_t *x, const float *wr, const float *b
 }
 
 // ------------------------------------------------------------ top-k kernel
-// Logits given: one wave per token, four tokens per workgroup.  k <= 64 keeps
-// every selection in registers; larger k selects serially through LDS.
-__global__ __launch_bounds__(256) void topk_wave_kernel(const float *__restrict__ logits, int T,
-                                                        int E, int k, int32_t *__restrict__ ids,
-                                                        float *__restrict__ w) {
-    const int wv = wave_uniform(threadIdx.x >> 6);
-    const int t = blockIdx.x * 4 + wv;
-    if (t >= T) return;
-    wave_topk_ord_any(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
-}
-
+// Logits given, k > 64: one wave per token, four tokens per workgroup, the
+// selection serial through LDS.
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
                                                    int k, int32_t *__restrict__ ids,
                                                    float *__restrict__ w) {
@@ -893,12 +791,52 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
                          sel[wv], seli[wv]);
 }
 
+// Logits given, k <= 64: one wave per token, four tokens per workgroup, the
+// pruned selection of the one-launch router (wave_select: a lower bound from
+// group maxima of the value words, then exact ranks of the keys above it)
+// on the token's keys staged in LDS: a few LDS round trips per token instead
+// of k serial max-and-clear rounds over the wave.
+template <int P>
+__global__ __launch_bounds__(256) void topk_sel_kernel(const float *__restrict__ logits, int T, int E, int k,
+                                                       int32_t *__restrict__ ids, float *__restrict__ w) {
+    __shared__ __attribute__((aligned(16))) unsigned long long rows[4][64 * P + 16];
+    __shared__ __attribute__((aligned(16))) unsigned long long scr[4][128];   // per wave: M, sel
+    const int wv = wave_uniform(threadIdx.x >> 6), l = __lane_id();
+    const int t = blockIdx.x * 4 + wv;
+    if (t >= T) return;
+    const float *lg = logits + (size_t)t * E;
+    float v[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int e = l + 64 * i;
+        v[i] = lg[e < E ? e : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int e = l + 64 * i;
+        rows[wv][e] = e < E ? route_key(v[i], e) : 0ull;
+    }
+    // each lane reads back only what it wrote; the selection's exchanges are
+    // within the wave, whose LDS operations complete in order
+    select_token<P>(rows[wv], k, reinterpret_cast<uint32_t *>(scr[wv]), scr[wv] + 64, ids + (size_t)t * k,
+                    w + (size_t)t * k, nullptr);
+}
+
 hipError_t launch_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w,
                        hipStream_t s) {
-    if (k <= kWaveTopkMaxK)
-        hipLaunchKernelGGL(topk_wave_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k,
-                           ids, w);
-    else
+    const dim3 grid((T + 3) / 4), blk(256);
+    if (k <= kWaveTopkMaxK) {
+        if (E <= 64)
+            hipLaunchKernelGGL(topk_sel_kernel<1>, grid, blk, 0, s, logits, T, E, k, ids, w);
+        else if (E <= 128)
+            hipLaunchKernelGGL(topk_sel_kernel<2>, grid, blk, 0, s, logits, T, E, k, ids, w);
+        else if (E <= 256)
+            hipLaunchKernelGGL(topk_sel_kernel<4>, grid, blk, 0, s, logits, T, E, k, ids, w);
+        else if (E <= 512)
+            hipLaunchKernelGGL(topk_sel_kernel<8>, grid, blk, 0, s, logits, T, E, k, ids, w);
+        else
+            hipLaunchKernelGGL(topk_sel_kernel<16>, grid, blk, 0, s, logits, T, E, k, ids, w);
+    } else
         hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
     return hipGetLastError();
 }
