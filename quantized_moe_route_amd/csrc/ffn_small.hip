@@ -433,6 +433,32 @@ __device__ __forceinline__ void down_block(const DownUnit<FMT, MT> &U, f32x4 *ac
     }
 }
 
+// SPREAD form (at most 4 group rows): group row r's h_hi fills matrix rows
+// 4r, 4r + 1 and its h_lo rows 4r + 2, 4r + 3, so lane group r holds both in
+// result registers 0 and 2: two epilogue FMAs per block (Q2: four) where the
+// stacked form (hi rows 0-7 over lo rows 8-15) ran one per row on every lane.
+// The same products and sums per row: y is bit-identical to the stacked
+// form's.
+template <int FMT, int J>
+__device__ __forceinline__ void down_block_spread(const DownUnit<FMT, 1> &U, float (&acc)[2]) {
+    const u32x4 ones = {kOneF16x2, kOneF16x2, kOneF16x2, kOneF16x2};
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    u32x4 B, H;
+    block_operands<J, true, FMT>(U.lw[J >> 1], U.hw, B, H);
+    const float dv = half_of(U.sw, J);
+    f32x4 p = mfma_f16(U.A[0][J], B, zero);
+    if constexpr (FMT == MOE_FMT_Q3_B32) {
+        p = mfma_f16(U.A[0][J], H, p);
+        acc[0] = fmaf(dv, p[0], acc[0]);
+        acc[1] = fmaf(dv, p[2], acc[1]);
+    } else {
+        const float mv = half_of(U.mw, J);
+        const f32x4 hs = mfma_f16(U.A[0][J], ones, zero);
+        acc[0] = fmaf(dv, p[0], fmaf(mv, hs[0], acc[0]));
+        acc[1] = fmaf(dv, p[2], fmaf(mv, hs[2], acc[1]));
+    }
+}
+
 // Down-projection weights of one batch of a wave's units (units u0 + NW b),
 // loadable before h is needed: the weights do not depend on it.
 template <int FMT, int MT, int NW>
@@ -485,13 +511,14 @@ __device__ __forceinline__ void down_load_w(DownW<FMT, MT, NW> &Wt, const QMatDe
 // HL: the group's h rows (hi and lo, at most 8 each) are staged in LDS by
 // global-to-LDS copies: stored row S = (lo ? nrows : 0) + r, chunk c of it at
 // S * (f / 8) + (c ^ (S & 7)); the A operands are read from there.
-template <int FMT, int MT, int IMAX, int NW, bool DEV, bool HL>
+template <int FMT, int MT, int IMAX, int NW, bool DEV, bool HL, bool SPREAD = false, int RI = SPREAD ? 2 : IMAX>
 __device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev &down, const QMatDev &sdown,
                                           const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
                                           const int32_t *__restrict__ hx, int d, int f, const Group &grp, int ot,
-                                          int wq, float (*red)[MT][IMAX][64], float *__restrict__ y_pairs,
+                                          int wq, float (*red)[MT][RI][64], float *__restrict__ y_pairs,
                                           float *__restrict__ y_shared, uint16_t *hs, u32x4 *pieces) {
     static_assert(!HL || MT == 1, "staged h: groups of at most 8 rows");
+    static_assert(!SPREAD || MT == 1, "spread rows: groups of at most 4 rows");
     const int lane = __lane_id();
     const int gq = lane >> 4, rr = lane & 15;
     const int KC = f / 128;
@@ -503,22 +530,25 @@ __device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev 
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < IMAX; ++i) {
-            int r = mt * 8 + gq * 4 + i;
+            int r = SPREAD ? gq : mt * 8 + gq * 4 + i;
             r = r < nrows ? r : nrows - 1;
             ya[mt][i] = wq == 0 ? 2 * hx[grp.hrow0 + r] : 0;
         }
     const int cpr = f / 8;
     const uint16_t *hrow[MT];
+    // this lane's A row: group row ar, its h_lo half if alo
+    const int ar = SPREAD ? rr >> 2 : rr & 7;
+    const bool alo = SPREAD ? (rr & 3) >= 2 : rr >= 8;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        int r = mt * 8 + (rr & 7);
+        int r = mt * 8 + ar;
         r = r < nrows ? r : nrows - 1;
-        hrow[mt] = (rr < 8 ? h_hi : h_lo) + (size_t)(grp.hrow0 + r) * f;
+        hrow[mt] = (alo ? h_lo : h_hi) + (size_t)(grp.hrow0 + r) * f;
     }
     int srow = 0;   // HL: this lane's stored row
     if constexpr (HL) {
-        const int r = (rr & 7) < nrows ? (rr & 7) : nrows - 1;
-        srow = (rr < 8 ? 0 : nrows) + r;
+        const int r = ar < nrows ? ar : nrows - 1;
+        srow = (alo ? nrows : 0) + r;
         const int nch = 2 * nrows * cpr;
         for (int q = wq; q * 64 < nch; q += NW) {
             const int L = q * 64 + lane;
@@ -535,6 +565,7 @@ __device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev 
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float acs[2] = {0.f, 0.f};   // SPREAD: this lane's row, h_hi and h_lo halves
     constexpr int NB = DownW<FMT, MT, NW>::NB;
     for (int u0 = wq; u0 < KC; u0 += NW * NB) {
         if (u0 != wq) down_load_w<FMT, MT, NW>(Wt, down, sdown, d, f, grp, ot, u0);
@@ -568,10 +599,17 @@ __device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev 
                         U[b].A[0][j] = *reinterpret_cast<const u32x4 *>(hs + ((size_t)srow * cpr + (c ^ (srow & 7))) * 8);
                     }
                 }
-                down_block<FMT, MT, IMAX, 0>(U[b], acc);
-                down_block<FMT, MT, IMAX, 1>(U[b], acc);
-                down_block<FMT, MT, IMAX, 2>(U[b], acc);
-                down_block<FMT, MT, IMAX, 3>(U[b], acc);
+                if constexpr (SPREAD) {
+                    down_block_spread<FMT, 0>(U[b], acs);
+                    down_block_spread<FMT, 1>(U[b], acs);
+                    down_block_spread<FMT, 2>(U[b], acs);
+                    down_block_spread<FMT, 3>(U[b], acs);
+                } else {
+                    down_block<FMT, MT, IMAX, 0>(U[b], acc);
+                    down_block<FMT, MT, IMAX, 1>(U[b], acc);
+                    down_block<FMT, MT, IMAX, 2>(U[b], acc);
+                    down_block<FMT, MT, IMAX, 3>(U[b], acc);
+                }
             }
         }
     }
@@ -579,21 +617,38 @@ __device__ __forceinline__ void down_task(DownW<FMT, MT, NW> &Wt, const QMatDev 
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int i = 0; i < IMAX; ++i) red[wq][mt][i][lane] = acc[mt][i];
+            for (int i = 0; i < RI; ++i) red[wq][mt][i][lane] = SPREAD ? acs[i] : acc[mt][i];
         __syncthreads();
         if (wq == 0) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int i = 0; i < IMAX; ++i) {
+                for (int i = 0; i < RI; ++i) {
                     float v = red[0][mt][i][lane];
 #pragma unroll
                     for (int w2 = 1; w2 < NW; ++w2) v += red[w2][mt][i][lane];
-                    acc[mt][i] = v;
+                    if constexpr (SPREAD)
+                        acs[i] = v;
+                    else
+                        acc[mt][i] = v;
                 }
         }
     }
     if (wq != 0) return;
+    if constexpr (SPREAD) {
+        // lane group gq: group row gq, h_hi + h_lo in one lane
+        const int r = gq;
+        if (r < nrows) {
+            const float y = ldexpf(acs[0] + acs[1], ya[0][0]);
+            const int o = ot * 16 + rr;
+            float *dst = grp.expert < 0 ? y_shared + (size_t)r * d + o : y_pairs + (size_t)(grp.row0 + r) * d + o;
+            if constexpr (DEV)
+                store_dev(dst, y);   // read by another workgroup of this launch
+            else
+                *dst = y;
+        }
+        return;
+    }
     // hi (rows 0..7, lanes 0..31) + lo (rows 8..15, lanes 32..63)
     const int o = ot * 16 + rr;
 #pragma unroll
@@ -726,12 +781,12 @@ void gateup_small_kernel(
 
 // grid: (d_model/16 row tiles, group slots); NW waves split K = d_ff.  FUSE:
 // the last workgroup of each row tile also computes the tile of out.
-template <int FMT, int MT, int IMAX, int NW, bool FUSE, bool HL>
+template <int FMT, int MT, int IMAX, int NW, bool FUSE, bool HL, bool SPREAD = false>
 __global__ __launch_bounds__(64 * NW) void down_small_kernel(
     QMatDev down, QMatDev sdown, const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
     const int32_t *__restrict__ hx, int d, int f, const Group *__restrict__ table, float *__restrict__ y_pairs,
     float *__restrict__ y_shared, CombineArgs cb) {
-    __shared__ float red[NW][MT][IMAX][64];
+    __shared__ float red[NW][MT][SPREAD ? 2 : IMAX][64];
     __shared__ u32x4 pieces[NW][64 * PieceGather<kDownBatch * 2>::N];   // per wave: a batch's scale pieces
     extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];   // HL: the group's h rows
     const Group grp = table[blockIdx.y];   // written by the gate/up kernel
@@ -739,7 +794,7 @@ __global__ __launch_bounds__(64 * NW) void down_small_kernel(
         const int wq = wave_uniform(threadIdx.x >> 6);
         DownW<FMT, MT, NW> Wt;
         down_load_w<FMT, MT, NW>(Wt, down, sdown, d, f, grp, blockIdx.x, wq);
-        down_task<FMT, MT, IMAX, NW, FUSE, HL>(Wt, down, sdown, h_hi, h_lo, hx, d, f, grp, blockIdx.x, wq, red,
+        down_task<FMT, MT, IMAX, NW, FUSE, HL, SPREAD>(Wt, down, sdown, h_hi, h_lo, hx, d, f, grp, blockIdx.x, wq, red,
                                                y_pairs, y_shared, xs_dyn, pieces[wq]);
     }
     if constexpr (FUSE) combine_tile(cb, y_pairs, y_shared, d, blockIdx.x, gridDim.y);
@@ -1045,22 +1100,33 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
     const size_t hbytes = (size_t)2 * T * f * 2;
     constexpr bool HLOK = MTD == 1;
     const bool hl = HLOK && T <= 4 && hbytes <= kXsMaxBytes;
-    if (cb.out && hl)
-        hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, true, HLOK>), dim3(d / 16, slots),
-                           dim3(64 * NWD), (unsigned)hbytes, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f,
-                           table, y_pairs, y_shared, cb);
-    else if (cb.out)
-        hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, true, false>), dim3(d / 16, slots),
-                           dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f, table,
-                           y_pairs, y_shared, cb);
-    else if (hl)
-        hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, false, HLOK>), dim3(d / 16, slots),
-                           dim3(64 * NWD), (unsigned)hbytes, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f,
-                           table, y_pairs, y_shared, cb);
-    else
-        hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, false, false>), dim3(d / 16, slots),
-                           dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f, table,
-                           y_pairs, y_shared, cb);
+    // up to 4 tokens (groups of at most 4 rows): the spread row form
+    auto launch_down = [&](auto spread_c) {
+        constexpr bool SP = decltype(spread_c)::value;
+        if (cb.out && hl)
+            hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, true, HLOK, SP>), dim3(d / 16, slots),
+                               dim3(64 * NWD), (unsigned)hbytes, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f,
+                               table, y_pairs, y_shared, cb);
+        else if (cb.out)
+            hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, true, false, SP>), dim3(d / 16, slots),
+                               dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f, table,
+                               y_pairs, y_shared, cb);
+        else if (hl)
+            hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, false, HLOK, SP>), dim3(d / 16, slots),
+                               dim3(64 * NWD), (unsigned)hbytes, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f,
+                               table, y_pairs, y_shared, cb);
+        else
+            hipLaunchKernelGGL((down_small_kernel<FMT, MTD, IMAX, NWD, false, false, SP>), dim3(d / 16, slots),
+                               dim3(64 * NWD), 0, s, qm(L.down), qm(L.sh_down), h_hi, h_lo, hx, d, f, table,
+                               y_pairs, y_shared, cb);
+    };
+    if constexpr (MTD == 1) {
+        if (T <= 4) {
+            launch_down(std::true_type{});
+            return;
+        }
+    }
+    launch_down(std::false_type{});
 }
 
 template <int FMT>
