@@ -131,7 +131,9 @@ __device__ __forceinline__ float half_of(const u32x2 &v, int j) {
 // IMAX = number of valid D rows per lane group i (compile time): 1 for a
 // single-token batch, 2 for two tokens, 4 otherwise.  The epilogue touches
 // only those rows, so small batches pay no selects.
-template <int FMT, int MT, int IMAX, int J>
+// RS: result registers between successive rows used (token rows spread
+// over the matrix rows: accumulator i takes result register i RS)
+template <int FMT, int MT, int IMAX, int J, int RS = 1>
 __device__ __forceinline__ void gateup_block(const GateUpUnit<FMT, MT> &U, f32x4 *ag, f32x4 *au) {
     const u32x4 ones = {kOneBf16x2, kOneBf16x2, kOneBf16x2, kOneBf16x2};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -154,15 +156,15 @@ __device__ __forceinline__ void gateup_block(const GateUpUnit<FMT, MT> &U, f32x4
             pu = mfma_bf16(U.A[mt][J], Hu, pu);
 #pragma unroll
             for (int i = 0; i < IMAX; ++i) {
-                ag[mt][i] = fmaf(dg, pg[i], ag[mt][i]);
-                au[mt][i] = fmaf(du, pu[i], au[mt][i]);
+                ag[mt][i] = fmaf(dg, pg[i * RS], ag[mt][i]);
+                au[mt][i] = fmaf(du, pu[i * RS], au[mt][i]);
             }
         } else {
             const f32x4 xs = mfma_bf16(U.A[mt][J], ones, zero);
 #pragma unroll
             for (int i = 0; i < IMAX; ++i) {
-                ag[mt][i] = fmaf(dg, pg[i], fmaf(mgv, xs[i], ag[mt][i]));
-                au[mt][i] = fmaf(du, pu[i], fmaf(muv, xs[i], au[mt][i]));
+                ag[mt][i] = fmaf(dg, pg[i * RS], fmaf(mgv, xs[i * RS], ag[mt][i]));
+                au[mt][i] = fmaf(du, pu[i * RS], fmaf(muv, xs[i * RS], au[mt][i]));
             }
         }
     }
@@ -207,13 +209,15 @@ __device__ __forceinline__ uint32_t max_mag_bf16x8(const u32x4 &v, uint32_t mx) 
     return mx;
 }
 
-// SPREAD (up to 4 tokens, x staged): token t fills matrix rows 4t .. 4t + 3,
-// so lane group t holds token t's sums in its first result register and
-// the per-block epilogue runs one FMA per matrix (RI = 1) instead of one per
-// token on every lane (with tokens in rows 0 .. T-1 only lane group 0 held
-// useful rows, while all four ran the FMAs).
-template <int FMT, int IMAX, int NW, bool XL, int TPW, int NB = 16 / NW, bool SPREAD = false,
-          int RI = SPREAD ? 1 : IMAX>
+// SP: matrix rows per token (x staged for SP > 1).  Token t fills rows
+// SP t .. SP t + SP - 1, so with SP = 4 (up to 4 tokens) lane group t holds
+// token t's sums in its first result register and the per-block epilogue
+// runs one FMA per matrix (RI = 1), and with SP = 2 (up to 8 tokens) lane
+// group g holds tokens 2g and 2g + 1 in registers 0 and 2 (RI = 2); with the
+// tokens in rows 0 .. T-1 (SP = 1) only the first lane groups held useful
+// rows, while all four ran T FMAs.
+__host__ __device__ constexpr int spread_ri(int sp, int imax) { return sp == 1 ? imax : (4 / sp < imax ? 4 / sp : imax); }
+template <int FMT, int IMAX, int NW, bool XL, int TPW, int NB = 16 / NW, int SP = 1, int RI = spread_ri(SP, IMAX)>
 __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &up, const QMatDev &sgate,
                                             const QMatDev &sup, const uint16_t *__restrict__ x, int T, int k, int d,
                                             int f, const int32_t *__restrict__ sorted_pair, const Group &grp,
@@ -222,7 +226,7 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
                                             int32_t *__restrict__ hx, uint16_t *xs, u32x4 *pieces) {
     static_assert(NW > 1, "token rows: K split over waves");
     static_assert(TPW == 1 || XL, "several tiles per workgroup share the staged x");
-    static_assert(!SPREAD || (XL && IMAX <= 4), "spread token rows: x staged, at most 4 tokens");
+    static_assert(SP == 1 || (XL && (SP == 2 || SP == 4)), "spread token rows: x staged, 2 or 4 rows per token");
     const int lane = __lane_id();
     // TPW tiles per workgroup: waves [NW g, NW g + NW) take tile nt + g
     const int wall = wave_uniform(threadIdx.x >> 6);
@@ -251,7 +255,7 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
     ag[0] = f32x4{0.f, 0.f, 0.f, 0.f};
     au[0] = f32x4{0.f, 0.f, 0.f, 0.f};
     // the token row of this lane's matrix row
-    const int xr = SPREAD ? ((rr >> 2) < T ? (rr >> 2) : T - 1) : (rr < T ? rr : T - 1);
+    const int xr = rr / SP < T ? rr / SP : T - 1;
     const uint16_t *xrow[1] = {x + (size_t)xr * d};
     const int cpr = d / 8;                // 16-byte chunks per x row
     uint32_t xmax = 0u;                   // largest |x| bits of this lane's row over its K slices
@@ -349,10 +353,10 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
 #pragma unroll
                     for (int j = 0; j < 4; ++j) xmax = max_mag_bf16x8(U[b].A[0][j], xmax);
                 }
-                gateup_block<FMT, 1, RI, 0>(U[b], ag, au);
-                gateup_block<FMT, 1, RI, 1>(U[b], ag, au);
-                gateup_block<FMT, 1, RI, 2>(U[b], ag, au);
-                gateup_block<FMT, 1, RI, 3>(U[b], ag, au);
+                gateup_block<FMT, 1, RI, 0, SP>(U[b], ag, au);
+                gateup_block<FMT, 1, RI, 1, SP>(U[b], ag, au);
+                gateup_block<FMT, 1, RI, 2, SP>(U[b], ag, au);
+                gateup_block<FMT, 1, RI, 3, SP>(U[b], ag, au);
             }
         }
     }
@@ -371,16 +375,17 @@ __device__ __forceinline__ void gateup_task(const QMatDev &gate, const QMatDev &
     }
     __syncthreads();
     if (wv != 0) return;
-    // output row r = 4 gq + i (SPREAD: r = gq) takes the sums of its
-    // token's matrix row
+    // output row r = 4 gq + i (SP = 4: r = gq) takes the sums of its token's
+    // matrix rows: token t's are in lane group SP t / 4, accumulator
+    // t % (4 / SP)
     const int n = nt * 16 + rr;
 #pragma unroll
-    for (int i = 0; i < (SPREAD ? 1 : IMAX); ++i) {
-        const int r = SPREAD ? gq : 4 * gq + i;
+    for (int i = 0; i < (SP == 4 ? 1 : IMAX); ++i) {
+        const int r = SP == 4 ? gq : 4 * gq + i;
         const int tk = __shfl(rtok, r, 64);
         if (r >= nrows) continue;
         const int t = shared ? tk : tk / k;
-        const int sl = SPREAD ? t * 16 + rr : (t >> 2) * 16 + rr, si = SPREAD ? 0 : t & 3;
+        const int sl = ((SP * t) >> 2) * 16 + rr, si = t % (4 / SP);
         float gs = red[0][0][si][sl], us = red[0][1][si][sl];
         uint32_t mx = XL ? redx[t % NW][t] : redx[0][t];
 #pragma unroll
@@ -723,14 +728,14 @@ __device__ __forceinline__ void combine_tile(const CombineArgs &cb, const float 
 // first tile of each slot also records the slot's group (nrows 0: none) in
 // `table`, so the down kernel reads it with one load.  NB: units each wave
 // has in flight per batch (fewer hold fewer registers).
-template <int FMT, int IMAX, int NW, bool XL, int TPW, int NB = 16 / NW, bool SPREAD = false>
+template <int FMT, int IMAX, int NW, bool XL, int TPW, int NB = 16 / NW, int SP = 1>
 __global__ __launch_bounds__(64 * NW * TPW) __attribute__((amdgpu_waves_per_eu(IMAX > 2 && NB == 2 ? 5 : 1)))
 void gateup_small_kernel(
     QMatDev gate, QMatDev up, QMatDev sgate, QMatDev sup, const uint16_t *__restrict__ x, int T,
     int k, int d, int f, int E, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ sorted_pair, uint16_t *__restrict__ h_hi,
     uint16_t *__restrict__ h_lo, int32_t *__restrict__ hx, Group *__restrict__ table, int slot0) {
-    __shared__ float red[NW * TPW][2][SPREAD ? 1 : IMAX][64];
+    __shared__ float red[NW * TPW][2][spread_ri(SP, IMAX)][64];
     __shared__ uint32_t redx[NW * TPW][16];
     // per wave: a batch's scale pieces (16 units' worth: 2 matrices x 2 planes)
     __shared__ u32x4 pieces[NW * TPW][8 * NB * 2 * 2];
@@ -774,7 +779,7 @@ void gateup_small_kernel(
         if (rec) *reinterpret_cast<u32x4 *>(&table[blockIdx.y]) = u32x4{0u, 0u, 0u, 0u};
         return;
     }
-    gateup_task<FMT, IMAX, NW, XL, TPW, NB, SPREAD>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp,
+    gateup_task<FMT, IMAX, NW, XL, TPW, NB, SP>(gate, up, sgate, sup, x, T, k, d, f, sorted_pair, grp,
                                         (int)blockIdx.x * TPW, red, redx, h_hi, h_lo, hx, xs_dyn, &pieces[0][0]);
     if (rec) *reinterpret_cast<u32x4 *>(&table[blockIdx.y]) = __builtin_bit_cast(u32x4, grp);
 }
@@ -1055,16 +1060,17 @@ static void launch_small_fmt(const moe_layer &L, const uint16_t *x, int T, int k
         // group's workgroups are resident at once (with four-unit batches,
         // 124 VGPRs, only four fit and the last groups ran as a second
         // round: workload 2 +3.5%, T = 4 Q2 +3%; at T = 8 it lost 0.5%)
-        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, true, 1, 2, true>), dim3(f / 16, slots),
+        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, true, 1, 2, 4>), dim3(f / 16, slots),
                            dim3(64 * NWG), (unsigned)xbytes, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up),
                            x, T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, hx, table, slot0);
     else if (IMAX == 2 && xbytes <= kXsMaxBytes)
         // two tokens: rows 0-3 and 4-7, one epilogue FMA per matrix
-        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, true, 1, 16 / NWG, true>), dim3(f / 16, slots),
+        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, true, 1, 16 / NWG, 4>), dim3(f / 16, slots),
                            dim3(64 * NWG), (unsigned)xbytes, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up),
                            x, T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, hx, table, slot0);
     else if (T <= 8 && xbytes <= kXsMaxBytes)
-        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, true, 1>), dim3(f / 16, slots),
+        // five to eight tokens: two rows per token
+        hipLaunchKernelGGL((gateup_small_kernel<FMT, IMAX, NWG, true, 1, 16 / NWG, IMAX == 4 ? 2 : 1>), dim3(f / 16, slots),
                            dim3(64 * NWG), (unsigned)xbytes, s, qm(L.gate), qm(L.up), qm(L.sh_gate), qm(L.sh_up),
                            x, T, k, d, f, E, offsets, sorted_pair, h_hi, h_lo, hx, table, slot0);
     else if (IMAX >= 2 && T <= 16 && xbytes <= 2 * kXsMaxBytes && (f / 16) % 2 == 0)
