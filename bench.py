@@ -65,8 +65,8 @@ METRIC = "MoE-layer tokens/s (decode T=1/4, prefill 8192); % HBM BW or % MFMA pe
 # the kernel sources it was taken on and is reported as null once those
 # sources change.
 TRAFFIC = {
-    1: (("common.h", "ffn_small.hip"), "646639c06bc3644e", 20210222),
-    2: (("common.h", "ffn_small.hip"), "646639c06bc3644e", 49050597),
+    1: (("common.h", "ffn_small.hip"), "40d151a67ca95019", 20211060),
+    2: (("common.h", "ffn_small.hip"), "40d151a67ca95019", 49040681),
     3: (("common.h", "ffn_prefill.hip"), "a8b8e7f47d56f428", 2502124811),
     4: (("common.h", "ffn_prefill.hip"), "a8b8e7f47d56f428", 2159120651),
 }
