@@ -64,7 +64,10 @@
  *         two code bits of four columns; column c of the four is at bit
  *         4*(c&1) + 2*(c>>1) (so bits 1:0 = c0, 3:2 = c2, 5:4 = c1, 7:6 = c3).
  *   hi    (Q3 only) 256 bytes per unit: little-endian 32-bit word g*16 + rr,
- *         bit 4*s + j holds code bit 2.
+ *         bit 4*n + t holds code bit 2, with n = 4*(j%2) + 2*(s/4) + s%2 and
+ *         t = 2*(j/2) + (s/2)%2 (the bit of the code whose low bits are in
+ *         nibble n of the word's 32-bit lo dword j/2 at bits 1:0 of the
+ *         nibble when t is even, at bits 3:2 when t is odd).
  *   scale 64 fp16 per unit, element rr*4 + j.
  *   min   (Q2 only) 64 fp16 per unit, element rr*4 + j.
  * n matrices of one kind are stacked expert-major (expert e starts at unit

@@ -32,7 +32,10 @@
  *   g = (k%32)/8 ; s = k%8.
  *   lo   : 512 B per unit, byte (((g*16+rr)*4+j)*2 + s/4); within that byte
  *          the 2-bit code of s%4 = c sits at bit 4*(c&1) + 2*(c>>1).
- *   hi   : (Q3) 256 B per unit, 32-bit word (g*16+rr), bit 4*s + j.
+ *   hi   : (Q3) 256 B per unit, 32-bit word (g*16+rr), bit 4*n + t with
+ *          n = 4*(j%2) + 2*(s/4) + s%2 and t = 2*(j/2) + (s/2)%2 (the third
+ *          bit of the code whose low bits sit in nibble n of the lane's lo
+ *          dword j/2, or of that dword shifted right by 2 when t is odd).
  *   scale: 64 fp16 per unit, element rr*4 + j.      min: same as scale (Q2).
  *   n matrices are stacked expert-major.
  */
@@ -93,7 +96,8 @@ int oracle_code(const oracle_qmat *m, int fmt, int rows, int K, int e, int r, in
         const uint8_t *wp = m->hi + u * 256 + (g * 16 + rr) * 4;
         uint32_t word = (uint32_t)wp[0] | ((uint32_t)wp[1] << 8) | ((uint32_t)wp[2] << 16) |
                         ((uint32_t)wp[3] << 24);
-        q |= (int)((word >> (4 * s + j)) & 1) << 2;
+        int n = 4 * (j % 2) + 2 * (s / 4) + s % 2, t = 2 * (j / 2) + (s / 2) % 2;
+        q |= (int)((word >> (4 * n + t)) & 1) << 2;
     }
     return q;
 }

@@ -102,7 +102,7 @@ __device__ __forceinline__ uint32_t cvt_fp4_f16(uint32_t v, float scale) {
 
 // B operand (8 values, k = 8g..8g+7 of one 32-block) from the lane's lo dword
 // holding blocks (2*half, 2*half+1): HALF selects which 16 bits.  SCALE is 2
-// (exact codes) for lo bits; for Q3 hi bits use hi_operand below.
+// (exact codes) for lo bits; Q3 takes q3_operand below.
 template <int HALF, bool F16>
 __device__ __forceinline__ u32x4 lo_operand(uint32_t dw) {
     const uint32_t a = dw & 0x33333333u;         // codes 0,1 of every byte
@@ -122,44 +122,33 @@ __device__ __forceinline__ u32x4 lo_operand(uint32_t dw) {
     return r;
 }
 
-// Q3 code bit 2 of block j as an operand holding 4*bit: nibble s of
-// (H >> j) & 0x11111111 is 0 or 1 = fp4 0 or 0.5, scaled by 8.
+// Q3 operand holding q - 4 for the 8 codes of block J (lane's lo dword J/2,
+// the lane's third-bit word H).  The third bits are stored so that bit
+// 4 n + 2 (J/2) of H belongs to the code whose low bits sit in nibble n of
+// (lo & 0x33333333) and bit 4 n + 2 (J/2) + 1 to nibble n of
+// ((lo >> 2) & 0x33333333).  A low-bits nibble A (0..3) then becomes the
+// fp4 (e2m1) code of (q - 4) / 2: A itself when the third bit is set
+// (q - 4 = A), 12 - A when it is clear (sign bit and magnitude 4 - A:
+// q - 4 = A - 4), so one conversion with scale 2 gives q - 4 exactly.
 template <int J, bool F16>
-__device__ __forceinline__ u32x4 hi_operand(uint32_t H) {
-    const uint32_t v = (H >> J) & 0x11111111u;
+__device__ __forceinline__ u32x4 q3_operand(uint32_t dw, uint32_t H) {
+    constexpr int D = J >> 1, HALF = J & 1;
+    const uint32_t a = dw & 0x33333333u, b = (dw >> 2) & 0x33333333u;
+    const uint32_t ha = (H >> (2 * D)) & 0x11111111u, hb = (H >> (2 * D + 1)) & 0x11111111u;
+    const uint32_t ma = (ha << 4) - ha, mb = (hb << 4) - hb;   // 0xF where the third bit is set
+    const uint32_t na = (a & ma) | ((0xCCCCCCCCu - a) & ~ma);
+    const uint32_t nb = (b & mb) | ((0xCCCCCCCCu - b) & ~mb);
     u32x4 r;
     if constexpr (F16) {
-        r[0] = cvt_fp4_f16<0>(v, 8.0f);
-        r[1] = cvt_fp4_f16<1>(v, 8.0f);
-        r[2] = cvt_fp4_f16<2>(v, 8.0f);
-        r[3] = cvt_fp4_f16<3>(v, 8.0f);
+        r[0] = cvt_fp4_f16<2 * HALF>(na, 2.0f);
+        r[1] = cvt_fp4_f16<2 * HALF>(nb, 2.0f);
+        r[2] = cvt_fp4_f16<2 * HALF + 1>(na, 2.0f);
+        r[3] = cvt_fp4_f16<2 * HALF + 1>(nb, 2.0f);
     } else {
-        r[0] = cvt_fp4_bf16<0>(v, 8.0f);
-        r[1] = cvt_fp4_bf16<1>(v, 8.0f);
-        r[2] = cvt_fp4_bf16<2>(v, 8.0f);
-        r[3] = cvt_fp4_bf16<3>(v, 8.0f);
-    }
-    return r;
-}
-
-// Q3 code bit 2 of block j as an operand holding 4*bit - 4 (-4 or 0): the
-// nibbles where the bit is clear become 9 = fp4 -0.5, scaled by 8; the others
-// stay 0.  With the low-bits operand the matrix op then sums x * (q - 4).
-template <int J, bool F16>
-__device__ __forceinline__ u32x4 hi_operand_m4(uint32_t H) {
-    uint32_t v = ((H >> J) & 0x11111111u) ^ 0x11111111u;
-    v |= v << 3;
-    u32x4 r;
-    if constexpr (F16) {
-        r[0] = cvt_fp4_f16<0>(v, 8.0f);
-        r[1] = cvt_fp4_f16<1>(v, 8.0f);
-        r[2] = cvt_fp4_f16<2>(v, 8.0f);
-        r[3] = cvt_fp4_f16<3>(v, 8.0f);
-    } else {
-        r[0] = cvt_fp4_bf16<0>(v, 8.0f);
-        r[1] = cvt_fp4_bf16<1>(v, 8.0f);
-        r[2] = cvt_fp4_bf16<2>(v, 8.0f);
-        r[3] = cvt_fp4_bf16<3>(v, 8.0f);
+        r[0] = cvt_fp4_bf16<2 * HALF>(na, 2.0f);
+        r[1] = cvt_fp4_bf16<2 * HALF>(nb, 2.0f);
+        r[2] = cvt_fp4_bf16<2 * HALF + 1>(na, 2.0f);
+        r[3] = cvt_fp4_bf16<2 * HALF + 1>(nb, 2.0f);
     }
     return r;
 }

@@ -274,38 +274,31 @@ __device__ __forceinline__ uint32_t pk_fma_f16(uint32_t a, uint32_t b, uint32_t 
     __asm__("v_pk_fma_f16 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
     return r;
 }
-__device__ __forceinline__ uint32_t pk_add_f16(uint32_t a, uint32_t b) {
-    uint32_t r;
-    __asm__("v_pk_add_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
-}
 
 // fp16(w) for the 8 weights of block J (rounded once).
 template <int FMT, int J>
 __device__ __forceinline__ u32x4 bfrag_f16(const BRaw<FMT> &b) {
-    const u32x4 q = lo_operand<J & 1, true>(b.lo[J >> 1]);      // exact codes 0..3 as fp16
     const uint32_t d = half_pair(b.sc, J);
     u32x4 r;
     if constexpr (FMT == MOE_FMT_Q2_B32) {
+        const u32x4 q = lo_operand<J & 1, true>(b.lo[J >> 1]);   // exact codes 0..3 as fp16
         const uint32_t m = half_pair(b.mn, J);
         r.x = pk_fma_f16(q.x, d, m);
         r.y = pk_fma_f16(q.y, d, m);
         r.z = pk_fma_f16(q.z, d, m);
         r.w = pk_fma_f16(q.w, d, m);
     } else {
-        const u32x4 h4 = hi_operand<J, true>(b.hi);               // 4*bit2 as fp16
-        // -4d, exact: fp16 bits of d with the exponent raised by 2 and the sign set
-        const uint32_t m4 = pk_fma_f16(d, 0xC400C400u /* -4.0, -4.0 */, 0u);
-        r.x = pk_fma_f16(pk_add_f16(q.x, h4.x), d, m4);
-        r.y = pk_fma_f16(pk_add_f16(q.y, h4.y), d, m4);
-        r.z = pk_fma_f16(pk_add_f16(q.z, h4.z), d, m4);
-        r.w = pk_fma_f16(pk_add_f16(q.w, h4.w), d, m4);
+        const u32x4 q = q3_operand<J, true>(b.lo[J >> 1], b.hi);   // exact q - 4 as fp16
+        r.x = pk_fma_f16(q.x, d, 0u);
+        r.y = pk_fma_f16(q.y, d, 0u);
+        r.z = pk_fma_f16(q.z, d, 0u);
+        r.w = pk_fma_f16(q.w, d, 0u);
     }
     return r;
 }
 
 // exact weights split as fp16 hi + lo: w = fp32(d*q + m) (exact), hi = fp16(w),
-// lo = fp16(w - hi).  qword holds two fp16 codes (Q3: lo + 4*bit2).
+// lo = fp16(w - hi).  qword holds two fp16 codes (Q3: q - 4, with m = 0).
 // Exact weights split into fp16 hi + lo.  hi = fp16(d*q + m) is one packed
 // fp16 FMA (one rounding).  lo = fp16(w - hi) with w = d*q + m from a
 // mixed-precision FMA on the fp16 inputs, exact in fp32 for block-32 codes
@@ -332,17 +325,14 @@ __device__ __forceinline__ uint32_t residual_pair(uint32_t hi2, float w0s, float
 // exact weights of block J as fp16 hi + lo (lo multiplied by lo_scale, 1 or 0)
 template <int FMT, int J>
 __device__ __forceinline__ void bfrag_split(const BRaw<FMT> &b, float lo_scale, u32x4 &hi, u32x4 &lo) {
-    u32x4 q = lo_operand<J & 1, true>(b.lo[J >> 1]);
     const uint32_t d = half_pair(b.sc, J);
+    u32x4 q;
     uint32_t m;
     if constexpr (FMT == MOE_FMT_Q3_B32) {
-        const u32x4 h4 = hi_operand<J, true>(b.hi);
-        q.x = pk_add_f16(q.x, h4.x);
-        q.y = pk_add_f16(q.y, h4.y);
-        q.z = pk_add_f16(q.z, h4.z);
-        q.w = pk_add_f16(q.w, h4.w);
-        m = pk_fma_f16(d, 0xC400C400u /* -4.0, -4.0 */, 0u);   // -4d, exact
+        q = q3_operand<J, true>(b.lo[J >> 1], b.hi);   // q - 4: w = d (q - 4)
+        m = 0u;
     } else {
+        q = lo_operand<J & 1, true>(b.lo[J >> 1]);
         m = half_pair(b.mn, J);
     }
     const uint32_t s2 = lo_scale != 0.f ? 0x3C003C00u : 0u;   // (s, s) in fp16

@@ -13,8 +13,9 @@
 //     every lane one 8-byte piece (4 blocks x 8 codes) per 16x128 unit, so a
 //     wave load is 512 contiguous bytes;
 //   - 2-bit codes become exact bf16/fp16 integers with the fp4 conversion
-//     (two masks + four converts per 16 codes); Q3's third bit is a second
-//     operand holding 4*bit - 4 (-4 or 0), so the two hold q - 4;
+//     (two masks + four converts per 16 codes); for Q3 each code's third bit
+//     turns its low-bits nibble into the fp4 code of (q - 4) / 2 (a select
+//     per nibble), so the same four converts give q - 4 exactly;
 //   - the 32-wide K block is exactly one 16x16x32 matrix-core step, so the
 //     product codes x activations comes out per block, and the block scale and
 //     minimum are applied in fp32: acc += d*P + m*X (Q2, X = sum of the
@@ -118,10 +119,13 @@ __device__ __forceinline__ void gateup_load_x(GateUpUnit<FMT, MT> &U, int u, int
             U.A[mt][j] = *reinterpret_cast<const u32x4 *>(xrow[mt] + u * 128 + j * 32 + gq * 8);
 }
 
+// The weight operand of block J: Q2 exact codes q, Q3 q - 4 (both exact)
 template <int J, bool F16, int FMT>
-__device__ __forceinline__ void block_operands(uint32_t lo_dw, uint32_t hi_w, u32x4 &B, u32x4 &H) {
-    B = lo_operand<J & 1, F16>(lo_dw);
-    if constexpr (FMT == MOE_FMT_Q3_B32) H = hi_operand_m4<J, F16>(hi_w);   // 4 bit2 - 4
+__device__ __forceinline__ u32x4 block_operand(uint32_t lo_dw, uint32_t hi_w) {
+    if constexpr (FMT == MOE_FMT_Q3_B32)
+        return q3_operand<J, F16>(lo_dw, hi_w);
+    else
+        return lo_operand<J & 1, F16>(lo_dw);
 }
 
 __device__ __forceinline__ float half_of(const u32x2 &v, int j) {
@@ -137,9 +141,8 @@ template <int FMT, int MT, int IMAX, int J, int RS = 1>
 __device__ __forceinline__ void gateup_block(const GateUpUnit<FMT, MT> &U, f32x4 *ag, f32x4 *au) {
     const u32x4 ones = {kOneBf16x2, kOneBf16x2, kOneBf16x2, kOneBf16x2};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    u32x4 Bg, Bu, Hg, Hu;
-    block_operands<J, false, FMT>(U.lg[J >> 1], U.hg, Bg, Hg);
-    block_operands<J, false, FMT>(U.lu[J >> 1], U.hu, Bu, Hu);
+    const u32x4 Bg = block_operand<J, false, FMT>(U.lg[J >> 1], U.hg);
+    const u32x4 Bu = block_operand<J, false, FMT>(U.lu[J >> 1], U.hu);
     const float dg = half_of(U.sg, J), du = half_of(U.su, J);
     float mgv = 0.f, muv = 0.f;
     if constexpr (FMT == MOE_FMT_Q2_B32) {
@@ -151,9 +154,7 @@ __device__ __forceinline__ void gateup_block(const GateUpUnit<FMT, MT> &U, f32x4
         f32x4 pg = mfma_bf16(U.A[mt][J], Bg, zero);
         f32x4 pu = mfma_bf16(U.A[mt][J], Bu, zero);
         if constexpr (FMT == MOE_FMT_Q3_B32) {
-            // x . (q - 4): the offset rides in the bit-2 operand
-            pg = mfma_bf16(U.A[mt][J], Hg, pg);
-            pu = mfma_bf16(U.A[mt][J], Hu, pu);
+            // x . (q - 4) in one matrix op (the operand holds q - 4)
 #pragma unroll
             for (int i = 0; i < IMAX; ++i) {
                 ag[mt][i] = fmaf(dg, pg[i * RS], ag[mt][i]);
@@ -417,17 +418,15 @@ template <int FMT, int MT, int IMAX, int J>
 __device__ __forceinline__ void down_block(const DownUnit<FMT, MT> &U, f32x4 *acc) {
     const u32x4 ones = {kOneF16x2, kOneF16x2, kOneF16x2, kOneF16x2};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    u32x4 B, H;
-    block_operands<J, true, FMT>(U.lw[J >> 1], U.hw, B, H);
+    const u32x4 B = block_operand<J, true, FMT>(U.lw[J >> 1], U.hw);
     const float dv = half_of(U.sw, J);
     float mv = 0.f;
     if constexpr (FMT == MOE_FMT_Q2_B32) mv = half_of(U.mw, J);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        f32x4 p = mfma_f16(U.A[mt][J], B, zero);
+        const f32x4 p = mfma_f16(U.A[mt][J], B, zero);
         if constexpr (FMT == MOE_FMT_Q3_B32) {
-            // h . (q - 4): the offset rides in the bit-2 operand
-            p = mfma_f16(U.A[mt][J], H, p);
+            // h . (q - 4) in one matrix op
 #pragma unroll
             for (int i = 0; i < IMAX; ++i) acc[mt][i] = fmaf(dv, p[i], acc[mt][i]);
         } else {
@@ -448,12 +447,10 @@ template <int FMT, int J>
 __device__ __forceinline__ void down_block_spread(const DownUnit<FMT, 1> &U, float (&acc)[2]) {
     const u32x4 ones = {kOneF16x2, kOneF16x2, kOneF16x2, kOneF16x2};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    u32x4 B, H;
-    block_operands<J, true, FMT>(U.lw[J >> 1], U.hw, B, H);
+    const u32x4 B = block_operand<J, true, FMT>(U.lw[J >> 1], U.hw);
     const float dv = half_of(U.sw, J);
-    f32x4 p = mfma_f16(U.A[0][J], B, zero);
+    const f32x4 p = mfma_f16(U.A[0][J], B, zero);
     if constexpr (FMT == MOE_FMT_Q3_B32) {
-        p = mfma_f16(U.A[0][J], H, p);
         acc[0] = fmaf(dv, p[0], acc[0]);
         acc[1] = fmaf(dv, p[2], acc[1]);
     } else {

@@ -8,7 +8,8 @@ Format, one rows x K matrix (rows % 16 == 0, K % 128 == 0):
   unit u = (r // 16) * (K // 128) + k // 128, rr = r % 16, j = (k % 128) // 32,
   g = (k % 32) // 8, s = k % 8, c = s % 4.
   lo    512 B/unit: byte ((g*16 + rr)*4 + j)*2 + s//4, bits at 4*(c&1) + 2*(c>>1).
-  hi    256 B/unit (Q3): little-endian 32-bit word g*16 + rr, bit 4*s + j.
+  hi    256 B/unit (Q3): little-endian 32-bit word g*16 + rr, bit 4*n + t,
+        n = 4*(j%2) + 2*(s//4) + s%2, t = 2*(j//2) + (s//2)%2.
   scale 64 fp16/unit: element rr*4 + j.   min: same (Q2).
 """
 import numpy as np
@@ -23,8 +24,9 @@ def _positions(rows, K):
     c = s % 4
     lo_byte = unit * 512 + ((g * 16 + rr) * 4 + j) * 2 + s // 4
     lo_shift = 4 * (c & 1) + 2 * (c >> 1)
-    hi_byte = unit * 256 + (g * 16 + rr) * 4 + (4 * s + j) // 8
-    hi_shift = (4 * s + j) % 8
+    hbit = 4 * (4 * (j % 2) + 2 * (s // 4) + s % 2) + 2 * (j // 2) + (s // 2) % 2
+    hi_byte = unit * 256 + (g * 16 + rr) * 4 + hbit // 8
+    hi_shift = hbit % 8
     sidx = unit * 64 + rr * 4 + j
     return lo_byte, lo_shift, hi_byte, hi_shift, sidx
 
