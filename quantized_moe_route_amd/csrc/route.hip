@@ -482,7 +482,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     __shared__ int32_t eoff[1024];
     __shared__ int32_t wtot[4];
     __shared__ int last_flag, tile_flag;
-    static_assert(4 * TT * kRS * 4 <= sizeof(keys), "phase A's sums fit the key rows");
+    static_assert(4 * TT * 4 * kRS * 4 <= sizeof(keys), "phase A's pair sums fit the key rows");
 
     const int ES = (E + kRS - 1) / kRS, KC = d / kRK;
     const int slice = blockIdx.x % ES, kc = blockIdx.x / ES, tt = blockIdx.y;
@@ -550,31 +550,34 @@ __global__ __launch_bounds__(256) void route_small_kernel(
                 for (int c = 0; c < 4; ++c) acc[t][c] = fmaf(xf, wv4[i][c], acc[t][c]);
             }
         }
-        // the 8 row lanes of a wave (same eq) by butterfly, in a fixed order;
-        // then the 4 waves through LDS
+        // the 8 row lanes of a wave (same eq): row pairs (rs, rs ^ 1) in the
+        // lane (rotation by 8 within each 16-lane row, no LDS), the four
+        // pair sums through LDS; the sum over rows is then
+        // ((p01 + p23) + (p45 + p67)) per wave and the waves add in order
 #pragma unroll
         for (int t = 0; t < TT; ++t)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                float v = acc[t][c];
-                v += __shfl_xor(v, 8, 64);
-                v += __shfl_xor(v, 16, 64);
-                v += __shfl_xor(v, 32, 64);
-                acc[t][c] = v;
-            }
-        float *red = reinterpret_cast<float *>(&keys[0][0]);   // [4 waves][TT][32]
-        if (rs == 0) {
+            for (int c = 0; c < 4; ++c)
+                acc[t][c] += __int_as_float(
+                    __builtin_amdgcn_update_dpp(0, __float_as_int(acc[t][c]), 0x128, 0xF, 0xF, false));
+        float *red = reinterpret_cast<float *>(&keys[0][0]);   // [4 waves][TT][4 pairs][32]
+        if ((rs & 1) == 0) {
 #pragma unroll
             for (int t = 0; t < TT; ++t)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) red[(wv * TT + t) * kRS + eq * 4 + c] = acc[t][c];
+                *reinterpret_cast<f32x4 *>(&red[((wv * TT + t) * 4 + (rs >> 1)) * kRS + eq * 4]) =
+                    f32x4{acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
         }
         __syncthreads();
         if (tid < TT * kRS) {
             const int t = tid / kRS, e = tid % kRS;
             if (t < Tt) {
-                const float s = (((red[(0 * TT + t) * kRS + e] + red[(1 * TT + t) * kRS + e]) +
-                                  red[(2 * TT + t) * kRS + e]) + red[(3 * TT + t) * kRS + e]) + bias_e;
+                float sw[4];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float *q = &red[((w * TT + t) * 4) * kRS + e];
+                    sw[w] = (q[0] + q[kRS]) + (q[2 * kRS] + q[3 * kRS]);
+                }
+                const float s = (((sw[0] + sw[1]) + sw[2]) + sw[3]) + bias_e;
                 store_dev(&ptile[(((size_t)slice * KC + kc) * kRT + t) * kRS + e], s);
             }
         }
