@@ -65,10 +65,10 @@ METRIC = "MoE-layer tokens/s (decode T=1/4, prefill 8192); % HBM BW or % MFMA pe
 # the kernel sources it was taken on and is reported as null once those
 # sources change.
 TRAFFIC = {
-    1: (("common.h", "ffn_small.hip"), "0f3102109453b0af", 20211049),
-    2: (("common.h", "ffn_small.hip"), "0f3102109453b0af", 49021950),
-    3: (("common.h", "ffn_prefill.hip"), "9ef069ee536495f6", 2503412102),
-    4: (("common.h", "ffn_prefill.hip"), "9ef069ee536495f6", 2201449650),
+    1: (("common.h", "ffn_small.hip"), "0f3102109453b0af", 20210893),
+    2: (("common.h", "ffn_small.hip"), "0f3102109453b0af", 49021881),
+    3: (("common.h", "ffn_prefill.hip"), "9ef069ee536495f6", 2501741976),
+    4: (("common.h", "ffn_prefill.hip"), "9ef069ee536495f6", 2202330775),
 }
 
 
